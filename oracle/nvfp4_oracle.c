@@ -1,0 +1,527 @@
+/*
+ * NVFP4 CPU oracle -- TEST INFRASTRUCTURE ONLY.
+ *
+ * Plain, slow, scalar C.  Only the test suite, the smoke check and the CPU
+ * baseline leg of the benchmark may load this file's shared library; the
+ * product path (the HIP library) never links, calls or imports it, and the
+ * two share no code, header, table or constant generator.
+ *
+ * What it computes (sources):
+ *   [NV-SUM] "Pretraining Large Language Models with NVFP4", gist.science
+ *            summary page, section "Resumo tecnico", part 2 "Metodologia
+ *            Proposta": NVFP4 = FP4 values in blocks of 16, one E4M3 scale per
+ *            block, one FP32 scale per tensor ("Formato NVFP4" bullets);
+ *            random Hadamard transforms on the Wgrad inputs (technique 2);
+ *            16x16 2D scaling of weights so that forward and backward see the
+ *            same quantized weight (technique 3); stochastic rounding only on
+ *            gradients, round-to-nearest-even otherwise (technique 4).
+ *   [NV-NEWS] "NVIDIA cria metodo para treinar redes neurais com precisao de
+ *            4 bits", section "Como funciona": the Hadamard transforms are
+ *            16x16.
+ *   [OCP-MX] OCP Microscaling Formats (MX) v1.0, FP4 E2M1 element: values
+ *            {0, 0.5, 1, 1.5, 2, 3, 4, 6} with a sign bit, no Inf/NaN.
+ *   [OCP-F8] OCP 8-bit Floating Point Specification (OFP8), E4M3: bias 7,
+ *            largest finite 448 (0x7E), 0x7F/0xFF are NaN, subnormals m*2^-9.
+ *   [PCG]    M. Jarzynski, M. Olano, "Hash Functions for GPU Rendering",
+ *            JCGT 9(3), 2020: the "pcg" 32-bit hash.
+ *   [FWHT]   the radix-2 fast Walsh-Hadamard transform (Sylvester ordering).
+ *
+ * Where the pages are silent the oracle follows these readings (all FP32
+ * arithmetic is IEEE binary32, round-to-nearest-even, no contraction, in the
+ * order written; build with -ffp-contract=off, no fast-math):
+ *   tensor scale   S_enc = 2688/amax_t (6*448 = largest FP4 x E4M3 product),
+ *                  clamped to FLT_MAX; 1 when amax_t == 0; stored s_t = 1/S_enc
+ *   block scale    e_b = E4M3_nearest_even_satfinite((amax_b / 6) * S_enc)
+ *   element scale  r_b = 0 if e_b == 0 else min(S_enc / dec(e_b), FLT_MAX)
+ *   scaled value   v = y * r_b, E2M1 code = sign(y) | magnitude index
+ *   RNE            nearest E2M1 magnitude, ties to the even index, clamp at 6
+ *   SR             up iff r16 < frac * 65536, frac = (a - lo) / (hi - lo)
+ *   random bits    r16 from the pcg hash keyed by (seed, output index)
+ *   RHT            per 16 tokens of one column: sign flips, FWHT stages
+ *                  h = 1, 2, 4, 8 as (a + b, a - b), then * 0.25
+ *
+ * Parity pins: see tests/test_oracle_pins.py.  The FP32 operation order of
+ * the scale rule and of the FWHT is a reading, pinned only on inputs where it
+ * is exact and by the invariants the pages state ("parity unpinned" for the
+ * general rounding order).
+ */
+#include <float.h>
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORA_ROW_1D 0
+#define ORA_COL_1D 1
+#define ORA_TILE_2D 2
+#define ORA_RNE 0
+#define ORA_SR 1
+
+/* ------------------------------------------------------------------ */
+/* Element and scale formats                                          */
+/* ------------------------------------------------------------------ */
+
+/* [OCP-MX] E2M1 magnitudes by 3-bit index. */
+static const double E2M1_MAG[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+
+double ora_e2m1_value(int code)
+{
+    double m = E2M1_MAG[code & 7];
+    return (code & 8) ? -m : m;
+}
+
+/* [OCP-F8] E4M3 ("FN" flavour) decode of an 8-bit code.  NaN for 0x7F/0xFF. */
+double ora_e4m3_value(int code)
+{
+    int s = (code >> 7) & 1, e = (code >> 3) & 15, m = code & 7;
+    double v;
+    if (e == 15 && m == 7)
+        return NAN;
+    if (e == 0)
+        v = ldexp((double)m, -9);
+    else
+        v = ldexp(1.0 + m / 8.0, e - 7);
+    return s ? -v : v;
+}
+
+/* Nearest finite non-negative E4M3 value to x >= 0, ties to the even code,
+ * anything at or beyond the largest finite value (448) gives 0x7E.
+ * Plain search over all 127 finite codes. */
+static double E4M3_FINITE[0x7F];
+
+__attribute__((constructor)) static void init_e4m3_table(void)
+{
+    int c;
+    for (c = 0; c <= 0x7E; c++)
+        E4M3_FINITE[c] = ora_e4m3_value(c);
+}
+
+int ora_e4m3_rne_satfinite(float x)
+{
+    int best = 0, c;
+    double bestd, xd = (double)x;
+    if (!(xd > 0.0))
+        return 0;
+    if (xd >= 448.0)
+        return 0x7E;
+    bestd = xd;
+    for (c = 1; c <= 0x7E; c++) {
+        double d = fabs(xd - E4M3_FINITE[c]);
+        if (d < bestd || (d == bestd && (c & 1) == 0 && (best & 1) != 0)) {
+            best = c;
+            bestd = d;
+        }
+    }
+    return best;
+}
+
+/* E2M1 round-to-nearest-even of an already scaled value v.
+ * Nearest of the 8 magnitudes, ties to the even index, saturating at 6.
+ * The sign is the sign bit of v (so -0 gives code 8). */
+int ora_e2m1_rne(float v)
+{
+    int sign = signbit(v) ? 8 : 0, best = 0, i;
+    double a = fabs((double)v), bestd;
+    if (a >= 6.0)
+        return sign | 7;
+    bestd = a;
+    for (i = 1; i < 8; i++) {
+        double d = fabs(a - E2M1_MAG[i]);
+        if (d < bestd || (d == bestd && (i & 1) == 0 && (best & 1) != 0)) {
+            best = i;
+            bestd = d;
+        }
+    }
+    return sign | best;
+}
+
+/* E2M1 stochastic rounding of v with 16 random bits r16 in [0, 65535].
+ * a = min(|v|, 6); lo = largest magnitude <= a, hi = the next one;
+ * rounds up iff r16 < frac * 65536 with frac = (a - lo) / (hi - lo), so the
+ * probability of rounding up is ceil(frac * 65536) / 65536. */
+int ora_e2m1_sr(float v, uint32_t r16)
+{
+    int sign = signbit(v) ? 8 : 0, k = 0, i;
+    double a = fabs((double)v), frac;
+    if (a > 6.0)
+        a = 6.0;
+    for (i = 0; i < 8; i++)
+        if (E2M1_MAG[i] <= a)
+            k = i;
+    if (k == 7)
+        return sign | 7;
+    frac = (a - E2M1_MAG[k]) / (E2M1_MAG[k + 1] - E2M1_MAG[k]);
+    if ((double)r16 < frac * 65536.0)
+        k += 1;
+    return sign | k;
+}
+
+/* ------------------------------------------------------------------ */
+/* Counter-based random bits for stochastic rounding                  */
+/* ------------------------------------------------------------------ */
+
+/* [PCG] the pcg hash, all arithmetic modulo 2^32. */
+uint32_t ora_pcg(uint32_t v)
+{
+    uint32_t state = v * 747796405u + 2891336453u;
+    uint32_t word = ((state >> ((state >> 28u) + 4u)) ^ state) * 277803737u;
+    return (word >> 22u) ^ word;
+}
+
+/* 16 random bits for output element index i under a 64-bit seed.
+ * key = pcg(lo32(seed) ^ pcg(hi32(seed))); one hash per pair of elements,
+ * the even element takes the low half-word, the odd one the high half-word. */
+uint32_t ora_sr_bits(uint64_t seed, uint64_t i)
+{
+    uint32_t key = ora_pcg((uint32_t)seed ^ ora_pcg((uint32_t)(seed >> 32)));
+    uint32_t w = ora_pcg(key ^ (uint32_t)(i >> 1));
+    return (i & 1) ? (w >> 16) : (w & 0xFFFFu);
+}
+
+/* ------------------------------------------------------------------ */
+/* Random Hadamard transform of 16 values                             */
+/* ------------------------------------------------------------------ */
+
+/* y = 0.25 * H16 * diag(d) * x, d_j = -1 where bit j of sign_mask is set,
+ * H16 the Sylvester Hadamard matrix, evaluated in FP32 by the radix-2 FWHT:
+ * stages h = 1, 2, 4, 8, each pair (p, p + h) with (p & h) == 0 becomes
+ * (u_p + u_{p+h}, u_p - u_{p+h}); the 0.25 factor is applied last.
+ * [NV-SUM] technique 2, [NV-NEWS] "Como funciona" (16x16). */
+void ora_rht16(const float *x, uint32_t sign_mask, float *y)
+{
+    float u[16];
+    int j, h, p;
+    for (j = 0; j < 16; j++)
+        u[j] = ((sign_mask >> j) & 1u) ? -x[j] : x[j];
+    for (h = 1; h < 16; h <<= 1) {
+        for (p = 0; p < 16; p++) {
+            if ((p & h) == 0) {
+                float a = u[p], b = u[p + h];
+                u[p] = a + b;
+                u[p + h] = a - b;
+            }
+        }
+    }
+    for (j = 0; j < 16; j++)
+        y[j] = 0.25f * u[j];
+}
+
+/* ------------------------------------------------------------------ */
+/* Scales                                                             */
+/* ------------------------------------------------------------------ */
+
+/* FP32 encode scale from the tensor amax (two-level scaling, [NV-SUM]
+ * "Escala em Dois Niveis"). */
+float ora_encode_scale(float amax_t)
+{
+    float s;
+    if (!(amax_t > 0.0f))
+        return 1.0f;
+    s = 2688.0f / amax_t;
+    if (s > FLT_MAX)
+        s = FLT_MAX;
+    return s;
+}
+
+/* E4M3 block scale code from a block amax and the tensor encode scale. */
+int ora_block_scale(float amax_b, float s_enc)
+{
+    float t = amax_b / 6.0f;
+    float sb = t * s_enc;
+    return ora_e4m3_rne_satfinite(sb);
+}
+
+/* Multiplier that maps a block's values onto the E2M1 grid. */
+float ora_element_scale(int e_b, float s_enc)
+{
+    float d, r;
+    if (e_b == 0)
+        return 0.0f;
+    d = (float)ora_e4m3_value(e_b);
+    r = s_enc / d;
+    if (r > FLT_MAX)
+        r = FLT_MAX;
+    return r;
+}
+
+static int encode(float y, float r_b, int rnd, uint64_t seed, uint64_t out_index)
+{
+    float v = y * r_b;
+    if (rnd == ORA_SR)
+        return ora_e2m1_sr(v, ora_sr_bits(seed, out_index));
+    return ora_e2m1_rne(v);
+}
+
+static void put_nibble(uint8_t *codes, uint64_t index, int code)
+{
+    uint8_t *b = &codes[index >> 1];
+    if (index & 1)
+        *b = (uint8_t)((*b & 0x0F) | (code << 4));
+    else
+        *b = (uint8_t)((*b & 0xF0) | (code & 0x0F));
+}
+
+/* Input element as FP32: bf16 is the upper half of an FP32 bit pattern. */
+static float load(const void *x, int dtype, int64_t ld, int64_t r, int64_t c)
+{
+    if (dtype == 0) {
+        uint16_t h = ((const uint16_t *)x)[r * ld + c];
+        uint32_t b = (uint32_t)h << 16;
+        float f;
+        memcpy(&f, &b, 4);
+        return f;
+    }
+    return ((const float *)x)[r * ld + c];
+}
+
+/* ------------------------------------------------------------------ */
+/* Quantization                                                       */
+/* ------------------------------------------------------------------ */
+
+static float tensor_amax(const void *x, int dtype, int64_t rows, int64_t cols, int64_t ld)
+{
+    float amax_t = 0.0f;
+    int64_t r;
+#pragma omp parallel for reduction(max : amax_t) schedule(static)
+    for (r = 0; r < rows; r++) {
+        int64_t c;
+        for (c = 0; c < cols; c++) {
+            float a = fabsf(load(x, dtype, ld, r, c));
+            if (a > amax_t)
+                amax_t = a;
+        }
+    }
+    return amax_t;
+}
+
+/* Quantize a rows x cols tensor (dtype 0 = bf16, 1 = fp32; leading dimension
+ * ld in elements) to NVFP4.  The tensor amax is always taken over the whole
+ * tensor; codes and scales are written only for the block lines in
+ * [begin, end) (rows for ROW_1D, columns for COL_1D, 16-row tile rows for
+ * TILE_2D), so that large tensors can be checked on samples.
+ *   ROW_1D : blocks of 16 along a row; codes [rows][cols/2], scales
+ *            [rows][cols/16]; output index i = r*cols + c.
+ *   COL_1D : blocks of 16 along a column; codes [cols][rows/2] and scales
+ *            [cols][rows/16] (transposed); output index i = c*rows + r.
+ *   TILE_2D: one scale per 16x16 tile ([NV-SUM] technique 3); codes
+ *            [rows][cols/2], scales [rows/16][cols/16]; optional codes_t
+ *            [cols][rows/2] and scales_t [cols/16][rows/16] hold the same
+ *            quantized values transposed; output index i = r*cols + c.
+ * Returns 0, or -1 on a bad shape or argument. */
+int ora_quantize_range(const void *x, int dtype, int64_t rows, int64_t cols, int64_t ld,
+                       int layout, int rnd, uint64_t seed, uint8_t *codes, uint8_t *scales,
+                       uint8_t *codes_t, uint8_t *scales_t, float *tensor_scale,
+                       float *amax_out, int64_t begin, int64_t end)
+{
+    int64_t line;
+    float amax_t, s_enc;
+    if (rows <= 0 || cols <= 0 || rows % 16 || cols % 16 || ld < cols || begin < 0)
+        return -1;
+    if (layout != ORA_ROW_1D && layout != ORA_COL_1D && layout != ORA_TILE_2D)
+        return -1;
+    amax_t = tensor_amax(x, dtype, rows, cols, ld);
+    s_enc = ora_encode_scale(amax_t);
+    *amax_out = amax_t;
+    *tensor_scale = 1.0f / s_enc;
+
+    if (layout == ORA_ROW_1D) {
+        if (end > rows)
+            end = rows;
+#pragma omp parallel for schedule(static)
+        for (line = begin; line < end; line++) {
+            int64_t r = line, c, j;
+            for (c = 0; c < cols; c += 16) {
+                float amax_b = 0.0f, r_b;
+                int e_b;
+                for (j = 0; j < 16; j++) {
+                    float a = fabsf(load(x, dtype, ld, r, c + j));
+                    if (a > amax_b)
+                        amax_b = a;
+                }
+                e_b = ora_block_scale(amax_b, s_enc);
+                r_b = ora_element_scale(e_b, s_enc);
+                scales[r * (cols / 16) + c / 16] = (uint8_t)e_b;
+                for (j = 0; j < 16; j++) {
+                    uint64_t idx = (uint64_t)(r * cols + c + j);
+                    put_nibble(codes, idx, encode(load(x, dtype, ld, r, c + j), r_b, rnd, seed, idx));
+                }
+            }
+        }
+    } else if (layout == ORA_COL_1D) {
+        if (end > cols)
+            end = cols;
+#pragma omp parallel for schedule(static)
+        for (line = begin; line < end; line++) {
+            int64_t c = line, r, j;
+            for (r = 0; r < rows; r += 16) {
+                float amax_b = 0.0f, r_b;
+                int e_b;
+                for (j = 0; j < 16; j++) {
+                    float a = fabsf(load(x, dtype, ld, r + j, c));
+                    if (a > amax_b)
+                        amax_b = a;
+                }
+                e_b = ora_block_scale(amax_b, s_enc);
+                r_b = ora_element_scale(e_b, s_enc);
+                scales[c * (rows / 16) + r / 16] = (uint8_t)e_b;
+                for (j = 0; j < 16; j++) {
+                    uint64_t idx = (uint64_t)(c * rows + r + j);
+                    put_nibble(codes, idx, encode(load(x, dtype, ld, r + j, c), r_b, rnd, seed, idx));
+                }
+            }
+        }
+    } else {
+        if (end > rows / 16)
+            end = rows / 16;
+#pragma omp parallel for schedule(static)
+        for (line = begin; line < end; line++) {
+            int64_t r = line * 16, c, i, j;
+            for (c = 0; c < cols; c += 16) {
+                float amax_b = 0.0f, r_b;
+                int e_b;
+                for (i = 0; i < 16; i++)
+                    for (j = 0; j < 16; j++) {
+                        float a = fabsf(load(x, dtype, ld, r + i, c + j));
+                        if (a > amax_b)
+                            amax_b = a;
+                    }
+                e_b = ora_block_scale(amax_b, s_enc);
+                r_b = ora_element_scale(e_b, s_enc);
+                scales[(r / 16) * (cols / 16) + c / 16] = (uint8_t)e_b;
+                if (scales_t)
+                    scales_t[(c / 16) * (rows / 16) + r / 16] = (uint8_t)e_b;
+                for (i = 0; i < 16; i++)
+                    for (j = 0; j < 16; j++) {
+                        uint64_t idx = (uint64_t)((r + i) * cols + c + j);
+                        int code = encode(load(x, dtype, ld, r + i, c + j), r_b, rnd, seed, idx);
+                        put_nibble(codes, idx, code);
+                        if (codes_t)
+                            put_nibble(codes_t, (uint64_t)((c + j) * rows + r + i), code);
+                    }
+            }
+        }
+    }
+    return 0;
+}
+
+int ora_quantize(const void *x, int dtype, int64_t rows, int64_t cols, int64_t ld,
+                 int layout, int rnd, uint64_t seed, uint8_t *codes, uint8_t *scales,
+                 uint8_t *codes_t, uint8_t *scales_t, float *tensor_scale, float *amax_out)
+{
+    return ora_quantize_range(x, dtype, rows, cols, ld, layout, rnd, seed, codes, scales,
+                              codes_t, scales_t, tensor_scale, amax_out, 0, INT64_MAX);
+}
+
+/* Random-Hadamard quantization of a Wgrad operand: x is tokens x cols; per
+ * column and per group of 16 consecutive tokens the 16 values go through
+ * ora_rht16, the tensor amax is taken over all transformed values, and each
+ * group is one 1D block.  Codes [cols][tokens/2], scales [cols][tokens/16]
+ * (token-contiguous, the layout the Wgrad contraction runs over); output
+ * index i = c*tokens + t.  Codes and scales are written for the columns in
+ * [begin, end) only. */
+int ora_rht_quantize_range(const void *x, int dtype, int64_t tokens, int64_t cols, int64_t ld,
+                           uint32_t sign_mask, int rnd, uint64_t seed, uint8_t *codes,
+                           uint8_t *scales, float *tensor_scale, float *amax_out,
+                           int64_t begin, int64_t end)
+{
+    int64_t line;
+    float amax_t = 0.0f, s_enc;
+    if (tokens <= 0 || cols <= 0 || tokens % 16 || cols % 16 || ld < cols || begin < 0)
+        return -1;
+#pragma omp parallel for reduction(max : amax_t) schedule(static)
+    for (line = 0; line < cols; line++) {
+        int64_t c = line, t, j;
+        float in[16], y[16];
+        for (t = 0; t < tokens; t += 16) {
+            for (j = 0; j < 16; j++)
+                in[j] = load(x, dtype, ld, t + j, c);
+            ora_rht16(in, sign_mask, y);
+            for (j = 0; j < 16; j++)
+                if (fabsf(y[j]) > amax_t)
+                    amax_t = fabsf(y[j]);
+        }
+    }
+    s_enc = ora_encode_scale(amax_t);
+    *amax_out = amax_t;
+    *tensor_scale = 1.0f / s_enc;
+    if (end > cols)
+        end = cols;
+#pragma omp parallel for schedule(static)
+    for (line = begin; line < end; line++) {
+        int64_t c = line, t, j;
+        float in[16], y[16];
+        for (t = 0; t < tokens; t += 16) {
+            float amax_b = 0.0f, r_b;
+            int e_b;
+            for (j = 0; j < 16; j++)
+                in[j] = load(x, dtype, ld, t + j, c);
+            ora_rht16(in, sign_mask, y);
+            for (j = 0; j < 16; j++)
+                if (fabsf(y[j]) > amax_b)
+                    amax_b = fabsf(y[j]);
+            e_b = ora_block_scale(amax_b, s_enc);
+            r_b = ora_element_scale(e_b, s_enc);
+            scales[c * (tokens / 16) + t / 16] = (uint8_t)e_b;
+            for (j = 0; j < 16; j++) {
+                uint64_t idx = (uint64_t)(c * tokens + t + j);
+                put_nibble(codes, idx, encode(y[j], r_b, rnd, seed, idx));
+            }
+        }
+    }
+    return 0;
+}
+
+int ora_rht_quantize(const void *x, int dtype, int64_t tokens, int64_t cols, int64_t ld,
+                     uint32_t sign_mask, int rnd, uint64_t seed, uint8_t *codes,
+                     uint8_t *scales, float *tensor_scale, float *amax_out)
+{
+    return ora_rht_quantize_range(x, dtype, tokens, cols, ld, sign_mask, rnd, seed, codes,
+                                  scales, tensor_scale, amax_out, 0, INT64_MAX);
+}
+
+/* Number of threads the OpenMP loops above use (1 without OpenMP). */
+int ora_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* ------------------------------------------------------------------ */
+/* Dequantization and the FP64 contraction                            */
+/* ------------------------------------------------------------------ */
+
+/* Dequantize n x k codes (row-major, k contiguous) to FP64:
+ * out = e2m1(code) * dec(scale) * s_t.  scale_rowdiv = 1 for 1D scales
+ * ([n][k/16]), 16 for a 16x16 tile grid ([n/16][k/16]).  Exact in FP64. */
+void ora_dequant(int64_t n, int64_t k, const uint8_t *codes, const uint8_t *scales,
+                 int scale_rowdiv, float s_t, double *out)
+{
+    int64_t r, c;
+    for (r = 0; r < n; r++)
+        for (c = 0; c < k; c++) {
+            int code = (codes[(r * k + c) >> 1] >> (((r * k + c) & 1) * 4)) & 15;
+            int e = scales[(r / scale_rowdiv) * (k / 16) + c / 16];
+            out[r * k + c] = ora_e2m1_value(code) * ora_e4m3_value(e) * (double)s_t;
+        }
+}
+
+/* C[m][n] = beta * C[m][n] + sum_k A[m][k] * B[n][k], all FP64, triple loop
+ * (for tiny shapes; large shapes use a BLAS dgemm on ora_dequant output). */
+void ora_gemm_f64(int64_t M, int64_t N, int64_t K, const double *A, const double *B,
+                  double beta, double *C)
+{
+    int64_t m, n, k;
+    for (m = 0; m < M; m++)
+        for (n = 0; n < N; n++) {
+            double s = 0.0;
+            for (k = 0; k < K; k++)
+                s += A[m * K + k] * B[n * K + k];
+            C[m * N + n] = (beta != 0.0 ? beta * C[m * N + n] : 0.0) + s;
+        }
+}
