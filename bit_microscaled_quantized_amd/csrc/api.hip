@@ -1,0 +1,98 @@
+// C-ABI entry points of libnvfp4 (declared and documented in include/nvfp4.h):
+// argument validation on the host, then asynchronous launches on the caller's
+// stream.  No allocation, no state.
+#include "../../include/nvfp4.h"
+#include "nvfp4_launch.hpp"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+nvfp4_status check_tensor(const void* x, int dt, int64_t rows, int64_t cols, int64_t ld) {
+  if (x == nullptr) return NVFP4_EINVAL;
+  if (dt != NVFP4_BF16 && dt != NVFP4_F32) return NVFP4_EINVAL;
+  if (rows <= 0 || cols <= 0 || rows % 16 != 0 || cols % 16 != 0) return NVFP4_ESHAPE;
+  if (ld < cols) return NVFP4_ESHAPE;
+  if (rows > ((int64_t(1) << 32) - 1) / cols) return NVFP4_ESHAPE;  // element indices fit 32 bits
+  if ((rows - 1) * ld + cols >= (int64_t(1) << 40)) return NVFP4_ESHAPE;
+  const int64_t esize = dt == NVFP4_BF16 ? 2 : 4;
+  if (!aligned16(x) || (ld * esize) % 16 != 0) return NVFP4_EALIGN;
+  return NVFP4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+nvfp4_status nvfp4_quantize(const void* x, int dt, int64_t rows, int64_t cols, int64_t ld_x,
+                            int layout, int rnd, uint64_t seed, uint8_t* codes, uint8_t* scales,
+                            uint8_t* codes_t, uint8_t* scales_t, float* tensor_scale, float* amax,
+                            void* stream) {
+  if (codes == nullptr || scales == nullptr || tensor_scale == nullptr || amax == nullptr)
+    return NVFP4_EINVAL;
+  if (layout != NVFP4_ROW_1D && layout != NVFP4_COL_1D && layout != NVFP4_TILE_2D) return NVFP4_EINVAL;
+  if (rnd != NVFP4_RNE && rnd != NVFP4_SR) return NVFP4_EINVAL;
+  if (layout != NVFP4_TILE_2D && (codes_t != nullptr || scales_t != nullptr)) return NVFP4_EINVAL;
+  if ((codes_t == nullptr) != (scales_t == nullptr)) return NVFP4_EINVAL;
+  nvfp4_status st = check_tensor(x, dt, rows, cols, ld_x);
+  if (st != NVFP4_OK) return st;
+  if (!aligned16(codes) || !aligned16(scales) || (codes_t && !aligned16(codes_t)) ||
+      (scales_t && !aligned16(scales_t)) || !aligned4(tensor_scale) || !aligned4(amax))
+    return NVFP4_EALIGN;
+  hipError_t e = nvfp4::launch_quantize(x, dt, rows, cols, ld_x, layout, rnd, seed, codes, scales,
+                                        codes_t, scales_t, tensor_scale, amax,
+                                        static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? NVFP4_OK : NVFP4_EHIP;
+}
+
+nvfp4_status nvfp4_rht_quantize(const void* x, int dt, int64_t tokens, int64_t cols, int64_t ld_x,
+                                uint32_t sign_mask, int rnd, uint64_t seed, uint8_t* codes,
+                                uint8_t* scales, float* tensor_scale, float* amax, void* stream) {
+  if (codes == nullptr || scales == nullptr || tensor_scale == nullptr || amax == nullptr)
+    return NVFP4_EINVAL;
+  if (rnd != NVFP4_RNE && rnd != NVFP4_SR) return NVFP4_EINVAL;
+  nvfp4_status st = check_tensor(x, dt, tokens, cols, ld_x);
+  if (st != NVFP4_OK) return st;
+  if (!aligned16(codes) || !aligned16(scales) || !aligned4(tensor_scale) || !aligned4(amax))
+    return NVFP4_EALIGN;
+  hipError_t e = nvfp4::launch_rht_quantize(x, dt, tokens, cols, ld_x, sign_mask, rnd, seed, codes,
+                                            scales, tensor_scale, amax,
+                                            static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? NVFP4_OK : NVFP4_EHIP;
+}
+
+nvfp4_status nvfp4_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
+                        const uint8_t* a_scales, const float* a_tensor_scale,
+                        const uint8_t* b_codes, const uint8_t* b_scales, int32_t b_scale_rowdiv,
+                        const float* b_tensor_scale, float* c, int64_t ldc, float beta,
+                        void* stream) {
+  if (a_codes == nullptr || a_scales == nullptr || a_tensor_scale == nullptr ||
+      b_codes == nullptr || b_scales == nullptr || b_tensor_scale == nullptr || c == nullptr)
+    return NVFP4_EINVAL;
+  if (b_scale_rowdiv != 1 && b_scale_rowdiv != 16) return NVFP4_EINVAL;
+  if (beta != 0.0f && beta != 1.0f) return NVFP4_EINVAL;
+  if (M <= 0 || N <= 0 || K <= 0 || M % 16 != 0 || N % 16 != 0 || K % 64 != 0) return NVFP4_ESHAPE;
+  if (M >= (int64_t(1) << 31) || N >= (int64_t(1) << 31) || K >= (int64_t(1) << 31)) return NVFP4_ESHAPE;
+  if (ldc < N) return NVFP4_ESHAPE;
+  if (!aligned16(a_codes) || !aligned16(b_codes) || !aligned4(a_scales) || !aligned4(b_scales) ||
+      !aligned4(a_tensor_scale) || !aligned4(b_tensor_scale) || !aligned16(c) || ldc % 4 != 0)
+    return NVFP4_EALIGN;
+  hipError_t e = nvfp4::launch_gemm(M, N, K, a_codes, a_scales, a_tensor_scale, b_codes, b_scales,
+                                    b_scale_rowdiv, b_tensor_scale, c, ldc, beta == 1.0f ? 1 : 0,
+                                    static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? NVFP4_OK : NVFP4_EHIP;
+}
+
+const char* nvfp4_status_str(int status) {
+  switch (status) {
+    case NVFP4_OK: return "NVFP4_OK";
+    case NVFP4_EINVAL: return "NVFP4_EINVAL: null pointer or invalid argument value";
+    case NVFP4_ESHAPE: return "NVFP4_ESHAPE: unsupported shape";
+    case NVFP4_EALIGN: return "NVFP4_EALIGN: misaligned pointer or leading dimension";
+    case NVFP4_EHIP: return "NVFP4_EHIP: HIP launch failed";
+    default: return "unknown nvfp4 status";
+  }
+}
+
+}  // extern "C"

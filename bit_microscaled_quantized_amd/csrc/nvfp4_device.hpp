@@ -1,0 +1,159 @@
+// Device-side NVFP4 helpers for gfx950.
+//
+// Format and scale rule (see include/nvfp4.h for the full statement):
+//   "Pretraining Large Language Models with NVFP4" (gist.science summary),
+//   Resumo tecnico, 2. Metodologia Proposta, "Formato NVFP4": 16-element
+//   blocks, E4M3 block scale, FP32 tensor scale.  E2M1 / E4M3 encodings per
+//   the OCP MX v1.0 and OCP OFP8 specifications.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
+
+constexpr float kFltMax = 3.402823466e+38f;
+
+// S_enc from the tensor amax: 2688 / amax (2688 = 6 * 448, the largest
+// E2M1 x E4M3 product), clamped to FLT_MAX, 1 for an all-zero tensor.
+__device__ __forceinline__ float encode_scale(float amax_t) {
+  if (!(amax_t > 0.0f)) return 1.0f;
+  return fminf(2688.0f / amax_t, kFltMax);
+}
+
+// E4M3 code of sb >= 0: nearest finite value, ties to the even code,
+// saturating at 448 (0x7E).  Subnormal codes k * 2^-9 (k <= 8, code 8 being
+// the smallest normal 2^-6) come from rounding sb * 2^9 to an integer; normal
+// codes from rounding the FP32 mantissa to 3 bits.
+__device__ __forceinline__ uint32_t e4m3_encode(float sb) {
+  if (!(sb > 0.0f)) return 0u;
+  if (sb >= 448.0f) return 0x7Eu;
+  if (sb < 0.015625f) return (uint32_t)__builtin_rintf(sb * 512.0f);
+  uint32_t b = __float_as_uint(sb);
+  uint32_t r = b + 0x7FFFFu + ((b >> 20) & 1u);
+  uint32_t code = (r >> 20) - (120u << 3);
+  return code < 0x7Eu ? code : 0x7Eu;
+}
+
+// Value of a finite non-negative E4M3 code.
+__device__ __forceinline__ float e4m3_decode(uint32_t e) {
+  if (e < 8u) return (float)e * 0.001953125f;
+  return __uint_as_float((e << 20) + (120u << 23));
+}
+
+// Multiplier mapping a block onto the E2M1 grid: S_enc / dec(e_b), 0 for an
+// empty scale, clamped to FLT_MAX so that v = y * r_b is never NaN.
+__device__ __forceinline__ float element_scale(uint32_t e_b, float s_enc) {
+  if (e_b == 0u) return 0.0f;
+  return fminf(s_enc / e4m3_decode(e_b), kFltMax);
+}
+
+// Block scale code and element multiplier from a block amax.
+__device__ __forceinline__ void block_scale(float amax_b, float s_enc, uint32_t& e_b, float& r_b) {
+  float t = amax_b / 6.0f;
+  float sb = t * s_enc;
+  e_b = e4m3_encode(sb);
+  r_b = element_scale(e_b, s_enc);
+}
+
+// Two values to two E2M1 codes, round-to-nearest-even with saturation, placed
+// in byte `sel` of `old` (v0 in the low nibble).  The gfx950 conversion with
+// scale 1.0 was checked against the nearest-even rule on every FP32 value.
+template <int sel>
+__device__ __forceinline__ uint32_t cvt_rne_pk(uint32_t old, float v0, float v1) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, v0, v1, 1.0f, sel);
+}
+
+// Pack eight scaled values into eight E2M1 codes (RNE), element 0 in the low
+// nibble of byte 0.
+__device__ __forceinline__ uint32_t pack8_rne(const float* v) {
+  uint32_t w = 0u;
+  w = cvt_rne_pk<0>(w, v[0], v[1]);
+  w = cvt_rne_pk<1>(w, v[2], v[3]);
+  w = cvt_rne_pk<2>(w, v[4], v[5]);
+  w = cvt_rne_pk<3>(w, v[6], v[7]);
+  return w;
+}
+
+// pcg hash (Jarzynski & Olano, "Hash Functions for GPU Rendering", JCGT 2020).
+__device__ __forceinline__ uint32_t pcg(uint32_t v) {
+  uint32_t state = v * 747796405u + 2891336453u;
+  uint32_t word = ((state >> ((state >> 28u) + 4u)) ^ state) * 277803737u;
+  return (word >> 22u) ^ word;
+}
+
+__host__ __device__ __forceinline__ uint32_t pcg_host(uint32_t v) {
+  uint32_t state = v * 747796405u + 2891336453u;
+  uint32_t word = ((state >> ((state >> 28u) + 4u)) ^ state) * 277803737u;
+  return (word >> 22u) ^ word;
+}
+
+// Stochastic rounding of a scaled value v to a 4-bit E2M1 code with 16
+// random bits r16: with a = min(|v|, 6), lo the largest E2M1 magnitude <= a
+// and hi the next one, round up iff r16 < (a - lo) / (hi - lo) * 65536.
+//   a >= 1  : lo is a with the FP32 mantissa cut to one bit, and the fraction
+//             times 2^22 is the 22 mantissa bits below it;
+//   a < 1   : step 0.5; for a >= 0.5 the fraction times 2^23 is the mantissa,
+//             below 0.5 the fraction is 2a (compared in FP32, exactly).
+__device__ __forceinline__ uint32_t sr_code(float v, uint32_t r16) {
+  uint32_t bits = __float_as_uint(v);
+  uint32_t sign = (bits >> 28) & 8u;
+  uint32_t b = bits & 0x7FFFFFFFu;
+  uint32_t idx;
+  if (b >= 0x40C00000u) {  // |v| >= 6 (or inf): saturate
+    idx = 7u;
+  } else if (b >= 0x3F800000u) {  // [1, 6)
+    uint32_t k = (b >> 22) - 252u;
+    idx = k + ((r16 << 6) < (b & 0x3FFFFFu) ? 1u : 0u);
+  } else if (b >= 0x3F000000u) {  // [0.5, 1)
+    idx = 1u + ((r16 << 7) < (b & 0x7FFFFFu) ? 1u : 0u);
+  } else {  // [0, 0.5)
+    idx = ((float)r16 < __uint_as_float(b) * 131072.0f) ? 1u : 0u;
+  }
+  return sign | idx;
+}
+
+// Random bits of the SR hash: key = pcg(lo32(seed) ^ pcg(hi32(seed))); one
+// pcg(key ^ (i >> 1)) per element pair, low half-word for the even element.
+__host__ __forceinline__ uint32_t sr_key(uint64_t seed) {
+  return pcg_host((uint32_t)seed ^ pcg_host((uint32_t)(seed >> 32)));
+}
+
+// Integer max over |bf16| pairs in a 32-bit word (sign bits cleared).
+__device__ __forceinline__ uint32_t absmax_bf16x2(uint32_t acc, uint32_t w) {
+  uint32_t a = w & 0x7FFF7FFFu;
+  uint32_t lo = a & 0xFFFFu, hi = a >> 16;
+  uint32_t m = lo > hi ? lo : hi;
+  return acc > m ? acc : m;
+}
+
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Radix-2 Walsh-Hadamard butterflies over 16 values with sign flips first and
+// the 1/4 normalization last: y = (1/4) H16 diag(d) x, Sylvester ordering.
+__device__ __forceinline__ void rht16(float* u, uint32_t sign_mask) {
+#pragma unroll
+  for (int j = 0; j < 16; j++)
+    if ((sign_mask >> j) & 1u) u[j] = -u[j];
+#pragma unroll
+  for (int h = 1; h < 16; h <<= 1) {
+#pragma unroll
+    for (int p = 0; p < 16; p++) {
+      if ((p & h) == 0) {
+        float a = u[p], b = u[p + h];
+        u[p] = a + b;
+        u[p + h] = a - b;
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 16; j++) u[j] = 0.25f * u[j];
+}
+
+}  // namespace nvfp4

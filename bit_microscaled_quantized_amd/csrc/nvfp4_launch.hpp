@@ -1,0 +1,23 @@
+// Kernel launchers shared by the C-ABI entry points (host side).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+hipError_t launch_quantize(const void* x, int dt, int64_t rows, int64_t cols, int64_t ld,
+                           int layout, int rnd, uint64_t seed, uint8_t* codes, uint8_t* scales,
+                           uint8_t* codes_t, uint8_t* scales_t, float* tensor_scale, float* amax,
+                           hipStream_t s);
+
+hipError_t launch_rht_quantize(const void* x, int dt, int64_t tokens, int64_t cols, int64_t ld,
+                               uint32_t sign_mask, int rnd, uint64_t seed, uint8_t* codes,
+                               uint8_t* scales, float* tensor_scale, float* amax, hipStream_t s);
+
+hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
+                       const uint8_t* a_scales, const float* a_ts, const uint8_t* b_codes,
+                       const uint8_t* b_scales, int b_rowdiv, const float* b_ts, float* c,
+                       int64_t ldc, int accumulate, hipStream_t s);
+
+}  // namespace nvfp4

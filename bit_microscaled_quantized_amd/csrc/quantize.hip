@@ -1,0 +1,525 @@
+// NVFP4 quantization kernels for gfx950: tensor amax, 1D row cast, 1D column
+// cast (optionally after the 16x16 random Hadamard transform) and 2D 16x16
+// tile cast with both orientations of the output.
+//
+// Method: "Pretraining Large Language Models with NVFP4" (gist.science
+// summary), Resumo tecnico, 2. Metodologia Proposta -- "Formato NVFP4"
+// (16-element blocks, E4M3 block scales, FP32 tensor scale) and techniques 2
+// (random Hadamard transform on the Wgrad inputs), 3 (16x16 2D weight
+// scaling) and 4 (stochastic rounding for gradients only).
+//
+// Every pass is bound by HBM bandwidth: loads are 16 bytes per lane and
+// contiguous across a wave, block maxima are reduced in registers (1D row:
+// with the partner lane through DPP), and the column and tile casts stage
+// their outputs through LDS so the transposed stores stay contiguous.
+#include "nvfp4_device.hpp"
+#include "nvfp4_launch.hpp"
+
+namespace nvfp4 {
+
+// ---------------------------------------------------------------------------
+// Tensor amax
+// ---------------------------------------------------------------------------
+
+__global__ void k_zero_amax(float* amax) {
+  if (threadIdx.x == 0 && blockIdx.x == 0) amax[0] = 0.0f;
+}
+
+// Per-block maximum of non-negative float bit patterns -> one atomicMax.
+__device__ __forceinline__ void block_atomic_max(uint32_t m, float* amax) {
+  __shared__ uint32_t red[8];
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    uint32_t o = __shfl_xor(m, off);
+    m = m > o ? m : o;
+  }
+  int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[wave] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t r = red[0];
+    for (int w = 1; w < (int)(blockDim.x >> 6); w++) r = r > red[w] ? r : red[w];
+    if (r != 0u) atomicMax(reinterpret_cast<unsigned int*>(amax), r);
+  }
+}
+
+// amax over a rows x cols tensor with leading dimension ld (elements).  Each
+// thread takes UNROLL 16-byte chunks per round, contiguous across the block.
+template <typename T, int UNROLL>
+__global__ __launch_bounds__(256) void k_amax(const T* __restrict__ x, int64_t rows, int64_t cols,
+                                              int64_t ld, float* amax) {
+  constexpr int EPC = 16 / sizeof(T);  // elements per 16-byte chunk
+  const int64_t cpr = cols / EPC;       // chunks per row
+  uint32_t m = 0u;
+  for (int64_t r = blockIdx.y; r < rows; r += gridDim.y) {
+    const uint4* row = reinterpret_cast<const uint4*>(x + r * ld);
+    for (int64_t base = (int64_t)blockIdx.x * 256 * UNROLL; base < cpr;
+         base += (int64_t)gridDim.x * 256 * UNROLL) {
+      uint4 v[UNROLL];
+#pragma unroll
+      for (int j = 0; j < UNROLL; j++) {
+        int64_t c = base + j * 256 + threadIdx.x;
+        v[j] = c < cpr ? row[c] : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int j = 0; j < UNROLL; j++) {
+        if constexpr (sizeof(T) == 2) {
+          m = absmax_bf16x2(m, v[j].x);
+          m = absmax_bf16x2(m, v[j].y);
+          m = absmax_bf16x2(m, v[j].z);
+          m = absmax_bf16x2(m, v[j].w);
+        } else {
+          uint32_t a = v[j].x & 0x7FFFFFFFu, b = v[j].y & 0x7FFFFFFFu;
+          uint32_t c = v[j].z & 0x7FFFFFFFu, d = v[j].w & 0x7FFFFFFFu;
+          a = a > b ? a : b;
+          c = c > d ? c : d;
+          a = a > c ? a : c;
+          m = m > a ? m : a;
+        }
+      }
+    }
+  }
+  if constexpr (sizeof(T) == 2) m <<= 16;
+  block_atomic_max(m, amax);
+}
+
+// ---------------------------------------------------------------------------
+// Element loads: 8 consecutive elements as FP32
+// ---------------------------------------------------------------------------
+
+template <typename T>
+__device__ __forceinline__ void load8(const T* p, float* v);
+
+template <>
+__device__ __forceinline__ void load8<uint16_t>(const uint16_t* p, float* v) {
+  uint4 w = *reinterpret_cast<const uint4*>(p);
+  v[0] = bf16lo(w.x); v[1] = bf16hi(w.x);
+  v[2] = bf16lo(w.y); v[3] = bf16hi(w.y);
+  v[4] = bf16lo(w.z); v[5] = bf16hi(w.z);
+  v[6] = bf16lo(w.w); v[7] = bf16hi(w.w);
+}
+
+template <>
+__device__ __forceinline__ void load8<float>(const float* p, float* v) {
+  float4 a = *reinterpret_cast<const float4*>(p);
+  float4 b = *reinterpret_cast<const float4*>(p + 4);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+
+// Encode 8 scaled values: RNE through the hardware conversion, SR in
+// software with pcg bits for output elements idx0 .. idx0 + 7 (idx0 even).
+template <int RND>
+__device__ __forceinline__ uint32_t encode8(const float* v, uint32_t key, uint32_t pair0) {
+  if constexpr (RND == 0) {
+    return pack8_rne(v);
+  } else {
+    uint32_t w = 0u;
+#pragma unroll
+    for (int p = 0; p < 4; p++) {
+      uint32_t h = pcg(key ^ (pair0 + p));
+      uint32_t c0 = sr_code(v[2 * p], h & 0xFFFFu);
+      uint32_t c1 = sr_code(v[2 * p + 1], h >> 16);
+      w |= (c0 | (c1 << 4)) << (8 * p);
+    }
+    return w;
+  }
+}
+
+__device__ __forceinline__ float dpp_swap_pair(float x) {
+  // quad_perm [1,0,3,2]: exchange with the neighbouring lane
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));
+}
+
+// ---------------------------------------------------------------------------
+// 1D row cast: blocks of 16 along a row.  Lane pairs hold one block (8
+// elements each); UNROLL half-blocks per lane per round, contiguous across the
+// workgroup.  codes [rows][cols/2], scales [rows][cols/16].
+// ---------------------------------------------------------------------------
+template <typename T, int RND, int UNROLL>
+__global__ __launch_bounds__(256) void k_cast_row1d(const T* __restrict__ x, int64_t rows,
+                                                    int64_t cols, int64_t ld,
+                                                    const float* __restrict__ amax,
+                                                    uint8_t* __restrict__ codes,
+                                                    uint8_t* __restrict__ scales,
+                                                    float* __restrict__ tensor_scale, uint32_t key) {
+  const float s_enc = encode_scale(amax[0]);
+  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) tensor_scale[0] = 1.0f / s_enc;
+  const int64_t items = cols / 8;  // half-blocks per row
+  for (int64_t r = blockIdx.y; r < rows; r += gridDim.y) {
+    const T* row = x + r * ld;
+    uint32_t* crow = reinterpret_cast<uint32_t*>(codes + r * (cols / 2));
+    uint8_t* srow = scales + r * (cols / 16);
+    const uint32_t row_index = (uint32_t)(r * cols);
+    for (int64_t base = (int64_t)blockIdx.x * 256 * UNROLL; base < items;
+         base += (int64_t)gridDim.x * 256 * UNROLL) {
+      float v[UNROLL][8];
+#pragma unroll
+      for (int j = 0; j < UNROLL; j++) {
+        int64_t it = base + j * 256 + threadIdx.x;
+        if (it < items) {
+          load8<T>(row + it * 8, v[j]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; e++) v[j][e] = 0.0f;
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < UNROLL; j++) {
+        int64_t it = base + j * 256 + threadIdx.x;
+        float am = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; e++) am = fmaxf(am, fabsf(v[j][e]));
+        am = fmaxf(am, dpp_swap_pair(am));
+        uint32_t e_b;
+        float r_b;
+        block_scale(am, s_enc, e_b, r_b);
+        float s[8];
+#pragma unroll
+        for (int e = 0; e < 8; e++) s[e] = v[j][e] * r_b;
+        if (it < items) {
+          uint32_t pair0 = (row_index + (uint32_t)(it * 8)) >> 1;
+          crow[it] = encode8<RND>(s, key, pair0);
+          if ((threadIdx.x & 1) == 0) srow[it >> 1] = (uint8_t)e_b;
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 1D column cast (COL_1D, and the Wgrad RHT path): blocks of 16 consecutive
+// rows (tokens) in one column, written transposed.  A workgroup covers 512
+// tokens x 64 columns: thread (g, co) loads 16 rows x 8 columns (16-byte
+// row segments, 8 threads per 128-byte line), transforms and encodes its 8
+// column blocks, and stages codes and scales in LDS so each output row
+// (one input column) is written as contiguous 16-byte pieces.
+// codes [cols][rows/2], scales [cols][rows/16].
+// ---------------------------------------------------------------------------
+constexpr int kColTok = 512;  // tokens per workgroup tile
+constexpr int kColCols = 64;  // columns per workgroup tile
+
+template <typename T>
+__device__ __forceinline__ void load_col8(const T* p, float* v) {
+  load8<T>(p, v);
+}
+
+template <typename T, int RND, bool RHT>
+__global__ __launch_bounds__(256) void k_cast_col1d(const T* __restrict__ x, int64_t rows,
+                                                    int64_t cols, int64_t ld, uint32_t sign_mask,
+                                                    const float* __restrict__ amax,
+                                                    uint8_t* __restrict__ codes,
+                                                    uint8_t* __restrict__ scales,
+                                                    float* __restrict__ tensor_scale, uint32_t key) {
+  __shared__ __align__(16) uint8_t lcodes[kColCols][kColTok / 2];
+  __shared__ __align__(16) uint8_t lscales[kColCols][kColTok / 16];
+  const float s_enc = encode_scale(amax[0]);
+  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) tensor_scale[0] = 1.0f / s_enc;
+
+  const int64_t t0 = (int64_t)blockIdx.y * kColTok;
+  const int64_t c0 = (int64_t)blockIdx.x * kColCols;
+  const int co = threadIdx.x & 7;   // column octet
+  const int g = threadIdx.x >> 3;   // 16-token group within the tile
+  const int64_t tg = t0 + 16 * g;   // first token of the group
+  const int64_t cc = c0 + 8 * co;   // first column of the octet
+  const bool valid = tg < rows && cc < cols;
+
+  float u[8][16];
+  if (valid) {
+#pragma unroll
+    for (int j = 0; j < 16; j++) {
+      float v[8];
+      load_col8<T>(x + (tg + j) * ld + cc, v);
+#pragma unroll
+      for (int k = 0; k < 8; k++) u[k][j] = v[k];
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < 8; k++) {
+    uint32_t e_b = 0u;
+    uint32_t w0 = 0u, w1 = 0u;
+    if (valid) {
+      if constexpr (RHT) rht16(u[k], sign_mask);
+      float am = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 16; j++) am = fmaxf(am, fabsf(u[k][j]));
+      float r_b;
+      block_scale(am, s_enc, e_b, r_b);
+      float s[16];
+#pragma unroll
+      for (int j = 0; j < 16; j++) s[j] = u[k][j] * r_b;
+      uint32_t pair0 = (uint32_t)((cc + k) * rows + tg) >> 1;
+      w0 = encode8<RND>(s, key, pair0);
+      w1 = encode8<RND>(s + 8, key, pair0 + 4);
+    }
+    *reinterpret_cast<uint2*>(&lcodes[8 * co + k][8 * g]) = make_uint2(w0, w1);
+    lscales[8 * co + k][g] = (uint8_t)e_b;
+  }
+  __syncthreads();
+
+  // codes: 64 rows of 256 bytes; 16 threads per row, 16 bytes each
+  const int64_t row_bytes = rows / 2;
+  for (int pass = 0; pass < 4; pass++) {
+    int lc = pass * 16 + (threadIdx.x >> 4);  // local column
+    int piece = threadIdx.x & 15;
+    int64_t c = c0 + lc;
+    int64_t off = t0 / 2 + 16 * piece;  // byte offset within the output row
+    if (c < cols && off < row_bytes) {
+      uint8_t* dst = codes + c * row_bytes + off;
+      const uint2* src = reinterpret_cast<const uint2*>(&lcodes[lc][16 * piece]);
+      // row_bytes is a multiple of 8; 16-byte stores only where aligned
+      if (off + 16 <= row_bytes && ((c * row_bytes + off) & 15) == 0) {
+        *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+      } else {
+        reinterpret_cast<uint2*>(dst)[0] = src[0];
+        if (off + 16 <= row_bytes) reinterpret_cast<uint2*>(dst)[1] = src[1];
+      }
+    }
+  }
+  // scales: 64 rows of 32 bytes; 2 threads per row, 16 bytes each
+  if (threadIdx.x < 128) {
+    int lc = threadIdx.x >> 1;
+    int piece = threadIdx.x & 1;
+    int64_t c = c0 + lc;
+    const int64_t srow = rows / 16;
+    int64_t off = t0 / 16 + 16 * piece;
+    if (c < cols && off < srow) {
+      uint8_t* dst = scales + c * srow + off;
+      const uint8_t* src = &lscales[lc][16 * piece];
+      if (off + 16 <= srow && ((c * srow + off) & 15) == 0) {
+        *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+      } else {
+        for (int b = 0; b < 16 && off + b < srow; b++) dst[b] = src[b];
+      }
+    }
+  }
+}
+
+// amax of the RHT output: same thread mapping as the column cast, no LDS.
+template <typename T>
+__global__ __launch_bounds__(256) void k_rht_amax(const T* __restrict__ x, int64_t rows,
+                                                  int64_t cols, int64_t ld, uint32_t sign_mask,
+                                                  float* amax) {
+  const int64_t t0 = (int64_t)blockIdx.y * kColTok;
+  const int64_t c0 = (int64_t)blockIdx.x * kColCols;
+  const int co = threadIdx.x & 7;
+  const int g = threadIdx.x >> 3;
+  const int64_t tg = t0 + 16 * g;
+  const int64_t cc = c0 + 8 * co;
+  float am = 0.0f;
+  if (tg < rows && cc < cols) {
+    float u[8][16];
+#pragma unroll
+    for (int j = 0; j < 16; j++) {
+      float v[8];
+      load_col8<T>(x + (tg + j) * ld + cc, v);
+#pragma unroll
+      for (int k = 0; k < 8; k++) u[k][j] = v[k];
+    }
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+      rht16(u[k], sign_mask);
+#pragma unroll
+      for (int j = 0; j < 16; j++) am = fmaxf(am, fabsf(u[k][j]));
+    }
+  }
+  block_atomic_max(__float_as_uint(am), amax);
+}
+
+// ---------------------------------------------------------------------------
+// 2D tile cast: one scale per 16x16 tile.  A workgroup covers 64 x 64
+// elements; wave w takes rows 16w..16w+15, lane l holds row l%16 of tile
+// column l/16 (16 elements).  The tile amax is reduced over the 16 lanes of
+// a tile.  Row-major codes go straight out (8 bytes per lane, 4 lanes per
+// 32-byte row piece); the transposed codes are rebuilt from an LDS copy of
+// the unpacked codes in column-major order.
+// codes [rows][cols/2], scales [rows/16][cols/16],
+// codes_t [cols][rows/2], scales_t [cols/16][rows/16].
+// ---------------------------------------------------------------------------
+template <typename T, int RND>
+__global__ __launch_bounds__(256) void k_cast_tile2d(const T* __restrict__ x, int64_t rows,
+                                                     int64_t cols, int64_t ld,
+                                                     const float* __restrict__ amax,
+                                                     uint8_t* __restrict__ codes,
+                                                     uint8_t* __restrict__ scales,
+                                                     uint8_t* __restrict__ codes_t,
+                                                     uint8_t* __restrict__ scales_t,
+                                                     float* __restrict__ tensor_scale, uint32_t key) {
+  __shared__ __align__(16) uint8_t lt[64][64 + 16];  // [local col][local row], padded
+  const float s_enc = encode_scale(amax[0]);
+  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) tensor_scale[0] = 1.0f / s_enc;
+
+  const int64_t r0 = (int64_t)blockIdx.y * 64;
+  const int64_t c0 = (int64_t)blockIdx.x * 64;
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int tc = lane >> 4;  // tile column in the region
+  const int rr = lane & 15;  // row within the tile
+  const int lr = 16 * wave + rr;  // local row
+  const int64_t r = r0 + lr;
+  const int64_t c = c0 + 16 * tc;
+  const bool tile_valid = (r0 + 16 * wave) < rows && c < cols;  // whole tile in or out
+
+  float v[16];
+  if (tile_valid) {
+    load8<T>(x + r * ld + c, v);
+    load8<T>(x + r * ld + c + 8, v + 8);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 16; e++) v[e] = 0.0f;
+  }
+  float am = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 16; e++) am = fmaxf(am, fabsf(v[e]));
+#pragma unroll
+  for (int off = 1; off < 16; off <<= 1) am = fmaxf(am, __shfl_xor(am, off));
+  uint32_t e_b;
+  float r_b;
+  block_scale(am, s_enc, e_b, r_b);
+  float s[16];
+#pragma unroll
+  for (int e = 0; e < 16; e++) s[e] = v[e] * r_b;
+  const uint32_t pair0 = (uint32_t)(r * cols + c) >> 1;
+  uint32_t w0 = encode8<RND>(s, key, pair0);
+  uint32_t w1 = encode8<RND>(s + 8, key, pair0 + 4);
+  if (tile_valid) {
+    *reinterpret_cast<uint2*>(codes + r * (cols / 2) + c / 2) = make_uint2(w0, w1);
+    if (rr == 0) {
+      scales[(r / 16) * (cols / 16) + c / 16] = (uint8_t)e_b;
+      if (scales_t) scales_t[(c / 16) * (rows / 16) + r / 16] = (uint8_t)e_b;
+    }
+  }
+  if (codes_t == nullptr) return;
+  // unpacked codes, column-major in LDS
+#pragma unroll
+  for (int e = 0; e < 8; e++) {
+    lt[16 * tc + e][lr] = (uint8_t)((w0 >> (4 * e)) & 15u);
+    lt[16 * tc + 8 + e][lr] = (uint8_t)((w1 >> (4 * e)) & 15u);
+  }
+  __syncthreads();
+  // thread -> (local column, quarter of the rows): 16 rows -> 8 bytes
+  const int lc = threadIdx.x >> 2;
+  const int q = threadIdx.x & 3;
+  const int64_t ct = c0 + lc;
+  const int64_t rq = r0 + 16 * q;
+  if (ct < cols && rq < rows) {
+    uint4 b = *reinterpret_cast<const uint4*>(&lt[lc][16 * q]);
+    uint32_t in[4] = {b.x, b.y, b.z, b.w};
+    uint32_t out[2];
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+      uint32_t a0 = in[2 * h], a1 = in[2 * h + 1];
+      // bytes (codes) c0..c3 of a0 and c4..c7 of a1 -> nibbles
+      uint32_t o = (a0 & 0xFu) | ((a0 >> 4) & 0xF0u) | ((a0 >> 8) & 0xF00u) | ((a0 >> 12) & 0xF000u);
+      o |= ((a1 & 0xFu) | ((a1 >> 4) & 0xF0u) | ((a1 >> 8) & 0xF00u) | ((a1 >> 12) & 0xF000u)) << 16;
+      out[h] = o;
+    }
+    *reinterpret_cast<uint2*>(codes_t + ct * (rows / 2) + rq / 2) = make_uint2(out[0], out[1]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Launchers
+// ---------------------------------------------------------------------------
+
+static inline unsigned grid_cap(int64_t want, int64_t cap) {
+  if (want < 1) want = 1;
+  return (unsigned)(want < cap ? want : cap);
+}
+
+template <typename T>
+static hipError_t launch_amax(const void* x, int64_t rows, int64_t cols, int64_t ld, float* amax,
+                              hipStream_t s) {
+  constexpr int EPC = 16 / sizeof(T);
+  constexpr int UNROLL = 4;
+  if (ld == cols) {  // contiguous: one long row
+    cols = rows * cols;
+    ld = cols;
+    rows = 1;
+  }
+  int64_t cpr = cols / EPC;
+  dim3 grid(grid_cap((cpr + 256 * UNROLL - 1) / (256 * UNROLL), 8192), grid_cap(rows, 65535));
+  k_amax<T, UNROLL><<<grid, 256, 0, s>>>(static_cast<const T*>(x), rows, cols, ld, amax);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize(const void* x, int dt, int64_t rows, int64_t cols, int64_t ld,
+                           int layout, int rnd, uint64_t seed, uint8_t* codes, uint8_t* scales,
+                           uint8_t* codes_t, uint8_t* scales_t, float* tensor_scale, float* amax,
+                           hipStream_t s) {
+  k_zero_amax<<<1, 64, 0, s>>>(amax);
+  hipError_t e = dt == 0 ? launch_amax<uint16_t>(x, rows, cols, ld, amax, s)
+                         : launch_amax<float>(x, rows, cols, ld, amax, s);
+  if (e != hipSuccess) return e;
+  const uint32_t key = sr_key(seed);
+  if (layout == 0) {
+    constexpr int UNROLL = 4;
+    int64_t r = rows, c = cols, l = ld;
+    if (ld == cols) {
+      c = rows * cols;
+      l = c;
+      r = 1;
+    }
+    int64_t items = c / 8;
+    dim3 grid(grid_cap((items + 256 * UNROLL - 1) / (256 * UNROLL), 8192), grid_cap(r, 65535));
+#define ROW_LAUNCH(T, R)                                                                        \
+  k_cast_row1d<T, R, UNROLL><<<grid, 256, 0, s>>>(static_cast<const T*>(x), r, c, l, amax, codes, \
+                                                  scales, tensor_scale, key)
+    if (dt == 0) {
+      if (rnd == 0) ROW_LAUNCH(uint16_t, 0); else ROW_LAUNCH(uint16_t, 1);
+    } else {
+      if (rnd == 0) ROW_LAUNCH(float, 0); else ROW_LAUNCH(float, 1);
+    }
+#undef ROW_LAUNCH
+  } else if (layout == 1) {
+    dim3 grid((unsigned)((cols + kColCols - 1) / kColCols), (unsigned)((rows + kColTok - 1) / kColTok));
+#define COL_LAUNCH(T, R)                                                                          \
+  k_cast_col1d<T, R, false><<<grid, 256, 0, s>>>(static_cast<const T*>(x), rows, cols, ld, 0u, amax, \
+                                                 codes, scales, tensor_scale, key)
+    if (dt == 0) {
+      if (rnd == 0) COL_LAUNCH(uint16_t, 0); else COL_LAUNCH(uint16_t, 1);
+    } else {
+      if (rnd == 0) COL_LAUNCH(float, 0); else COL_LAUNCH(float, 1);
+    }
+#undef COL_LAUNCH
+  } else {
+    dim3 grid((unsigned)((cols + 63) / 64), (unsigned)((rows + 63) / 64));
+#define TILE_LAUNCH(T, R)                                                                  \
+  k_cast_tile2d<T, R><<<grid, 256, 0, s>>>(static_cast<const T*>(x), rows, cols, ld, amax, \
+                                           codes, scales, codes_t, scales_t, tensor_scale, key)
+    if (dt == 0) {
+      if (rnd == 0) TILE_LAUNCH(uint16_t, 0); else TILE_LAUNCH(uint16_t, 1);
+    } else {
+      if (rnd == 0) TILE_LAUNCH(float, 0); else TILE_LAUNCH(float, 1);
+    }
+#undef TILE_LAUNCH
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_rht_quantize(const void* x, int dt, int64_t tokens, int64_t cols, int64_t ld,
+                               uint32_t sign_mask, int rnd, uint64_t seed, uint8_t* codes,
+                               uint8_t* scales, float* tensor_scale, float* amax, hipStream_t s) {
+  sign_mask &= 0xFFFFu;
+  k_zero_amax<<<1, 64, 0, s>>>(amax);
+  dim3 grid((unsigned)((cols + kColCols - 1) / kColCols), (unsigned)((tokens + kColTok - 1) / kColTok));
+  if (dt == 0)
+    k_rht_amax<uint16_t><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(x), tokens, cols, ld, sign_mask, amax);
+  else
+    k_rht_amax<float><<<grid, 256, 0, s>>>(static_cast<const float*>(x), tokens, cols, ld, sign_mask, amax);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const uint32_t key = sr_key(seed);
+#define RHT_LAUNCH(T, R)                                                                         \
+  k_cast_col1d<T, R, true><<<grid, 256, 0, s>>>(static_cast<const T*>(x), tokens, cols, ld,       \
+                                                sign_mask, amax, codes, scales, tensor_scale, key)
+  if (dt == 0) {
+    if (rnd == 0) RHT_LAUNCH(uint16_t, 0); else RHT_LAUNCH(uint16_t, 1);
+  } else {
+    if (rnd == 0) RHT_LAUNCH(float, 0); else RHT_LAUNCH(float, 1);
+  }
+#undef RHT_LAUNCH
+  return hipGetLastError();
+}
+
+}  // namespace nvfp4

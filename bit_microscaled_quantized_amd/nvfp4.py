@@ -1,0 +1,110 @@
+"""Python binding of libnvfp4 (include/nvfp4.h): argument marshalling only.
+
+Each function has the name and the argument order of its C entry point.  Tensor
+arguments may be torch tensors (their data_ptr is passed), raw integer device
+addresses, or None for NULL.  `stream=None` means torch's current stream on the
+current device.  Every step of the computation runs in the HIP library; if the
+library is missing or fails to load, the call raises -- there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libnvfp4.so")
+
+NVFP4_OK, NVFP4_EINVAL, NVFP4_ESHAPE, NVFP4_EALIGN, NVFP4_EHIP = range(5)
+NVFP4_BF16, NVFP4_F32 = 0, 1
+NVFP4_RNE, NVFP4_SR = 0, 1
+NVFP4_ROW_1D, NVFP4_COL_1D, NVFP4_TILE_2D = 0, 1, 2
+
+EXPORTED = ("nvfp4_quantize", "nvfp4_rht_quantize", "nvfp4_gemm", "nvfp4_status_str")
+
+_lib = None
+
+
+class Nvfp4Error(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn} failed: {msg} (status {status})")
+        self.status = status
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libnvfp4.so (built by bit_microscaled_quantized_amd.build)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is missing: build it with "
+                           "`python -m bit_microscaled_quantized_amd.build`")
+    L = ctypes.CDLL(_LIB_PATH)
+    i64, u64, u32, i32 = ctypes.c_int64, ctypes.c_uint64, ctypes.c_uint32, ctypes.c_int
+    vp, f32 = ctypes.c_void_p, ctypes.c_float
+    L.nvfp4_quantize.argtypes = [vp, i32, i64, i64, i64, i32, i32, u64, vp, vp, vp, vp, vp, vp, vp]
+    L.nvfp4_quantize.restype = i32
+    L.nvfp4_rht_quantize.argtypes = [vp, i32, i64, i64, i64, u32, i32, u64, vp, vp, vp, vp, vp]
+    L.nvfp4_rht_quantize.restype = i32
+    L.nvfp4_gemm.argtypes = [i64, i64, i64, vp, vp, vp, vp, vp, i32, vp, vp, i64, f32, vp]
+    L.nvfp4_gemm.restype = i32
+    L.nvfp4_status_str.argtypes = [i32]
+    L.nvfp4_status_str.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def _addr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def nvfp4_status_str(status: int) -> str:
+    return load_library().nvfp4_status_str(status).decode()
+
+
+def _check(fn: str, status: int, raise_on_error: bool) -> int:
+    if status != NVFP4_OK and raise_on_error:
+        raise Nvfp4Error(fn, status, nvfp4_status_str(status))
+    return status
+
+
+def nvfp4_quantize(x, dt, rows, cols, ld_x, layout, rnd, seed, codes, scales, codes_t,
+                   scales_t, tensor_scale, amax, stream=None, raise_on_error=True) -> int:
+    st = load_library().nvfp4_quantize(
+        _addr(x), dt, rows, cols, ld_x, layout, rnd, seed & (2 ** 64 - 1), _addr(codes),
+        _addr(scales), _addr(codes_t), _addr(scales_t), _addr(tensor_scale), _addr(amax),
+        _stream(stream))
+    return _check("nvfp4_quantize", st, raise_on_error)
+
+
+def nvfp4_rht_quantize(x, dt, tokens, cols, ld_x, sign_mask, rnd, seed, codes, scales,
+                       tensor_scale, amax, stream=None, raise_on_error=True) -> int:
+    st = load_library().nvfp4_rht_quantize(
+        _addr(x), dt, tokens, cols, ld_x, sign_mask & 0xFFFFFFFF, rnd, seed & (2 ** 64 - 1),
+        _addr(codes), _addr(scales), _addr(tensor_scale), _addr(amax), _stream(stream))
+    return _check("nvfp4_rht_quantize", st, raise_on_error)
+
+
+def nvfp4_gemm(M, N, K, a_codes, a_scales, a_tensor_scale, b_codes, b_scales, b_scale_rowdiv,
+               b_tensor_scale, c, ldc, beta, stream=None, raise_on_error=True) -> int:
+    st = load_library().nvfp4_gemm(
+        M, N, K, _addr(a_codes), _addr(a_scales), _addr(a_tensor_scale), _addr(b_codes),
+        _addr(b_scales), b_scale_rowdiv, _addr(b_tensor_scale), _addr(c), ldc, float(beta),
+        _stream(stream))
+    return _check("nvfp4_gemm", st, raise_on_error)

@@ -1,0 +1,149 @@
+/*
+ * libnvfp4 -- NVFP4 quantize-and-contract for one linear layer on MI355X (gfx950).
+ *
+ * The method ("Pretraining Large Language Models with NVFP4", gist.science
+ * summary, section "Resumo tecnico", part 2 "Metodologia Proposta"):
+ *   - NVFP4 stores FP4 (E2M1) values in blocks of 16 with one FP8 E4M3 scale
+ *     per block and one FP32 scale per tensor (bullets "Bloco Menor",
+ *     "Fatores de Escala Precisos", "Escala em Dois Niveis");
+ *   - weights are scaled per 16x16 tile so forward and backward use the same
+ *     quantized weight (technique 3, "Escala Bidimensional (2D) para Pesos");
+ *   - the Wgrad inputs go through a 16x16 random Hadamard transform
+ *     (technique 2; the 16x16 size is stated in "NVIDIA cria metodo para
+ *     treinar redes neurais com precisao de 4 bits", section "Como funciona");
+ *   - gradients use stochastic rounding, everything else round-to-nearest-even
+ *     (technique 4, "Arredondamento Estocastico").
+ * Arithmetic details the pages leave open are fixed as follows (IEEE binary32,
+ * round-to-nearest-even, in this order):
+ *   amax_t = max |y| over the tensor (y = x, or the RHT output)
+ *   S_enc  = amax_t > 0 ? min(2688 / amax_t, FLT_MAX) : 1;  tensor_scale = 1 / S_enc
+ *   e_b    = E4M3 nearest-even, saturating at 448, of (amax_b / 6) * S_enc
+ *   r_b    = e_b == 0 ? 0 : min(S_enc / dec(e_b), FLT_MAX);   v = y * r_b
+ *   code   = sign(y) << 3 | E2M1 index of |v|: RNE (ties to even index,
+ *            saturating at 6) or SR (round up iff r16 < frac * 65536, r16 =
+ *            16 bits of the pcg hash of Jarzynski & Olano, JCGT 2020, keyed by
+ *            the seed and the element's index in the output code array).
+ *   Dequantized value = e2m1(code) * dec(e_b) * tensor_scale.
+ *
+ * Packing: two codes per byte, the even element in the low nibble.
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers owned by the caller.  The library
+ *     allocates and frees nothing, keeps no state between calls and is
+ *     reentrant; calls on different streams may overlap.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
+ *     work is enqueued asynchronously on it; results are visible after the
+ *     caller synchronizes that stream.
+ *   - Argument errors are detected on the host before anything is enqueued and
+ *     return NVFP4_EINVAL / NVFP4_ESHAPE / NVFP4_EALIGN; NVFP4_EHIP means a
+ *     launch failed.  Faults during execution surface at the caller's
+ *     synchronization.
+ *   - Inputs must be finite; codes for NaN/Inf inputs are unspecified.
+ *   - Tensor element counts must stay below 2^32.
+ */
+#ifndef NVFP4_H
+#define NVFP4_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    NVFP4_OK = 0,
+    NVFP4_EINVAL = 1, /* null pointer, unknown enum value, bad rowdiv/beta */
+    NVFP4_ESHAPE = 2, /* dimension not a multiple of 16 (quantize) or of the GEMM tile */
+    NVFP4_EALIGN = 3, /* pointer or leading dimension not 16-byte aligned */
+    NVFP4_EHIP = 4    /* a HIP launch failed */
+} nvfp4_status;
+
+typedef enum { NVFP4_BF16 = 0, NVFP4_F32 = 1 } nvfp4_dtype;
+typedef enum { NVFP4_RNE = 0, NVFP4_SR = 1 } nvfp4_rounding;
+typedef enum { NVFP4_ROW_1D = 0, NVFP4_COL_1D = 1, NVFP4_TILE_2D = 2 } nvfp4_layout;
+
+/*
+ * nvfp4_quantize -- amax, two-level scales and E2M1 cast of one tensor.
+ * ("Formato NVFP4" and techniques 3-4 of "Metodologia Proposta".)
+ *
+ *   x        [rows x cols] row-major, element type `dt`, leading dimension ld_x
+ *            elements (ld_x >= cols; ld_x * elem_size a multiple of 16 bytes).
+ *   layout   NVFP4_ROW_1D : blocks of 16 along a row (activations X for Fprop,
+ *                           gradients dY for Dgrad).
+ *                codes  [rows][cols/2], scales [rows][cols/16]
+ *            NVFP4_COL_1D : blocks of 16 along a column, written transposed
+ *                           (token-contiguous Wgrad operand without the RHT).
+ *                codes  [cols][rows/2], scales [cols][rows/16]
+ *            NVFP4_TILE_2D: one scale per 16x16 tile (weights).
+ *                codes  [rows][cols/2], scales [rows/16][cols/16]
+ *                codes_t [cols][rows/2], scales_t [cols/16][rows/16]: the SAME
+ *                quantized values transposed (the Dgrad operand); both may be
+ *                NULL to skip them.  Must be NULL for the 1D layouts.
+ *   rnd, seed  NVFP4_RNE, or NVFP4_SR with the 64-bit hash seed.  The SR index
+ *              of an element is its position in `codes` (r*cols + c for
+ *              ROW_1D and TILE_2D, c*rows + r for COL_1D).
+ *   tensor_scale, amax  one float each (device): outputs 1/S_enc and amax_t.
+ *   rows, cols must be positive multiples of 16; all pointers 16-byte aligned
+ *   except tensor_scale / amax (4-byte).
+ */
+nvfp4_status nvfp4_quantize(const void *x, int dt, int64_t rows, int64_t cols, int64_t ld_x,
+                            int layout, int rnd, uint64_t seed, uint8_t *codes, uint8_t *scales,
+                            uint8_t *codes_t, uint8_t *scales_t, float *tensor_scale,
+                            float *amax, void *stream);
+
+/*
+ * nvfp4_rht_quantize -- random Hadamard transform along tokens, then 1D
+ * column quantization of a Wgrad operand (technique 2 of "Metodologia
+ * Proposta"; 16x16 per "Como funciona").
+ *
+ *   x [tokens x cols] row-major (ld_x elements).  For every column c and every
+ *   group g of 16 consecutive tokens: u_j = x[16g + j][c], negated where bit j
+ *   of sign_mask is set; radix-2 Walsh-Hadamard butterflies with strides
+ *   1, 2, 4, 8 ((a, b) -> (a + b, a - b)); y_j = 0.25 * u_j.  That is
+ *   y = (1/4) H16 diag(d) x, orthonormal, so the same sign_mask on dY and X
+ *   cancels in dW = dY^T X.  amax_t is taken over y; each group is one block.
+ *   codes [cols][tokens/2], scales [cols][tokens/16] (token-contiguous).
+ *   SR index of an element: c*tokens + t.
+ *   tokens, cols positive multiples of 16; sign_mask uses its low 16 bits.
+ */
+nvfp4_status nvfp4_rht_quantize(const void *x, int dt, int64_t tokens, int64_t cols, int64_t ld_x,
+                                uint32_t sign_mask, int rnd, uint64_t seed, uint8_t *codes,
+                                uint8_t *scales, float *tensor_scale, float *amax, void *stream);
+
+/*
+ * nvfp4_gemm -- block-scaled NVFP4 contraction with FP32 accumulation
+ * (the NVFP4 GEMMs of "Suporte de Hardware", part 3 of the same page).
+ *
+ *   C[m][n] = beta * C[m][n]
+ *           + a_ts * b_ts * sum_k (e2m1(A[m][k]) * dec(sA[m][k/16]))
+ *                                * (e2m1(B[n][k]) * dec(sB[n/b_scale_rowdiv][k/16]))
+ *   Both operands are K-contiguous ("NT"):
+ *     a_codes [M][K/2], a_scales [M][K/16]                       (1D scales)
+ *     b_codes [N][K/2], b_scales [N/b_scale_rowdiv][K/16]       (rowdiv 1: 1D,
+ *                                                               16: 2D tile grid)
+ *     a_tensor_scale, b_tensor_scale: one device float each (tensor_scale
+ *     outputs of the quantize calls).
+ *     c [M][ldc] FP32, ldc >= N.  beta must be 0 (overwrite) or 1 (accumulate).
+ *   Fprop Y = X W^T : A = X row-1D, B = W tile-2D codes/scales (rowdiv 16).
+ *   Dgrad dX = dY W : A = dY row-1D, B = W tile-2D codes_t/scales_t (rowdiv 16).
+ *   Wgrad dW = dY^T X: A = RHT(dY) column-1D, B = RHT(X) column-1D (rowdiv 1),
+ *                      K = tokens.
+ *   M, N, K must be positive multiples of 256; ldc a multiple of 4.
+ *   Products e2m1 * E4M3 are exact in FP16, so the kernel dequantizes the
+ *   block-scaled operands exactly and contracts them on FP16 matrix cores with
+ *   FP32 accumulation; the two tensor scales are applied in the epilogue.
+ */
+nvfp4_status nvfp4_gemm(int64_t M, int64_t N, int64_t K, const uint8_t *a_codes,
+                        const uint8_t *a_scales, const float *a_tensor_scale,
+                        const uint8_t *b_codes, const uint8_t *b_scales, int32_t b_scale_rowdiv,
+                        const float *b_tensor_scale, float *c, int64_t ldc, float beta,
+                        void *stream);
+
+/* Static, human-readable name of a status code. */
+const char *nvfp4_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4_H */

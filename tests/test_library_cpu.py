@@ -1,0 +1,123 @@
+"""Host-side checks of libnvfp4 that need no GPU: the library loads, exports
+exactly the entry points include/nvfp4.h declares, and rejects bad arguments
+with the documented status codes before anything is enqueued."""
+import os
+import re
+import subprocess
+
+import pytest
+
+import bit_microscaled_quantized_amd as nv
+from bit_microscaled_quantized_amd import nvfp4 as b
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nvfp4.h")
+FAKE = 1 << 20  # a 16-byte aligned non-null address that is never dereferenced
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:nvfp4_status|const char \*)\s*(nvfp4_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_symbols() == sorted(b.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = nv.load_library()
+    for s in declared_symbols():
+        assert hasattr(lib, s), s
+    out = subprocess.run(["nm", "-D", "--defined-only", nv.library_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported_c = sorted({line.split()[-1] for line in out.splitlines()
+                         if line.split()[-1].startswith("nvfp4_")})
+    assert exported_c == declared_symbols()
+
+
+def test_status_strings():
+    assert nv.nvfp4_status_str(0) == "NVFP4_OK"
+    for s in range(1, 5):
+        assert nv.nvfp4_status_str(s).startswith("NVFP4_E")
+    assert "unknown" in nv.nvfp4_status_str(99)
+
+
+def q(**kw):
+    args = dict(x=FAKE, dt=0, rows=32, cols=32, ld_x=32, layout=0, rnd=0, seed=0, codes=FAKE,
+                scales=FAKE, codes_t=None, scales_t=None, tensor_scale=FAKE, amax=FAKE)
+    args.update(kw)
+    return nv.nvfp4_quantize(**args, stream=0, raise_on_error=False)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), b.NVFP4_EINVAL),
+    (dict(codes=None), b.NVFP4_EINVAL),
+    (dict(amax=None), b.NVFP4_EINVAL),
+    (dict(dt=7), b.NVFP4_EINVAL),
+    (dict(layout=3), b.NVFP4_EINVAL),
+    (dict(rnd=2), b.NVFP4_EINVAL),
+    (dict(codes_t=FAKE, scales_t=FAKE), b.NVFP4_EINVAL),          # transposed outputs on a 1D layout
+    (dict(layout=2, codes_t=FAKE), b.NVFP4_EINVAL),               # codes_t without scales_t
+    (dict(rows=24), b.NVFP4_ESHAPE),
+    (dict(cols=8, ld_x=8), b.NVFP4_ESHAPE),
+    (dict(rows=0), b.NVFP4_ESHAPE),
+    (dict(ld_x=16), b.NVFP4_ESHAPE),
+    (dict(rows=1 << 20, cols=1 << 12, ld_x=1 << 12), b.NVFP4_ESHAPE),  # 2^32 elements
+    (dict(x=FAKE + 4), b.NVFP4_EALIGN),
+    (dict(ld_x=36), b.NVFP4_EALIGN),                              # 72-byte bf16 rows
+    (dict(codes=FAKE + 8), b.NVFP4_EALIGN),
+    (dict(tensor_scale=FAKE + 2), b.NVFP4_EALIGN),
+])
+def test_quantize_argument_errors(kw, status):
+    assert q(**kw) == status
+
+
+def test_rht_quantize_argument_errors():
+    def r(**kw):
+        args = dict(x=FAKE, dt=0, tokens=32, cols=32, ld_x=32, sign_mask=0, rnd=0, seed=0,
+                    codes=FAKE, scales=FAKE, tensor_scale=FAKE, amax=FAKE)
+        args.update(kw)
+        return nv.nvfp4_rht_quantize(**args, stream=0, raise_on_error=False)
+    assert r(x=None) == b.NVFP4_EINVAL
+    assert r(rnd=5) == b.NVFP4_EINVAL
+    assert r(tokens=40) == b.NVFP4_ESHAPE
+    assert r(cols=20, ld_x=20) == b.NVFP4_ESHAPE
+    assert r(scales=FAKE + 1) == b.NVFP4_EALIGN
+
+
+def g(**kw):
+    args = dict(M=256, N=256, K=256, a_codes=FAKE, a_scales=FAKE, a_tensor_scale=FAKE, b_codes=FAKE,
+                b_scales=FAKE, b_scale_rowdiv=1, b_tensor_scale=FAKE, c=FAKE, ldc=256, beta=0.0)
+    args.update(kw)
+    return nv.nvfp4_gemm(**args, stream=0, raise_on_error=False)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(a_codes=None), b.NVFP4_EINVAL),
+    (dict(c=None), b.NVFP4_EINVAL),
+    (dict(b_scale_rowdiv=4), b.NVFP4_EINVAL),
+    (dict(beta=0.5), b.NVFP4_EINVAL),
+    (dict(M=250), b.NVFP4_ESHAPE),
+    (dict(N=8), b.NVFP4_ESHAPE),
+    (dict(K=96), b.NVFP4_ESHAPE),
+    (dict(K=0), b.NVFP4_ESHAPE),
+    (dict(ldc=128), b.NVFP4_ESHAPE),
+    (dict(a_codes=FAKE + 4), b.NVFP4_EALIGN),
+    (dict(c=FAKE + 4), b.NVFP4_EALIGN),
+    (dict(ldc=258), b.NVFP4_EALIGN),
+])
+def test_gemm_argument_errors(kw, status):
+    assert g(**kw) == status
+
+
+def test_errors_raise_in_checked_mode():
+    with pytest.raises(nv.Nvfp4Error) as e:
+        nv.nvfp4_gemm(256, 256, 100, FAKE, FAKE, FAKE, FAKE, FAKE, 1, FAKE, FAKE, 256, 0.0, stream=0)
+    assert e.value.status == b.NVFP4_ESHAPE
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(b, "_lib", None)
+    monkeypatch.setattr(b, "_LIB_PATH", str(tmp_path / "libnvfp4.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        b.load_library()
