@@ -1,0 +1,265 @@
+#!/usr/bin/env python3
+"""Benchmark of the NVFP4 quantize-and-contract step of one linear layer on
+one MI355X.
+
+A step is the whole hot path over one batch of the FFN up-projection layer
+(X bf16 8192x5120, W bf16 20480x5120 ~N(0, 0.02^2), dY bf16 8192x20480
+~N(0, 1e-3^2)): W 16x16 2D quantize (RNE, with the transposed copy), X row-1D
+RNE, Fprop GEMM, dY row-1D SR, Dgrad GEMM with the same quantized W, random
+Hadamard + column-1D quantize of dY (SR) and X (RNE), Wgrad GEMM.  Inputs are
+resident in HBM before the timed region.
+
+Output: one JSON line.  `value` is the step's GEMM work (3 x 2MNK flops)
+divided by the whole step's wall time, so quantization time counts against
+it; the per-component figures (quantize GB/s, GEMM TFLOP/s and their
+fractions of the MI355X peaks) sit beside it.  `roofline` describes the
+dominant kernel (the GEMM) from HIP events around every GEMM launch in the
+timed steps.  `cpu_baseline` times the CPU oracle on a bounded sample of the
+same step (1024 tokens, full weights).
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "NVFP4 quantize GB/s (% HBM peak) + NVFP4 GEMM TFLOPS (% MFMA peak), 1 GPU"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_F16_PEAK = 2500.0         # dense FP16 MFMA, TFLOP/s (the class the exact GEMM issues)
+MFMA_FP4_PEAK = 10100.0        # dense FP4 MFMA, TFLOP/s (context)
+
+TOKENS, D_IN, D_OUT = 8192, 5120, 20480
+
+# HBM traffic of one GEMM launch from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE,
+# each scaled by the same counter's reading for a plain copy kernel of known
+# size; valid only for the kernel source it was measured on.
+GEMM_TRAFFIC = None  # dict(src_sha256=..., bytes_per_launch=...) once measured
+
+
+def _src_sha(path: str) -> str:
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--cpu-sample-tokens", type=int, default=1024)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args()
+
+
+def make_inputs():
+    from bit_microscaled_quantized_amd import synth
+    d = synth.ffn_up(TOKENS, D_IN, D_OUT)
+    return dict(x=synth.f32_to_bf16_bits(d["x"]), w=synth.f32_to_bf16_bits(d["w"]),
+                dy=synth.f32_to_bf16_bits(d["dy"]), sign_mask=d["sign_mask"],
+                seed_row=d["sr_seed_row"], seed_col=d["sr_seed_col"])
+
+
+def quantize_bytes():
+    """Algorithmic bytes of the five quantize calls of a step: input read once,
+    codes (0.5 B/elem) and scales (1/16 B/elem, 1/256 B/elem for 2D tiles)
+    written; the 2D call also writes its transposed copy."""
+    T, I, O = TOKENS, D_IN, D_OUT
+    w = O * I * 2 + 2 * (O * I // 2 + O * I // 256)
+    x_row = T * I * 2 + T * I // 2 + T * I // 16
+    dy_row = T * O * 2 + T * O // 2 + T * O // 16
+    dy_rht = dy_row
+    x_rht = x_row
+    return dict(w=w, x_row=x_row, dy_row=dy_row, dy_rht=dy_rht, x_rht=x_rht)
+
+
+def gpu_bench(inp, steps, warmup):
+    import torch
+    import bit_microscaled_quantized_amd as nv
+    from bit_microscaled_quantized_amd.linear import LinearStep
+
+    nv.load_library()  # fails loudly if the HIP library is missing
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+
+    def up(a):
+        return torch.from_numpy(a.view(np.int16)).to(dev)
+
+    x, w, dy = up(inp["x"]), up(inp["w"]), up(inp["dy"])
+    st = LinearStep(TOKENS, D_IN, D_OUT, device=dev)
+    bf = nv.NVFP4_BF16
+    T, I, O = TOKENS, D_IN, D_OUT
+    mask, s_row, s_col = inp["sign_mask"], inp["seed_row"], inp["seed_col"]
+
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
+    def one_step(rec):
+        """One whole step; rec collects (name, start, end) events."""
+        def timed(name, fn):
+            if rec is None:
+                fn()
+                return
+            a, b = ev(), ev()
+            a.record()
+            fn()
+            b.record()
+            rec.append((name, a, b))
+        q = st.qw
+        timed("quant_w_2d", lambda: nv.nvfp4_quantize(
+            w, bf, O, I, I, nv.NVFP4_TILE_2D, nv.NVFP4_RNE, 0, q.codes, q.scales, q.codes_t,
+            q.scales_t, q.ts, q.amax))
+        qx = st.qx
+        timed("quant_x_row", lambda: nv.nvfp4_quantize(
+            x, bf, T, I, I, nv.NVFP4_ROW_1D, nv.NVFP4_RNE, 0, qx.codes, qx.scales, None, None,
+            qx.ts, qx.amax))
+        timed("gemm_fprop", lambda: nv.nvfp4_gemm(
+            T, O, I, qx.codes, qx.scales, qx.ts, q.codes, q.scales, 16, q.ts, st.y, O, 0.0))
+        qd = st.qdy
+        timed("quant_dy_row_sr", lambda: nv.nvfp4_quantize(
+            dy, bf, T, O, O, nv.NVFP4_ROW_1D, nv.NVFP4_SR, s_row, qd.codes, qd.scales, None, None,
+            qd.ts, qd.amax))
+        timed("gemm_dgrad", lambda: nv.nvfp4_gemm(
+            T, I, O, qd.codes, qd.scales, qd.ts, q.codes_t, q.scales_t, 16, q.ts, st.dx, I, 0.0))
+        a_, b_ = st.qdy_t, st.qx_t
+        timed("quant_dy_rht_sr", lambda: nv.nvfp4_rht_quantize(
+            dy, bf, T, O, O, mask, nv.NVFP4_SR, s_col, a_.codes, a_.scales, a_.ts, a_.amax))
+        timed("quant_x_rht", lambda: nv.nvfp4_rht_quantize(
+            x, bf, T, I, I, mask, nv.NVFP4_RNE, 0, b_.codes, b_.scales, b_.ts, b_.amax))
+        timed("gemm_wgrad", lambda: nv.nvfp4_gemm(
+            O, I, T, a_.codes, a_.scales, a_.ts, b_.codes, b_.scales, 1, b_.ts, st.dw, I, 0.0))
+
+    for _ in range(warmup):
+        one_step(None)
+    torch.cuda.synchronize()
+
+    # whole-step wall time: K steps between two synchronizations, no events
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        one_step(None)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    # per-call HIP-event durations over another K steps on the same stream
+    rec = []
+    for _ in range(steps):
+        one_step(rec)
+    torch.cuda.synchronize()
+    per = {}
+    for name, a, b in rec:
+        per.setdefault(name, []).append(a.elapsed_time(b))
+    return wall / steps, {k: float(np.mean(v)) for k, v in per.items()}
+
+
+def cpu_baseline(inp, tokens):
+    """The oracle, as it stands, on the same step restricted to the first
+    `tokens` tokens (full weight): five quantizations plus the three FP64
+    contractions of its dequantized operands."""
+    import oracle as ora
+    from threadpoolctl import threadpool_info
+    x, w, dy = inp["x"][:tokens], inp["w"], inp["dy"][:tokens]
+    mask, s_row, s_col = inp["sign_mask"], inp["seed_row"], inp["seed_col"]
+    t0 = time.perf_counter()
+    qw = ora.quantize(w, ora.TILE_2D, ora.RNE)
+    qx = ora.quantize(x, ora.ROW_1D, ora.RNE)
+    y = ora.gemm_f64(ora.dequant(qx["codes"], qx["scales"], qx["tensor_scale"]),
+                     ora.dequant(qw["codes"], qw["scales"], qw["tensor_scale"], 16))
+    qd = ora.quantize(dy, ora.ROW_1D, ora.SR, s_row)
+    dx = ora.gemm_f64(ora.dequant(qd["codes"], qd["scales"], qd["tensor_scale"]),
+                      ora.dequant(qw["codes_t"], qw["scales_t"], qw["tensor_scale"], 16))
+    qdt = ora.rht_quantize(dy, mask, ora.SR, s_col)
+    qxt = ora.rht_quantize(x, mask, ora.RNE)
+    dw = ora.gemm_f64(ora.dequant(qdt["codes"], qdt["scales"], qdt["tensor_scale"]),
+                      ora.dequant(qxt["codes"], qxt["scales"], qxt["tensor_scale"]))
+    dt = time.perf_counter() - t0
+    del y, dx, dw
+    flops = 3 * 2.0 * tokens * D_IN * D_OUT
+    blas = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    return dict(value=flops / dt / 1e12, unit="TFLOP/s", cores=max(ora.num_threads(), blas),
+                kind="oracle", seconds=dt,
+                sample=f"same step on the first {tokens} of {TOKENS} tokens with the full "
+                       f"{D_OUT}x{D_IN} weight: W 2D, X row, dY row SR, RHT(dY) SR, RHT(X) "
+                       f"quantization in the C oracle (OpenMP) + 3 FP64 BLAS contractions")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the sharded path is a design, not built)", file=sys.stderr)
+        sys.exit(2)
+    inp = make_inputs()
+    ms_step, per = gpu_bench(inp, args.steps, args.warmup)
+    ms_step *= 1e3
+
+    gemm_flops = 2.0 * TOKENS * D_IN * D_OUT  # each of the three GEMMs
+    gemm_ms = np.mean([per["gemm_fprop"], per["gemm_dgrad"], per["gemm_wgrad"]])
+    gemm_tflops = gemm_flops / (gemm_ms * 1e-3) / 1e12
+    qb = quantize_bytes()
+    qnames = dict(w="quant_w_2d", x_row="quant_x_row", dy_row="quant_dy_row_sr",
+                  dy_rht="quant_dy_rht_sr", x_rht="quant_x_rht")
+    q_ms = sum(per[qnames[k]] for k in qb)
+    q_gbs = sum(qb.values()) / (q_ms * 1e-3) / 1e9
+    value = 3 * gemm_flops / (ms_step * 1e-3) / 1e12
+
+    traffic = None
+    if GEMM_TRAFFIC is not None and GEMM_TRAFFIC["src_sha256"] == _src_sha(
+            os.path.join(ROOT, "bit_microscaled_quantized_amd", "csrc", "gemm.hip")):
+        traffic = GEMM_TRAFFIC["bytes_per_launch"]
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": "ffn_up_fwd_bwd: X bf16 8192x5120 N(0,1), W bf16 20480x5120 N(0,0.02^2), "
+                        "dY bf16 8192x20480 N(0,1e-3^2); W 2D RNE (+transposed), X row RNE, "
+                        "dY row SR, RHT+col (dY SR, X RNE); Fprop, Dgrad, Wgrad NVFP4 GEMMs",
+            "tokens": TOKENS, "d_in": D_IN, "d_out": D_OUT,
+        },
+        "roofline": {
+            "kernel": "k_gemm_nvfp4",
+            "bound": "mfma",
+            "achieved": round(gemm_tflops, 2),
+            "peak": MFMA_F16_PEAK,
+            "unit": "TFLOP/s",
+            "frac": round(gemm_tflops / MFMA_F16_PEAK, 4),
+            "traffic": traffic,
+            "avg_launch_ms": round(float(gemm_ms), 4),
+            "flops_per_launch": gemm_flops,
+        },
+        "components": {
+            "quantize_GBps": round(q_gbs, 1),
+            "quantize_frac_hbm": round(q_gbs / HBM_PEAK_GBS, 4),
+            "gemm_TFLOPs": round(gemm_tflops, 2),
+            "gemm_frac_mfma_f16": round(gemm_tflops / MFMA_F16_PEAK, 4),
+            "gemm_frac_mfma_fp4": round(gemm_tflops / MFMA_FP4_PEAK, 4),
+            "per_call_ms": {k: round(v, 4) for k, v in per.items()},
+            "quantize_bytes": qb,
+        },
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_sample_tokens)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
