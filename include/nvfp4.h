@@ -128,7 +128,8 @@ nvfp4_status nvfp4_rht_quantize(const void *x, int dt, int64_t tokens, int64_t c
  *   Dgrad dX = dY W : A = dY row-1D, B = W tile-2D codes_t/scales_t (rowdiv 16).
  *   Wgrad dW = dY^T X: A = RHT(dY) column-1D, B = RHT(X) column-1D (rowdiv 1),
  *                      K = tokens.
- *   M, N, K must be positive multiples of 256; ldc a multiple of 4.
+ *   M and N must be positive multiples of 16, K a positive multiple of 64 (all
+ *   below 2^31); ldc >= N and a multiple of 4; c 16-byte aligned.
  *   Products e2m1 * E4M3 are exact in FP16, so the kernel dequantizes the
  *   block-scaled operands exactly and contracts them on FP16 matrix cores with
  *   FP32 accumulation; the two tensor scales are applied in the epilogue.
