@@ -57,6 +57,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--cpu-sample-tokens", type=int, default=1024)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--copy-probe-mib", type=int, default=0,
+                   help="also run one plain device copy of this many MiB (calibrates "
+                        "the FETCH_SIZE / WRITE_SIZE counters against known bytes)")
     return p.parse_args()
 
 
@@ -199,6 +202,15 @@ def main():
         sys.exit(2)
     inp = make_inputs()
     ms_step, per = gpu_bench(inp, args.steps, args.warmup)
+    if args.copy_probe_mib:
+        import torch
+        n = args.copy_probe_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     ms_step *= 1e3
 
     gemm_flops = 2.0 * TOKENS * D_IN * D_OUT  # each of the three GEMMs

@@ -11,22 +11,38 @@
 // Exactness: an E2M1 value (<= 2 significant bits) times an E4M3 scale
 // (<= 4 significant bits, 2^-9 .. 448) has at most 6 significant bits and
 // lies in [2^-10, 2688], so it is exact in FP16, and the product of two such
-// values is exact in FP32.  The kernel therefore folds each block scale into
-// its operand while converting FP4 -> FP16 in registers (hardware FP4->F16
-// conversion, then a packed FP16 multiply by the scale), contracts on the FP16
-// matrix cores (v_mfma_f32_32x32x16_f16, FP32 accumulation) and applies the
-// two FP32 tensor scales once in the epilogue.  The only rounding is the FP32
-// accumulation and the final alpha multiply.
+// values is exact in FP32.  Each wave dequantizes its operand fragments in
+// registers (hardware FP4->F16 conversion, then a packed FP16 multiply by the
+// block scale), contracts them on the FP16 matrix cores
+// (v_mfma_f32_32x32x16_f16, FP32 accumulation) and applies the two FP32
+// tensor scales once in the epilogue.  The only rounding is the FP32
+// accumulation and the final alpha multiply.  One MFMA step covers 16
+// K-elements, i.e. exactly one scale block per operand row.
+//
+// Data movement: the operands stay 4.5 bits per element all the way into LDS.
+// A stage covers 256 K-elements: 128 code bytes (one full 128-byte line) and
+// 16 scale bytes per row, for the workgroup's 256 A rows and 256 B rows
+// (72 KB); two stages are double-buffered (144 KB of the 160 KB LDS).  Stages
+// are fetched with direct-to-LDS loads (global_load_lds, 16 bytes per lane for
+// codes, 4 for scales) issued one stage ahead, so no registers hold prefetched
+// data and each code load instruction covers eight full cache lines.  Chunk c
+// (16 bytes) of row r lands in slot 8r + (c ^ (r & 7)), which makes the
+// fragment reads (32 consecutive rows, same chunk) bank-conflict free.  One
+// barrier per stage.
 //
 // Tiling: 256 threads = 4 waves in a 2x2 grid; workgroup tile 256 x 256, wave
-// tile 128 x 128 = 4 x 4 MFMA tiles of 32 x 32 (256 FP32 accumulators per
-// lane); K advances 64 per stage.  Per stage the raw FP4 codes (32 bytes per
-// row) and the scales (converted once to FP16) are staged in LDS, double
-// buffered with one barrier per stage.  K is permuted inside a stage so every
-// lane reads its 32 codes as one 16-byte LDS load: lane half h = lane / 32,
-// k-step s, element e hold stage element 32h + 8s + e, identically for A and
-// B, which leaves the contraction unchanged.  Workgroups are remapped so that
-// neighbouring output tiles run on the same XCD (shared L2).
+// tile 128 x 128 = 4 x 4 MFMA tiles of 32 x 32 (256 FP32 accumulators per lane,
+// in AGPRs).  Inside a stage K is permuted so that one 16-byte chunk read feeds
+// four MFMA steps: lane half h reads chunks 4h .. 4h + 3 of its row; in quad g
+// (chunk 4h + g) step s uses the chunk's dword s, i.e. stage elements
+// 32(4h + g) + 8s .. + 7, identically for A and B, which leaves the
+// contraction unchanged.  Rows past M/N and chunks past K are fetched from
+// clamped in-row addresses; past K the scales are zeroed (exact 0
+// contribution), past M/N the outputs are never stored.  Workgroups are
+// remapped so that each XCD's share of the grid is a contiguous, grouped range
+// of output tiles (shared L2).
+#include <mutex>
+
 #include "nvfp4_device.hpp"
 #include "nvfp4_launch.hpp"
 
@@ -36,52 +52,41 @@ namespace {
 
 constexpr int BM = 256;
 constexpr int BN = 256;
-constexpr int BK = 64;          // K elements per stage
-constexpr int ROWB = BK / 2;    // code bytes per row per stage (32)
-constexpr int NSB = BK / 16;    // scale blocks per row per stage (4)
+constexpr int BKS = 256;                           // K elements per stage
+constexpr int CODE_BYTES = BM * (BKS / 2);         // 32 KB per operand
+constexpr int SCALE_BYTES = BM * (BKS / 16);       // 4 KB per operand
+constexpr int OFF_B = CODE_BYTES;                  // B codes
+constexpr int OFF_SA = 2 * CODE_BYTES;             // A scales
+constexpr int OFF_SB = 2 * CODE_BYTES + SCALE_BYTES;
+constexpr int STAGE_BYTES = 2 * CODE_BYTES + 2 * SCALE_BYTES;  // 72 KB
+constexpr int LDS_BYTES = 2 * STAGE_BYTES;                     // 144 KB
 
-struct __align__(16) Stage {
-  uint8_t a[BM * ROWB];        // [BM/32][2][32][16 B]
-  uint8_t b[BN * ROWB];
-  _Float16 sa[BM * NSB];       // [BM][4]
-  _Float16 sb[BN * NSB];
-};
+typedef __attribute__((address_space(1))) void gvoid;
+typedef __attribute__((address_space(3))) void lvoid;
 
-__device__ __forceinline__ int code_slot(int row, int h) {
-  return ((row >> 5) << 10) + (h << 9) + ((row & 31) << 4);
+// Each lane's `size` bytes at g land at l + lane * size (l wave-uniform).
+__device__ __forceinline__ void load_lds16(const uint8_t* g, uint8_t* l) {
+  __builtin_amdgcn_global_load_lds((gvoid*)g, (lvoid*)l, 16, 0, 0);
+}
+__device__ __forceinline__ void load_lds4(const uint8_t* g, uint8_t* l) {
+  __builtin_amdgcn_global_load_lds((gvoid*)g, (lvoid*)l, 4, 0, 0);
 }
 
-__device__ __forceinline__ uint64_t scales_to_f16x4(uint32_t w) {
-  uint64_t r = 0;
-#pragma unroll
-  for (int i = 0; i < 4; i++) {
-    _Float16 h = (_Float16)e4m3_decode((w >> (8 * i)) & 0xFFu);
-    r |= (uint64_t)__builtin_bit_cast(uint16_t, h) << (16 * i);
-  }
-  return r;
-}
-
-// 8 FP4 codes (one dword, element 0 in the low nibble) -> 8 FP16 values times
-// the block scale s (exact).
+// 8 FP4 codes -> 8 FP16 values times the block scale s (exact).
 __device__ __forceinline__ half8_t dequant8(uint32_t w, half2_t s) {
-  half2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0);
-  half2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1);
-  half2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2);
-  half2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3);
-  p0 = p0 * s;
-  p1 = p1 * s;
-  p2 = p2 * s;
-  p3 = p3 * s;
+  half2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s;
+  half2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * s;
+  half2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * s;
+  half2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * s;
   half8_t r;
   r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
   r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
   return r;
 }
 
-struct Prefetch {
-  uint4 a[2], b[2];
-  uint32_t sa, sb;
-};
+__device__ __forceinline__ uint32_t dw(const uint4& q, int i) {
+  return i == 0 ? q.x : i == 1 ? q.y : i == 2 ? q.z : q.w;
+}
 
 }  // namespace
 
@@ -90,10 +95,11 @@ __global__ __launch_bounds__(256, 1) void k_gemm_nvfp4(
     const float* __restrict__ a_ts, const uint8_t* __restrict__ b_codes,
     const uint8_t* __restrict__ b_scales, int b_rowdiv, const float* __restrict__ b_ts,
     float* __restrict__ c, int64_t ldc, int accumulate) {
-  __shared__ Stage st[2];
+  extern __shared__ __align__(16) uint8_t lds[];
 
   // XCD-aware tile order: the hardware deals workgroups round-robin over the
-  // 8 XCDs, so gather each XCD's share into a contiguous range of tiles.
+  // 8 XCDs, so gather each XCD's share into a contiguous range of tiles, then
+  // walk the tiles in groups of GROUP tile rows.
   const int G = gridDim.x;
   const int bid = blockIdx.x;
   const int xcd = bid & 7, per = G >> 3, rem = G & 7;
@@ -110,38 +116,65 @@ __global__ __launch_bounds__(256, 1) void k_gemm_nvfp4(
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
-  const int64_t kb = K / 2;    // code bytes per row
-  const int64_t ks = K / 16;   // scale bytes per row
+  const int h = lane >> 5;
+  const int lr = lane & 31;
+  const int64_t kb = K / 2;   // code bytes per row (a multiple of 32)
+  const int64_t ks = K / 16;  // scale bytes per row (a multiple of 4)
+  const int KT = (K + BKS - 1) / BKS;
 
-  // global -> register prefetch of one stage
-  auto load_stage = [&](int kt, Prefetch& p) {
+  // ---- stage fetch.  Code instruction j of a wave: rows 8(8 wave + j) + l/8,
+  // lane l takes chunk (l%8) ^ (row & 7) of its row.  Scale instruction i:
+  // rows 64 wave + 16 i + l/4, lane l takes dword l%4 of the row's 16 bytes.
+  const int crow = lane >> 3;
+  const int cchunk = (lane & 7) ^ crow;
+  const int sdw = lane & 3;
+  auto issue_stage = [&](int kt, uint8_t* st) {
+    // in-row byte offsets, clamped to the row's last chunk / dword
+    const int64_t coff = min((int64_t)kt * (BKS / 2) + 16 * cchunk, kb - 16);
+    const int64_t soff = min((int64_t)kt * (BKS / 16) + 4 * sdw, ks - 4);
 #pragma unroll
-    for (int i = 0; i < 2; i++) {
-      int q = tid + 256 * i;
-      int row = q >> 1, h = q & 1;
-      int64_t off = (int64_t)kt * ROWB + 16 * h;
-      p.a[i] = (m0 + row < M) ? *reinterpret_cast<const uint4*>(a_codes + (int64_t)(m0 + row) * kb + off)
-                              : make_uint4(0, 0, 0, 0);
-      p.b[i] = (n0 + row < N) ? *reinterpret_cast<const uint4*>(b_codes + (int64_t)(n0 + row) * kb + off)
-                              : make_uint4(0, 0, 0, 0);
+    for (int j = 0; j < 8; j++) {
+      const int r = 8 * (8 * wave + j) + crow;
+      load_lds16(a_codes + (int64_t)min(m0 + r, M - 1) * kb + coff, st + (8 * wave + j) * 1024);
+      load_lds16(b_codes + (int64_t)min(n0 + r, N - 1) * kb + coff, st + OFF_B + (8 * wave + j) * 1024);
     }
-    p.sa = (m0 + tid < M) ? *reinterpret_cast<const uint32_t*>(a_scales + (int64_t)(m0 + tid) * ks + kt * NSB) : 0u;
-    p.sb = (n0 + tid < N)
-               ? *reinterpret_cast<const uint32_t*>(b_scales + (int64_t)((n0 + tid) / b_rowdiv) * ks + kt * NSB)
-               : 0u;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int r = 64 * wave + 16 * i + (lane >> 2);
+      load_lds4(a_scales + (int64_t)min(m0 + r, M - 1) * ks + soff, st + OFF_SA + wave * 1024 + i * 256);
+      load_lds4(b_scales + (int64_t)(min(n0 + r, N - 1) / b_rowdiv) * ks + soff,
+                st + OFF_SB + wave * 1024 + i * 256);
+    }
   };
-  auto store_stage = [&](Stage& s, const Prefetch& p) {
-#pragma unroll
-    for (int i = 0; i < 2; i++) {
-      int q = tid + 256 * i;
-      int row = q >> 1, h = q & 1;
-      *reinterpret_cast<uint4*>(s.a + code_slot(row, h)) = p.a[i];
-      *reinterpret_cast<uint4*>(s.b + code_slot(row, h)) = p.b[i];
+  // In a stage that ends past K, zero the scale bytes of blocks >= K/16: their
+  // codes and scales came from clamped addresses and must contribute exactly 0.
+  auto fix_partial = [&](int kt, uint8_t* st) {
+    const int valid = (int)min((int64_t)BKS / 16, ks - (int64_t)kt * (BKS / 16));
+    if (valid >= BKS / 16) return;
+    uint8_t* ra = st + OFF_SA + tid * 16;
+    uint8_t* rb = st + OFF_SB + tid * 16;
+    for (int i = valid; i < 16; i++) {
+      ra[i] = 0;
+      rb[i] = 0;
     }
-    *reinterpret_cast<uint64_t*>(s.sa + tid * NSB) = scales_to_f16x4(p.sa);
-    *reinterpret_cast<uint64_t*>(s.sb + tid * NSB) = scales_to_f16x4(p.sb);
+  };
+
+  // ---- fragment reads.  Lane (h, lr) of A tile i reads row wm*128 + 32i + lr,
+  // chunk 4h + g in quad g: slot 8*row + ((4h + g) ^ (lr & 7)); its two scale
+  // bytes (blocks 2(4h + g), 2(4h + g) + 1) sit at row*16 + 2(4h + g).
+  const int rowa = wm * 128 + lr;
+  const int rowb = wn * 128 + lr;
+  auto read_quad = [&](const uint8_t* st, int g, uint4* ca, uint4* cb, uint32_t* sa, uint32_t* sb) {
+    const int sw = ((4 * h + g) ^ (lr & 7)) << 4;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      ca[i] = *reinterpret_cast<const uint4*>(st + (rowa + 32 * i) * 128 + sw);
+      cb[i] = *reinterpret_cast<const uint4*>(st + OFF_B + (rowb + 32 * i) * 128 + sw);
+      sa[i] = *reinterpret_cast<const uint16_t*>(st + OFF_SA + (rowa + 32 * i) * 16 + 2 * (4 * h + g));
+      sb[i] = *reinterpret_cast<const uint16_t*>(st + OFF_SB + (rowb + 32 * i) * 16 + 2 * (4 * h + g));
+    }
   };
 
   floatx16 acc[4][4];
@@ -152,41 +185,25 @@ __global__ __launch_bounds__(256, 1) void k_gemm_nvfp4(
 #pragma unroll
       for (int r = 0; r < 16; r++) acc[i][j][r] = 0.0f;
 
-  const int KT = K / BK;
-  Prefetch pf;
-  load_stage(0, pf);
-  store_stage(st[0], pf);
-  __syncthreads();
-
-  const int h = lane >> 5;
-  const int lr = lane & 31;
-  for (int kt = 0; kt < KT; kt++) {
-    if (kt + 1 < KT) load_stage(kt + 1, pf);
-    const Stage& s = st[kt & 1];
-    uint4 ca[4], cb[4];
-    half2_t sa[4][2], sb[4][2];
+  // one quad = 4 MFMA steps on the chunks read for it
+  auto quad = [&](const uint4* ca, const uint4* cb, const uint32_t* sa, const uint32_t* sb) {
+    half2_t sca[4][2], scb[4][2];
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-      int ra = wm * 128 + i * 32 + lr;
-      int rb = wn * 128 + i * 32 + lr;
-      ca[i] = *reinterpret_cast<const uint4*>(s.a + code_slot(ra, h));
-      cb[i] = *reinterpret_cast<const uint4*>(s.b + code_slot(rb, h));
-      half2_t pa = *reinterpret_cast<const half2_t*>(s.sa + ra * NSB + 2 * h);
-      half2_t pb = *reinterpret_cast<const half2_t*>(s.sb + rb * NSB + 2 * h);
-      sa[i][0] = half2_t{pa[0], pa[0]};
-      sa[i][1] = half2_t{pa[1], pa[1]};
-      sb[i][0] = half2_t{pb[0], pb[0]};
-      sb[i][1] = half2_t{pb[1], pb[1]};
+      half2_t pa = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sa[i], 1.0f, false);
+      half2_t pb = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sb[i], 1.0f, false);
+      sca[i][0] = half2_t{pa[0], pa[0]};
+      sca[i][1] = half2_t{pa[1], pa[1]};
+      scb[i][0] = half2_t{pb[0], pb[0]};
+      scb[i][1] = half2_t{pb[1], pb[1]};
     }
 #pragma unroll
-    for (int st_ = 0; st_ < 4; st_++) {
+    for (int s = 0; s < 4; s++) {
       half8_t fa[4], fb[4];
 #pragma unroll
       for (int i = 0; i < 4; i++) {
-        uint32_t wa = st_ == 0 ? ca[i].x : st_ == 1 ? ca[i].y : st_ == 2 ? ca[i].z : ca[i].w;
-        uint32_t wb = st_ == 0 ? cb[i].x : st_ == 1 ? cb[i].y : st_ == 2 ? cb[i].z : cb[i].w;
-        fa[i] = dequant8(wa, sa[i][st_ >> 1]);
-        fb[i] = dequant8(wb, sb[i][st_ >> 1]);
+        fa[i] = dequant8(dw(ca[i], s), sca[i][s >> 1]);
+        fb[i] = dequant8(dw(cb[i], s), scb[i][s >> 1]);
       }
 #pragma unroll
       for (int i = 0; i < 4; i++)
@@ -194,8 +211,33 @@ __global__ __launch_bounds__(256, 1) void k_gemm_nvfp4(
         for (int j = 0; j < 4; j++)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[i], fb[j], acc[i][j], 0, 0, 0);
     }
-    if (kt + 1 < KT) store_stage(st[(kt + 1) & 1], pf);
+  };
+
+  // prologue: stage 0
+  issue_stage(0, lds);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  fix_partial(0, lds);
+  __syncthreads();
+
+  for (int kt = 0; kt < KT; kt++) {
+    uint8_t* cur = lds + (kt & 1) * STAGE_BYTES;
+    uint8_t* nxt = lds + ((kt + 1) & 1) * STAGE_BYTES;
+    if (kt + 1 < KT) issue_stage(kt + 1, nxt);
+    uint4 ca[2][4], cb[2][4];
+    uint32_t sa[2][4], sb[2][4];
+    read_quad(cur, 0, ca[0], cb[0], sa[0], sb[0]);
+#pragma unroll
+    for (int g = 0; g < 4; g++) {
+      if (g < 3) read_quad(cur, g + 1, ca[(g + 1) & 1], cb[(g + 1) & 1], sa[(g + 1) & 1], sb[(g + 1) & 1]);
+      quad(ca[g & 1], cb[g & 1], sa[g & 1], sb[g & 1]);
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // this thread's share of stage kt + 1 is in LDS
     __syncthreads();
+    if (kt + 1 < KT) {
+      fix_partial(kt + 1, nxt);
+      __syncthreads();
+    }
   }
 
   const float alpha = a_ts[0] * b_ts[0];
@@ -221,9 +263,17 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
                        const uint8_t* a_scales, const float* a_ts, const uint8_t* b_codes,
                        const uint8_t* b_scales, int b_rowdiv, const float* b_ts, float* c,
                        int64_t ldc, int accumulate, hipStream_t s) {
+  static std::once_flag once;
+  static hipError_t attr_err = hipSuccess;
+  std::call_once(once, [] {
+    attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_nvfp4),
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
+  });
+  if (attr_err != hipSuccess) return attr_err;
   const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  k_gemm_nvfp4<<<(unsigned)tiles, 256, 0, s>>>((int)M, (int)N, (int)K, a_codes, a_scales, a_ts,
-                                                b_codes, b_scales, b_rowdiv, b_ts, c, ldc, accumulate);
+  k_gemm_nvfp4<<<(unsigned)tiles, 256, LDS_BYTES, s>>>((int)M, (int)N, (int)K, a_codes, a_scales,
+                                                       a_ts, b_codes, b_scales, b_rowdiv, b_ts, c,
+                                                       ldc, accumulate);
   return hipGetLastError();
 }
 
