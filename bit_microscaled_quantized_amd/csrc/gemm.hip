@@ -185,59 +185,107 @@ __global__ __launch_bounds__(256, 1) void k_gemm_nvfp4(
 #pragma unroll
       for (int r = 0; r < 16; r++) acc[i][j][r] = 0.0f;
 
-  // one quad = 4 MFMA steps on the chunks read for it
-  auto quad = [&](const uint4* ca, const uint4* cb, const uint32_t* sa, const uint32_t* sb) {
-    half2_t sca[4][2], scb[4][2];
+  // Quad data (chunks + scale bytes of 4 A and 4 B tiles), double-buffered by
+  // quad parity, and the FP16 fragments of one MFMA step, double-buffered by
+  // step parity.
+  uint4 qa[2][4], qb[2][4];
+  uint32_t qsa[2][4], qsb[2][4];
+  half2_t sca[2][4][2], scb[2][4][2];
+  half8_t fa[2][4], fb[2][4];
+
+  auto cvt_scales = [&](int p) {
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-      half2_t pa = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sa[i], 1.0f, false);
-      half2_t pb = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sb[i], 1.0f, false);
-      sca[i][0] = half2_t{pa[0], pa[0]};
-      sca[i][1] = half2_t{pa[1], pa[1]};
-      scb[i][0] = half2_t{pb[0], pb[0]};
-      scb[i][1] = half2_t{pb[1], pb[1]};
+      half2_t pa = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(qsa[p][i], 1.0f, false);
+      half2_t pb = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(qsb[p][i], 1.0f, false);
+      sca[p][i][0] = half2_t{pa[0], pa[0]};
+      sca[p][i][1] = half2_t{pa[1], pa[1]};
+      scb[p][i][0] = half2_t{pb[0], pb[0]};
+      scb[p][i][1] = half2_t{pb[1], pb[1]};
     }
+  };
+  // fragments of step s of the quad in buffer p into fragment buffer f
+  auto make_frags = [&](int p, int s, int f) {
 #pragma unroll
-    for (int s = 0; s < 4; s++) {
-      half8_t fa[4], fb[4];
+    for (int i = 0; i < 4; i++) {
+      fa[f][i] = dequant8(dw(qa[p][i], s), sca[p][i][s >> 1]);
+      fb[f][i] = dequant8(dw(qb[p][i], s), scb[p][i][s >> 1]);
+    }
+  };
+  auto mfmas = [&](int f) {
 #pragma unroll
-      for (int i = 0; i < 4; i++) {
-        fa[i] = dequant8(dw(ca[i], s), sca[i][s >> 1]);
-        fb[i] = dequant8(dw(cb[i], s), scb[i][s >> 1]);
-      }
+    for (int i = 0; i < 4; i++)
 #pragma unroll
-      for (int i = 0; i < 4; i++)
+      for (int j = 0; j < 4; j++)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[f][i], fb[f][j], acc[i][j], 0, 0, 0);
+  };
+  // MFMA / VALU / LDS interleave for one step: every MFMA is followed by the
+  // conversion work of the next step's fragments
+  auto step_schedule = [&]() {
 #pragma unroll
-        for (int j = 0; j < 4; j++)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    for (int q = 0; q < 16; q++) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU
+      if (q < 4) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
     }
   };
 
-  // prologue: stage 0
+  // prologue: stage 0 in buffer 0, quad 0 read, step-0 fragments built
   issue_stage(0, lds);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   fix_partial(0, lds);
   __syncthreads();
+  read_quad(lds, 0, qa[0], qb[0], qsa[0], qsb[0]);
+  cvt_scales(0);
+  make_frags(0, 0, 0);
 
   for (int kt = 0; kt < KT; kt++) {
     uint8_t* cur = lds + (kt & 1) * STAGE_BYTES;
     uint8_t* nxt = lds + ((kt + 1) & 1) * STAGE_BYTES;
-    if (kt + 1 < KT) issue_stage(kt + 1, nxt);
-    uint4 ca[2][4], cb[2][4];
-    uint32_t sa[2][4], sb[2][4];
-    read_quad(cur, 0, ca[0], cb[0], sa[0], sb[0]);
+    const bool more = kt + 1 < KT;
+    if (more) issue_stage(kt + 1, nxt);
+    __builtin_amdgcn_sched_barrier(0);
+    // quads 0..2: read the following quad of this stage while computing
 #pragma unroll
-    for (int g = 0; g < 4; g++) {
-      if (g < 3) read_quad(cur, g + 1, ca[(g + 1) & 1], cb[(g + 1) & 1], sa[(g + 1) & 1], sb[(g + 1) & 1]);
-      quad(ca[g & 1], cb[g & 1], sa[g & 1], sb[g & 1]);
+    for (int g = 0; g < 3; g++) {
+      const int p = g & 1;
+      read_quad(cur, g + 1, qa[p ^ 1], qb[p ^ 1], qsa[p ^ 1], qsb[p ^ 1]);
+#pragma unroll
+      for (int s = 0; s < 4; s++) {
+        if (s == 3) cvt_scales(p ^ 1);
+        if (s < 3) make_frags(p, s + 1, (s + 1) & 1);
+        else make_frags(p ^ 1, 0, 0);
+        mfmas(s & 1);
+        step_schedule();
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
-    __builtin_amdgcn_s_waitcnt(0);  // this thread's share of stage kt + 1 is in LDS
+    // quad 3 (buffer 1): the next stage becomes visible (B1) and its quad 0 is
+    // read into buffer 0 while this stage's last quad is computed; B2 then
+    // releases this stage's LDS buffer for the next prefetch.
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (kt + 1 < KT) {
-      fix_partial(kt + 1, nxt);
-      __syncthreads();
+    if (more) {
+      const int valid = (int)min((int64_t)BKS / 16, ks - (int64_t)(kt + 1) * (BKS / 16));
+      if (valid < BKS / 16) {
+        fix_partial(kt + 1, nxt);
+        __syncthreads();
+      }
+      read_quad(nxt, 0, qa[0], qb[0], qsa[0], qsb[0]);
     }
+#pragma unroll
+    for (int s = 0; s < 4; s++) {
+      if (s == 3) {
+        if (more) cvt_scales(0);
+      }
+      if (s < 3) make_frags(1, s + 1, (s + 1) & 1);
+      else if (more) make_frags(0, 0, 0);
+      mfmas(s & 1);
+      step_schedule();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __syncthreads();
   }
 
   const float alpha = a_ts[0] * b_ts[0];
