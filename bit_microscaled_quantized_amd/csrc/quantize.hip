@@ -39,7 +39,11 @@ __device__ __forceinline__ void block_atomic_max(uint32_t m, float* amax) {
   if (threadIdx.x == 0) {
     uint32_t r = red[0];
     for (int w = 1; w < (int)(blockDim.x >> 6); w++) r = r > red[w] ? r : red[w];
-    if (r != 0u) atomicMax(reinterpret_cast<unsigned int*>(amax), r);
+    // Most workgroups find a partial maximum below the running one: read it
+    // first (device-coherent) and skip the atomic, so thousands of workgroups
+    // do not serialize on one address.  The result is still the exact max.
+    unsigned int* a = reinterpret_cast<unsigned int*>(amax);
+    if (r > __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) atomicMax(a, r);
   }
 }
 
@@ -431,14 +435,14 @@ template <typename T>
 static hipError_t launch_amax(const void* x, int64_t rows, int64_t cols, int64_t ld, float* amax,
                               hipStream_t s) {
   constexpr int EPC = 16 / sizeof(T);
-  constexpr int UNROLL = 4;
+  constexpr int UNROLL = 8;
   if (ld == cols) {  // contiguous: one long row
     cols = rows * cols;
     ld = cols;
     rows = 1;
   }
   int64_t cpr = cols / EPC;
-  dim3 grid(grid_cap((cpr + 256 * UNROLL - 1) / (256 * UNROLL), 8192), grid_cap(rows, 65535));
+  dim3 grid(grid_cap((cpr + 256 * UNROLL - 1) / (256 * UNROLL), 2048), grid_cap(rows, 65535));
   k_amax<T, UNROLL><<<grid, 256, 0, s>>>(static_cast<const T*>(x), rows, cols, ld, amax);
   return hipGetLastError();
 }
