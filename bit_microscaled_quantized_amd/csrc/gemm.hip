@@ -27,12 +27,12 @@
 // codes, 4 for scales) issued one stage ahead, so no registers hold prefetched
 // data and each code load instruction covers eight full cache lines.  Chunk c
 // (16 bytes) of row r lands in slot 8r + (c ^ (r & 7)), which makes the
-// fragment reads (32 consecutive rows, same chunk) bank-conflict free.  One
-// barrier per stage.
+// fragment reads (32 consecutive rows, same chunk) bank-conflict free.
 //
-// Tiling: 256 threads = 4 waves in a 2x2 grid; workgroup tile 256 x 256, wave
-// tile 128 x 128 = 4 x 4 MFMA tiles of 32 x 32 (256 FP32 accumulators per lane,
-// in AGPRs).  Inside a stage K is permuted so that one 16-byte chunk read feeds
+// Tiling: 512 threads = 8 waves (two per SIMD, so one wave's conversions
+// overlap the other's MFMAs) in a 2 x 4 grid; workgroup tile 256 x 256, wave
+// tile 128 x 64 = 4 x 2 MFMA tiles of 32 x 32 (128 FP32 accumulators per
+// lane).  Inside a stage K is permuted so that one 16-byte chunk read feeds
 // four MFMA steps: lane half h reads chunks 4h .. 4h + 3 of its row; in quad g
 // (chunk 4h + g) step s uses the chunk's dword s, i.e. stage elements
 // 32(4h + g) + 8s .. + 7, identically for A and B, which leaves the
@@ -90,7 +90,7 @@ __device__ __forceinline__ uint32_t dw(const uint4& q, int i) {
 
 }  // namespace
 
-__global__ __launch_bounds__(256, 1) void k_gemm_nvfp4(
+__global__ __launch_bounds__(512, 1) void k_gemm_nvfp4(
     int M, int N, int K, const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
     const float* __restrict__ a_ts, const uint8_t* __restrict__ b_codes,
     const uint8_t* __restrict__ b_scales, int b_rowdiv, const float* __restrict__ b_ts,
@@ -117,16 +117,16 @@ __global__ __launch_bounds__(256, 1) void k_gemm_nvfp4(
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 2, wn = wave & 3;
   const int h = lane >> 5;
   const int lr = lane & 31;
   const int64_t kb = K / 2;   // code bytes per row (a multiple of 32)
   const int64_t ks = K / 16;  // scale bytes per row (a multiple of 4)
   const int KT = (K + BKS - 1) / BKS;
 
-  // ---- stage fetch.  Code instruction j of a wave: rows 8(8 wave + j) + l/8,
+  // ---- stage fetch.  Code instruction j of a wave: rows 8(4 wave + j) + l/8,
   // lane l takes chunk (l%8) ^ (row & 7) of its row.  Scale instruction i:
-  // rows 64 wave + 16 i + l/4, lane l takes dword l%4 of the row's 16 bytes.
+  // rows 32 wave + 16 i + l/4, lane l takes dword l%4 of the row's 16 bytes.
   const int crow = lane >> 3;
   const int cchunk = (lane & 7) ^ crow;
   const int sdw = lane & 3;
@@ -135,17 +135,17 @@ __global__ __launch_bounds__(256, 1) void k_gemm_nvfp4(
     const int64_t coff = min((int64_t)kt * (BKS / 2) + 16 * cchunk, kb - 16);
     const int64_t soff = min((int64_t)kt * (BKS / 16) + 4 * sdw, ks - 4);
 #pragma unroll
-    for (int j = 0; j < 8; j++) {
-      const int r = 8 * (8 * wave + j) + crow;
-      load_lds16(a_codes + (int64_t)min(m0 + r, M - 1) * kb + coff, st + (8 * wave + j) * 1024);
-      load_lds16(b_codes + (int64_t)min(n0 + r, N - 1) * kb + coff, st + OFF_B + (8 * wave + j) * 1024);
+    for (int j = 0; j < 4; j++) {
+      const int r = 8 * (4 * wave + j) + crow;
+      load_lds16(a_codes + (int64_t)min(m0 + r, M - 1) * kb + coff, st + (4 * wave + j) * 1024);
+      load_lds16(b_codes + (int64_t)min(n0 + r, N - 1) * kb + coff, st + OFF_B + (4 * wave + j) * 1024);
     }
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-      const int r = 64 * wave + 16 * i + (lane >> 2);
-      load_lds4(a_scales + (int64_t)min(m0 + r, M - 1) * ks + soff, st + OFF_SA + wave * 1024 + i * 256);
+    for (int i = 0; i < 2; i++) {
+      const int r = 32 * wave + 16 * i + (lane >> 2);
+      load_lds4(a_scales + (int64_t)min(m0 + r, M - 1) * ks + soff, st + OFF_SA + (2 * wave + i) * 256);
       load_lds4(b_scales + (int64_t)(min(n0 + r, N - 1) / b_rowdiv) * ks + soff,
-                st + OFF_SB + wave * 1024 + i * 256);
+                st + OFF_SB + (2 * wave + i) * 256);
     }
   };
   // In a stage that ends past K, zero the scale bytes of blocks >= K/16: their
@@ -153,117 +153,96 @@ __global__ __launch_bounds__(256, 1) void k_gemm_nvfp4(
   auto fix_partial = [&](int kt, uint8_t* st) {
     const int valid = (int)min((int64_t)BKS / 16, ks - (int64_t)kt * (BKS / 16));
     if (valid >= BKS / 16) return;
-    uint8_t* ra = st + OFF_SA + tid * 16;
-    uint8_t* rb = st + OFF_SB + tid * 16;
-    for (int i = valid; i < 16; i++) {
-      ra[i] = 0;
-      rb[i] = 0;
-    }
+    uint8_t* row = st + (tid < 256 ? OFF_SA + tid * 16 : OFF_SB + (tid - 256) * 16);
+    for (int i = valid; i < 16; i++) row[i] = 0;
   };
 
-  // ---- fragment reads.  Lane (h, lr) of A tile i reads row wm*128 + 32i + lr,
-  // chunk 4h + g in quad g: slot 8*row + ((4h + g) ^ (lr & 7)); its two scale
-  // bytes (blocks 2(4h + g), 2(4h + g) + 1) sit at row*16 + 2(4h + g).
+  // ---- fragment reads.  Lane (h, lr) of A tile i reads row wm*128 + 32i + lr
+  // (B tile j: row wn*64 + 32j + lr), chunk 4h + g in quad g: slot
+  // 8*row + ((4h + g) ^ (lr & 7)); its two scale bytes (blocks 2(4h + g) and
+  // 2(4h + g) + 1) sit at row*16 + 2(4h + g).
   const int rowa = wm * 128 + lr;
-  const int rowb = wn * 128 + lr;
+  const int rowb = wn * 64 + lr;
   auto read_quad = [&](const uint8_t* st, int g, uint4* ca, uint4* cb, uint32_t* sa, uint32_t* sb) {
     const int sw = ((4 * h + g) ^ (lr & 7)) << 4;
 #pragma unroll
     for (int i = 0; i < 4; i++) {
       ca[i] = *reinterpret_cast<const uint4*>(st + (rowa + 32 * i) * 128 + sw);
-      cb[i] = *reinterpret_cast<const uint4*>(st + OFF_B + (rowb + 32 * i) * 128 + sw);
       sa[i] = *reinterpret_cast<const uint16_t*>(st + OFF_SA + (rowa + 32 * i) * 16 + 2 * (4 * h + g));
-      sb[i] = *reinterpret_cast<const uint16_t*>(st + OFF_SB + (rowb + 32 * i) * 16 + 2 * (4 * h + g));
+    }
+#pragma unroll
+    for (int j = 0; j < 2; j++) {
+      cb[j] = *reinterpret_cast<const uint4*>(st + OFF_B + (rowb + 32 * j) * 128 + sw);
+      sb[j] = *reinterpret_cast<const uint16_t*>(st + OFF_SB + (rowb + 32 * j) * 16 + 2 * (4 * h + g));
     }
   };
 
-  floatx16 acc[4][4];
+  floatx16 acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; i++)
 #pragma unroll
-    for (int j = 0; j < 4; j++)
+    for (int j = 0; j < 2; j++)
 #pragma unroll
       for (int r = 0; r < 16; r++) acc[i][j][r] = 0.0f;
 
-  // Quad data (chunks + scale bytes of 4 A and 4 B tiles), double-buffered by
-  // quad parity, and the FP16 fragments of one MFMA step, double-buffered by
-  // step parity.
-  uint4 qa[2][4], qb[2][4];
-  uint32_t qsa[2][4], qsb[2][4];
-  half2_t sca[2][4][2], scb[2][4][2];
-  half8_t fa[2][4], fb[2][4];
+  // quad data double-buffered by quad parity
+  uint4 qa[2][4], qb[2][2];
+  uint32_t qsa[2][4], qsb[2][2];
 
-  auto cvt_scales = [&](int p) {
+  // 4 MFMA steps on the quad in buffer p: per step, convert the 6 fragments
+  // (48 VALU) and issue 8 MFMAs; the other wave on the SIMD overlaps them
+  auto quad = [&](int p) {
+    half2_t sca[4][2], scb[2][2];
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-      half2_t pa = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(qsa[p][i], 1.0f, false);
-      half2_t pb = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(qsb[p][i], 1.0f, false);
-      sca[p][i][0] = half2_t{pa[0], pa[0]};
-      sca[p][i][1] = half2_t{pa[1], pa[1]};
-      scb[p][i][0] = half2_t{pb[0], pb[0]};
-      scb[p][i][1] = half2_t{pb[1], pb[1]};
+      half2_t v = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(qsa[p][i], 1.0f, false);
+      sca[i][0] = half2_t{v[0], v[0]};
+      sca[i][1] = half2_t{v[1], v[1]};
     }
-  };
-  // fragments of step s of the quad in buffer p into fragment buffer f
-  auto make_frags = [&](int p, int s, int f) {
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-      fa[f][i] = dequant8(dw(qa[p][i], s), sca[p][i][s >> 1]);
-      fb[f][i] = dequant8(dw(qb[p][i], s), scb[p][i][s >> 1]);
+    for (int j = 0; j < 2; j++) {
+      half2_t v = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(qsb[p][j], 1.0f, false);
+      scb[j][0] = half2_t{v[0], v[0]};
+      scb[j][1] = half2_t{v[1], v[1]};
     }
-  };
-  auto mfmas = [&](int f) {
 #pragma unroll
-    for (int i = 0; i < 4; i++)
+    for (int s = 0; s < 4; s++) {
+      half8_t fa[4], fb[2];
 #pragma unroll
-      for (int j = 0; j < 4; j++)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[f][i], fb[f][j], acc[i][j], 0, 0, 0);
-  };
-  // MFMA / VALU / LDS interleave for one step: every MFMA is followed by the
-  // conversion work of the next step's fragments
-  auto step_schedule = [&]() {
+      for (int i = 0; i < 4; i++) fa[i] = dequant8(dw(qa[p][i], s), sca[i][s >> 1]);
 #pragma unroll
-    for (int q = 0; q < 16; q++) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU
-      if (q < 4) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+      for (int j = 0; j < 2; j++) fb[j] = dequant8(dw(qb[p][j], s), scb[j][s >> 1]);
+#pragma unroll
+      for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int j = 0; j < 2; j++)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[i], fb[j], acc[i][j], 0, 0, 0);
     }
   };
 
-  // prologue: stage 0 in buffer 0, quad 0 read, step-0 fragments built
+  // prologue: stage 0 in buffer 0, its quad 0 read
   issue_stage(0, lds);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   fix_partial(0, lds);
   __syncthreads();
   read_quad(lds, 0, qa[0], qb[0], qsa[0], qsb[0]);
-  cvt_scales(0);
-  make_frags(0, 0, 0);
 
   for (int kt = 0; kt < KT; kt++) {
     uint8_t* cur = lds + (kt & 1) * STAGE_BYTES;
     uint8_t* nxt = lds + ((kt + 1) & 1) * STAGE_BYTES;
     const bool more = kt + 1 < KT;
     if (more) issue_stage(kt + 1, nxt);
-    __builtin_amdgcn_sched_barrier(0);
     // quads 0..2: read the following quad of this stage while computing
 #pragma unroll
     for (int g = 0; g < 3; g++) {
       const int p = g & 1;
       read_quad(cur, g + 1, qa[p ^ 1], qb[p ^ 1], qsa[p ^ 1], qsb[p ^ 1]);
-#pragma unroll
-      for (int s = 0; s < 4; s++) {
-        if (s == 3) cvt_scales(p ^ 1);
-        if (s < 3) make_frags(p, s + 1, (s + 1) & 1);
-        else make_frags(p ^ 1, 0, 0);
-        mfmas(s & 1);
-        step_schedule();
-        __builtin_amdgcn_sched_barrier(0);
-      }
+      quad(p);
     }
-    // quad 3 (buffer 1): the next stage becomes visible (B1) and its quad 0 is
-    // read into buffer 0 while this stage's last quad is computed; B2 then
-    // releases this stage's LDS buffer for the next prefetch.
+    // quad 3 (buffer 1): the next stage becomes visible, its quad 0 is read
+    // into buffer 0 while this stage's last quad is computed, and a final
+    // barrier releases this stage's LDS buffer for the next prefetch.
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (more) {
@@ -274,17 +253,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_nvfp4(
       }
       read_quad(nxt, 0, qa[0], qb[0], qsa[0], qsb[0]);
     }
-#pragma unroll
-    for (int s = 0; s < 4; s++) {
-      if (s == 3) {
-        if (more) cvt_scales(0);
-      }
-      if (s < 3) make_frags(1, s + 1, (s + 1) & 1);
-      else if (more) make_frags(0, 0, 0);
-      mfmas(s & 1);
-      step_schedule();
-      __builtin_amdgcn_sched_barrier(0);
-    }
+    quad(1);
     __syncthreads();
   }
 
@@ -292,8 +261,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_nvfp4(
 #pragma unroll
   for (int i = 0; i < 4; i++)
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-      const int n = n0 + wn * 128 + j * 32 + lr;
+    for (int j = 0; j < 2; j++) {
+      const int n = n0 + wn * 64 + j * 32 + lr;
 #pragma unroll
       for (int r = 0; r < 16; r++) {
         const int m = m0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
@@ -319,7 +288,7 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
   });
   if (attr_err != hipSuccess) return attr_err;
   const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  k_gemm_nvfp4<<<(unsigned)tiles, 256, LDS_BYTES, s>>>((int)M, (int)N, (int)K, a_codes, a_scales,
+  k_gemm_nvfp4<<<(unsigned)tiles, 512, LDS_BYTES, s>>>((int)M, (int)N, (int)K, a_codes, a_scales,
                                                        a_ts, b_codes, b_scales, b_rowdiv, b_ts, c,
                                                        ldc, accumulate);
   return hipGetLastError();
