@@ -125,20 +125,20 @@ def gpu_bench(inp, steps, warmup):
             x, bf, T, I, I, nv.NVFP4_ROW_1D, nv.NVFP4_RNE, 0, qx.codes, qx.scales, None, None,
             qx.ts, qx.amax))
         timed("gemm_fprop", lambda: nv.nvfp4_gemm(
-            T, O, I, qx.codes, qx.scales, qx.ts, q.codes, q.scales, 16, q.ts, st.y, O, 0.0))
+            T, O, I, qx.codes, qx.scales, qx.ts, q.codes, q.scales, 16, q.ts, st.y, O, 0.0, workspace=st.ws))
         qd = st.qdy
         timed("quant_dy_row_sr", lambda: nv.nvfp4_quantize(
             dy, bf, T, O, O, nv.NVFP4_ROW_1D, nv.NVFP4_SR, s_row, qd.codes, qd.scales, None, None,
             qd.ts, qd.amax))
         timed("gemm_dgrad", lambda: nv.nvfp4_gemm(
-            T, I, O, qd.codes, qd.scales, qd.ts, q.codes_t, q.scales_t, 16, q.ts, st.dx, I, 0.0))
+            T, I, O, qd.codes, qd.scales, qd.ts, q.codes_t, q.scales_t, 16, q.ts, st.dx, I, 0.0, workspace=st.ws))
         a_, b_ = st.qdy_t, st.qx_t
         timed("quant_dy_rht_sr", lambda: nv.nvfp4_rht_quantize(
             dy, bf, T, O, O, mask, nv.NVFP4_SR, s_col, a_.codes, a_.scales, a_.ts, a_.amax))
         timed("quant_x_rht", lambda: nv.nvfp4_rht_quantize(
             x, bf, T, I, I, mask, nv.NVFP4_RNE, 0, b_.codes, b_.scales, b_.ts, b_.amax))
         timed("gemm_wgrad", lambda: nv.nvfp4_gemm(
-            O, I, T, a_.codes, a_.scales, a_.ts, b_.codes, b_.scales, 1, b_.ts, st.dw, I, 0.0))
+            O, I, T, a_.codes, a_.scales, a_.ts, b_.codes, b_.scales, 1, b_.ts, st.dw, I, 0.0, workspace=st.ws))
 
     for _ in range(warmup):
         one_step(None)

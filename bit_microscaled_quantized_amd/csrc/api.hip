@@ -1,6 +1,7 @@
 // C-ABI entry points of libnvfp4 (declared and documented in include/nvfp4.h):
 // argument validation on the host, then asynchronous launches on the caller's
-// stream.  No allocation, no state.
+// stream.  No allocation; the only state is a per-device cache of the compute
+// unit count.
 #include "../../include/nvfp4.h"
 #include "nvfp4_launch.hpp"
 
@@ -18,6 +19,12 @@ nvfp4_status check_tensor(const void* x, int dt, int64_t rows, int64_t cols, int
   if ((rows - 1) * ld + cols >= (int64_t(1) << 40)) return NVFP4_ESHAPE;
   const int64_t esize = dt == NVFP4_BF16 ? 2 : 4;
   if (!aligned16(x) || (ld * esize) % 16 != 0) return NVFP4_EALIGN;
+  return NVFP4_OK;
+}
+
+nvfp4_status check_gemm_shape(int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || N <= 0 || K <= 0 || M % 16 != 0 || N % 16 != 0 || K % 64 != 0) return NVFP4_ESHAPE;
+  if (M >= (int64_t(1) << 31) || N >= (int64_t(1) << 31) || K >= (int64_t(1) << 31)) return NVFP4_ESHAPE;
   return NVFP4_OK;
 }
 
@@ -62,24 +69,34 @@ nvfp4_status nvfp4_rht_quantize(const void* x, int dt, int64_t tokens, int64_t c
   return e == hipSuccess ? NVFP4_OK : NVFP4_EHIP;
 }
 
+nvfp4_status nvfp4_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int64_t* bytes) {
+  if (bytes == nullptr) return NVFP4_EINVAL;
+  nvfp4_status st = check_gemm_shape(M, N, K);
+  if (st != NVFP4_OK) return st;
+  *bytes = nvfp4::gemm_workspace_size(M, N, K);
+  return NVFP4_OK;
+}
+
 nvfp4_status nvfp4_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
                         const uint8_t* a_scales, const float* a_tensor_scale,
                         const uint8_t* b_codes, const uint8_t* b_scales, int32_t b_scale_rowdiv,
                         const float* b_tensor_scale, float* c, int64_t ldc, float beta,
-                        void* stream) {
+                        void* workspace, int64_t workspace_bytes, void* stream) {
   if (a_codes == nullptr || a_scales == nullptr || a_tensor_scale == nullptr ||
       b_codes == nullptr || b_scales == nullptr || b_tensor_scale == nullptr || c == nullptr)
     return NVFP4_EINVAL;
   if (b_scale_rowdiv != 1 && b_scale_rowdiv != 16) return NVFP4_EINVAL;
   if (beta != 0.0f && beta != 1.0f) return NVFP4_EINVAL;
-  if (M <= 0 || N <= 0 || K <= 0 || M % 16 != 0 || N % 16 != 0 || K % 64 != 0) return NVFP4_ESHAPE;
-  if (M >= (int64_t(1) << 31) || N >= (int64_t(1) << 31) || K >= (int64_t(1) << 31)) return NVFP4_ESHAPE;
-  if (ldc < N) return NVFP4_ESHAPE;
+  nvfp4_status st = check_gemm_shape(M, N, K);
+  if (st != NVFP4_OK) return st;
+  if (ldc < N || workspace_bytes < 0) return NVFP4_ESHAPE;
   if (!aligned16(a_codes) || !aligned16(b_codes) || !aligned4(a_scales) || !aligned4(b_scales) ||
-      !aligned4(a_tensor_scale) || !aligned4(b_tensor_scale) || !aligned16(c) || ldc % 4 != 0)
+      !aligned4(a_tensor_scale) || !aligned4(b_tensor_scale) || !aligned16(c) || ldc % 4 != 0 ||
+      !aligned16(workspace))
     return NVFP4_EALIGN;
   hipError_t e = nvfp4::launch_gemm(M, N, K, a_codes, a_scales, a_tensor_scale, b_codes, b_scales,
                                     b_scale_rowdiv, b_tensor_scale, c, ldc, beta == 1.0f ? 1 : 0,
+                                    workspace, workspace == nullptr ? 0 : workspace_bytes,
                                     static_cast<hipStream_t>(stream));
   return e == hipSuccess ? NVFP4_OK : NVFP4_EHIP;
 }

@@ -41,7 +41,17 @@
 // contribution), past M/N the outputs are never stored.  Workgroups are
 // remapped so that each XCD's share of the grid is a contiguous, grouped range
 // of output tiles (shared L2).
+//
+// Grid tail: with one 256 x 256 tile per CU, a tile count that is not a
+// multiple of the CU count leaves the last round partly idle (8192 x 5120
+// output: 640 tiles = 2.5 rounds).  Given a workspace, the launcher keeps the
+// whole rounds as they are and splits each of the t tiles of the last round
+// into S contiguous K ranges (t * S <= CUs); those units store their raw FP32
+// partial tiles in the workspace and a second kernel adds them in the fixed
+// order 0 .. S-1, scales by the tensor scales and applies beta, so the result
+// does not depend on scheduling.
 #include <mutex>
+#include <vector>
 
 #include "nvfp4_device.hpp"
 #include "nvfp4_launch.hpp"
@@ -88,30 +98,50 @@ __device__ __forceinline__ uint32_t dw(const uint4& q, int i) {
   return i == 0 ? q.x : i == 1 ? q.y : i == 2 ? q.z : q.w;
 }
 
+// Output tile of ordered tile index id: tiles are walked in groups of GROUP
+// tile rows, column by column inside a group.
+constexpr int GROUP = 8;
+__device__ __forceinline__ void tile_of(int id, int num_m, int num_n, int& pm, int& pn) {
+  const int width = GROUP * num_n;
+  const int first_m = (id / width) * GROUP;
+  const int gsz = min(num_m - first_m, GROUP);
+  pm = first_m + (id % width) % gsz;
+  pn = (id % width) / gsz;
+}
+
 }  // namespace
 
 __global__ __launch_bounds__(512, 1) void k_gemm_nvfp4(
     int M, int N, int K, const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
     const float* __restrict__ a_ts, const uint8_t* __restrict__ b_codes,
     const uint8_t* __restrict__ b_scales, int b_rowdiv, const float* __restrict__ b_ts,
-    float* __restrict__ c, int64_t ldc, int accumulate) {
+    float* __restrict__ c, int64_t ldc, int accumulate, int full_tiles, int split,
+    float* __restrict__ partial) {
   extern __shared__ __align__(16) uint8_t lds[];
 
-  // XCD-aware tile order: the hardware deals workgroups round-robin over the
-  // 8 XCDs, so gather each XCD's share into a contiguous range of tiles, then
-  // walk the tiles in groups of GROUP tile rows.
-  const int G = gridDim.x;
+  const int KT = (K + BKS - 1) / BKS;
   const int bid = blockIdx.x;
-  const int xcd = bid & 7, per = G >> 3, rem = G & 7;
-  const int id = (xcd < rem) ? xcd * (per + 1) + (bid >> 3) : rem * (per + 1) + (xcd - rem) * per + (bid >> 3);
+  int id, kt0 = 0, kt1 = KT;
+  float* part = nullptr;
+  if (bid < full_tiles) {
+    // XCD-aware order: the hardware deals workgroups round-robin over the 8
+    // XCDs, so each XCD's share becomes a contiguous range of ordered tiles.
+    const int G = full_tiles;
+    const int xcd = bid & 7, per = G >> 3, rem = G & 7;
+    id = (xcd < rem) ? xcd * (per + 1) + (bid >> 3) : rem * (per + 1) + (xcd - rem) * per + (bid >> 3);
+  } else {
+    // split unit u = tail tile (u / split), K part (u % split)
+    const int u = bid - full_tiles;
+    const int q = u % split;
+    id = full_tiles + u / split;
+    kt0 = (int)((int64_t)KT * q / split);
+    kt1 = (int)((int64_t)KT * (q + 1) / split);
+    part = partial + (int64_t)u * (BM * BN);
+  }
   const int num_m = (M + BM - 1) / BM;
   const int num_n = (N + BN - 1) / BN;
-  constexpr int GROUP = 8;
-  const int width = GROUP * num_n;
-  const int first_m = (id / width) * GROUP;
-  const int gsz = min(num_m - first_m, GROUP);
-  const int pm = first_m + (id % width) % gsz;
-  const int pn = (id % width) / gsz;
+  int pm, pn;
+  tile_of(id, num_m, num_n, pm, pn);
   const int m0 = pm * BM, n0 = pn * BN;
 
   const int tid = threadIdx.x;
@@ -122,7 +152,6 @@ __global__ __launch_bounds__(512, 1) void k_gemm_nvfp4(
   const int lr = lane & 31;
   const int64_t kb = K / 2;   // code bytes per row (a multiple of 32)
   const int64_t ks = K / 16;  // scale bytes per row (a multiple of 4)
-  const int KT = (K + BKS - 1) / BKS;
 
   // ---- stage fetch.  Code instruction j of a wave: rows 8(4 wave + j) + l/8,
   // lane l takes chunk (l%8) ^ (row & 7) of its row.  Scale instruction i:
@@ -220,18 +249,18 @@ __global__ __launch_bounds__(512, 1) void k_gemm_nvfp4(
     }
   };
 
-  // prologue: stage 0 in buffer 0, its quad 0 read
-  issue_stage(0, lds);
+  // prologue: stage kt0 in buffer 0, its quad 0 read
+  issue_stage(kt0, lds);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  fix_partial(0, lds);
+  fix_partial(kt0, lds);
   __syncthreads();
   read_quad(lds, 0, qa[0], qb[0], qsa[0], qsb[0]);
 
-  for (int kt = 0; kt < KT; kt++) {
-    uint8_t* cur = lds + (kt & 1) * STAGE_BYTES;
-    uint8_t* nxt = lds + ((kt + 1) & 1) * STAGE_BYTES;
-    const bool more = kt + 1 < KT;
+  for (int kt = kt0; kt < kt1; kt++) {
+    uint8_t* cur = lds + ((kt - kt0) & 1) * STAGE_BYTES;
+    uint8_t* nxt = lds + ((kt - kt0 + 1) & 1) * STAGE_BYTES;
+    const bool more = kt + 1 < kt1;
     if (more) issue_stage(kt + 1, nxt);
     // quads 0..2: read the following quad of this stage while computing
 #pragma unroll
@@ -257,6 +286,20 @@ __global__ __launch_bounds__(512, 1) void k_gemm_nvfp4(
     __syncthreads();
   }
 
+  if (part != nullptr) {
+    // raw partial tile, row-major 256 x 256 (rows / columns past M / N are
+    // stored too and ignored by the reduction)
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+      for (int j = 0; j < 2; j++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) {
+          const int tm = wm * 128 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+          part[tm * BN + wn * 64 + j * 32 + lr] = acc[i][j][r];
+        }
+    return;
+  }
   const float alpha = a_ts[0] * b_ts[0];
 #pragma unroll
   for (int i = 0; i < 4; i++)
@@ -276,10 +319,92 @@ __global__ __launch_bounds__(512, 1) void k_gemm_nvfp4(
     }
 }
 
+// Sum of the S partial tiles of each split tail tile in the order 0 .. S-1,
+// then C = alpha * sum (+ C).  Block (x, t): tail tile t, rows 4x .. 4x + 3;
+// thread: one row, four consecutive columns.
+__global__ __launch_bounds__(256) void k_gemm_split_reduce(int M, int N, int full_tiles, int split,
+                                                           const float* __restrict__ partial,
+                                                           const float* __restrict__ a_ts,
+                                                           const float* __restrict__ b_ts,
+                                                           float* __restrict__ c, int64_t ldc,
+                                                           int accumulate) {
+  const int t = blockIdx.y;
+  int pm, pn;
+  tile_of(full_tiles + t, (M + BM - 1) / BM, (N + BN - 1) / BN, pm, pn);
+  const int e = blockIdx.x * 256 + threadIdx.x;  // float4 index inside the tile
+  const int r = e / (BN / 4), c4 = (e % (BN / 4)) * 4;
+  const int m = pm * BM + r, n = pn * BN + c4;
+  if (m >= M || n >= N) return;  // N is a multiple of 16: a float4 is all in or all out
+  const float4* src = reinterpret_cast<const float4*>(partial + (int64_t)t * split * (BM * BN)) + e;
+  float4 v = src[0];
+  for (int q = 1; q < split; q++) {
+    const float4 w = src[(int64_t)q * (BM * BN / 4)];
+    v.x += w.x; v.y += w.y; v.z += w.z; v.w += w.w;
+  }
+  const float alpha = a_ts[0] * b_ts[0];
+  float4* dst = reinterpret_cast<float4*>(c + (int64_t)m * ldc + n);
+  float4 o = make_float4(alpha * v.x, alpha * v.y, alpha * v.z, alpha * v.w);
+  if (accumulate) {
+    const float4 old = *dst;
+    o.x += old.x; o.y += old.y; o.z += old.z; o.w += old.w;
+  }
+  *dst = o;
+}
+
+namespace {
+
+// Compute units of the current device (cached per device).
+int device_cus() {
+  static std::mutex mu;
+  static std::vector<int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  if ((int)cache.size() <= dev) cache.resize(dev + 1, 0);
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+struct SplitPlan {
+  int64_t tiles = 0;
+  int64_t full = 0;   // tiles computed whole
+  int split = 1;      // K parts per tail tile (1: no split)
+  int64_t bytes = 0;  // workspace bytes for the partial tiles
+};
+
+// Tail tiles t = tiles mod CUs; split S = min(CUs / t, KT / 4, 16) when that
+// is at least 2, so the t * S units fill at most one round and each part
+// keeps at least four K stages.
+SplitPlan plan_split(int64_t M, int64_t N, int64_t K) {
+  SplitPlan p;
+  p.tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  p.full = p.tiles;
+  const int cus = device_cus();
+  if (cus <= 0) return p;
+  const int64_t t = p.tiles % cus;
+  const int64_t kt = (K + BKS - 1) / BKS;
+  if (t == 0) return p;
+  const int64_t s = std::min<int64_t>(std::min<int64_t>(cus / t, kt / 4), 16);
+  if (s < 2) return p;
+  p.full = p.tiles - t;
+  p.split = (int)s;
+  p.bytes = t * s * (int64_t)(BM * BN) * (int64_t)sizeof(float);
+  return p;
+}
+
+}  // namespace
+
+int64_t gemm_workspace_size(int64_t M, int64_t N, int64_t K) { return plan_split(M, N, K).bytes; }
+
 hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
                        const uint8_t* a_scales, const float* a_ts, const uint8_t* b_codes,
                        const uint8_t* b_scales, int b_rowdiv, const float* b_ts, float* c,
-                       int64_t ldc, int accumulate, hipStream_t s) {
+                       int64_t ldc, int accumulate, void* workspace, int64_t workspace_bytes,
+                       hipStream_t s) {
   static std::once_flag once;
   static hipError_t attr_err = hipSuccess;
   std::call_once(once, [] {
@@ -287,10 +412,21 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
                                    hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
   });
   if (attr_err != hipSuccess) return attr_err;
-  const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  k_gemm_nvfp4<<<(unsigned)tiles, 512, LDS_BYTES, s>>>((int)M, (int)N, (int)K, a_codes, a_scales,
-                                                       a_ts, b_codes, b_scales, b_rowdiv, b_ts, c,
-                                                       ldc, accumulate);
+  SplitPlan p = plan_split(M, N, K);
+  if (p.split > 1 && (workspace == nullptr || workspace_bytes < p.bytes)) {
+    p.full = p.tiles;
+    p.split = 1;
+  }
+  const int64_t tail = p.tiles - p.full;
+  const int64_t grid = p.full + tail * p.split;
+  float* partial = static_cast<float*>(p.split > 1 ? workspace : nullptr);
+  k_gemm_nvfp4<<<(unsigned)grid, 512, LDS_BYTES, s>>>(
+      (int)M, (int)N, (int)K, a_codes, a_scales, a_ts, b_codes, b_scales, b_rowdiv, b_ts, c, ldc,
+      accumulate, (int)p.full, p.split, partial);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.split == 1) return e;
+  k_gemm_split_reduce<<<dim3(BM * BN / 4 / 256, (unsigned)tail), 256, 0, s>>>(
+      (int)M, (int)N, (int)p.full, p.split, partial, a_ts, b_ts, c, ldc, accumulate);
   return hipGetLastError();
 }
 

@@ -18,6 +18,11 @@ hipError_t launch_rht_quantize(const void* x, int dt, int64_t tokens, int64_t co
 hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
                        const uint8_t* a_scales, const float* a_ts, const uint8_t* b_codes,
                        const uint8_t* b_scales, int b_rowdiv, const float* b_ts, float* c,
-                       int64_t ldc, int accumulate, hipStream_t s);
+                       int64_t ldc, int accumulate, void* workspace, int64_t workspace_bytes,
+                       hipStream_t s);
+
+// Workspace bytes launch_gemm uses for this shape on the current device
+// (0: no split).
+int64_t gemm_workspace_size(int64_t M, int64_t N, int64_t K);
 
 }  // namespace nvfp4

@@ -9,7 +9,8 @@ summary, Resumo tecnico, 2. Metodologia Proposta):
                       SR on dY, RNE on X                          (techniques 2, 4)
 Shapes: X [T x IN], W [OUT x IN], dY [T x OUT]; Y [T x OUT], dX [T x IN],
 dW [OUT x IN].  Every step is one call into libnvfp4; this module only owns the
-device buffers (allocated once) and the call order on one stream.
+device buffers (allocated once, including the GEMM workspace shared by the three
+GEMMs, which therefore must stay on one stream) and the call order.
 """
 from __future__ import annotations
 
@@ -62,6 +63,9 @@ class LinearStep:
         self.y = torch.empty((T, OUT), **f32)
         self.dx = torch.empty((T, IN), **f32)
         self.dw = torch.zeros((OUT, IN), **f32)
+        ws = max(nv.nvfp4_gemm_workspace_size(T, OUT, IN), nv.nvfp4_gemm_workspace_size(T, IN, OUT),
+                 nv.nvfp4_gemm_workspace_size(OUT, IN, T))
+        self.ws = torch.empty(max(ws, 16), dtype=torch.uint8, device=device)
 
     def quantize_weight(self, w, dt, stream=None):
         q = self.qw
@@ -74,7 +78,7 @@ class LinearStep:
                           q.codes, q.scales, None, None, q.ts, q.amax, stream)
         w = self.qw
         nv.nvfp4_gemm(self.T, self.OUT, self.IN, q.codes, q.scales, q.ts, w.codes, w.scales, 16,
-                      w.ts, self.y, self.OUT, 0.0, stream)
+                      w.ts, self.y, self.OUT, 0.0, workspace=self.ws, stream=stream)
 
     def backward(self, x, dy, dt, sign_mask: int, seed_row: int, seed_col: int,
                  accumulate_wgrad: bool = False, stream=None):
@@ -84,14 +88,14 @@ class LinearStep:
                           q.codes, q.scales, None, None, q.ts, q.amax, stream)
         w = self.qw
         nv.nvfp4_gemm(T, IN, OUT, q.codes, q.scales, q.ts, w.codes_t, w.scales_t, 16, w.ts,
-                      self.dx, IN, 0.0, stream)
+                      self.dx, IN, 0.0, workspace=self.ws, stream=stream)
         a, b = self.qdy_t, self.qx_t
         nv.nvfp4_rht_quantize(dy, dt, T, OUT, OUT, sign_mask, nv.NVFP4_SR, seed_col, a.codes,
                               a.scales, a.ts, a.amax, stream)
         nv.nvfp4_rht_quantize(x, dt, T, IN, IN, sign_mask, nv.NVFP4_RNE, 0, b.codes, b.scales,
                               b.ts, b.amax, stream)
         nv.nvfp4_gemm(OUT, IN, T, a.codes, a.scales, a.ts, b.codes, b.scales, 1, b.ts, self.dw,
-                      IN, 1.0 if accumulate_wgrad else 0.0, stream)
+                      IN, 1.0 if accumulate_wgrad else 0.0, workspace=self.ws, stream=stream)
 
     def step(self, x, w, dy, dt, sign_mask: int, seed_row: int, seed_col: int,
              accumulate_wgrad: bool = False, quantize_weight: bool = True, stream=None):

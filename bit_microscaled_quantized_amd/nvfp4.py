@@ -19,7 +19,8 @@ NVFP4_BF16, NVFP4_F32 = 0, 1
 NVFP4_RNE, NVFP4_SR = 0, 1
 NVFP4_ROW_1D, NVFP4_COL_1D, NVFP4_TILE_2D = 0, 1, 2
 
-EXPORTED = ("nvfp4_quantize", "nvfp4_rht_quantize", "nvfp4_gemm", "nvfp4_status_str")
+EXPORTED = ("nvfp4_quantize", "nvfp4_rht_quantize", "nvfp4_gemm", "nvfp4_gemm_workspace_size",
+            "nvfp4_status_str")
 
 _lib = None
 
@@ -49,8 +50,10 @@ def load_library():
     L.nvfp4_quantize.restype = i32
     L.nvfp4_rht_quantize.argtypes = [vp, i32, i64, i64, i64, u32, i32, u64, vp, vp, vp, vp, vp]
     L.nvfp4_rht_quantize.restype = i32
-    L.nvfp4_gemm.argtypes = [i64, i64, i64, vp, vp, vp, vp, vp, i32, vp, vp, i64, f32, vp]
+    L.nvfp4_gemm.argtypes = [i64, i64, i64, vp, vp, vp, vp, vp, i32, vp, vp, i64, f32, vp, i64, vp]
     L.nvfp4_gemm.restype = i32
+    L.nvfp4_gemm_workspace_size.argtypes = [i64, i64, i64, ctypes.POINTER(i64)]
+    L.nvfp4_gemm_workspace_size.restype = i32
     L.nvfp4_status_str.argtypes = [i32]
     L.nvfp4_status_str.restype = ctypes.c_char_p
     _lib = L
@@ -102,9 +105,23 @@ def nvfp4_rht_quantize(x, dt, tokens, cols, ld_x, sign_mask, rnd, seed, codes, s
 
 
 def nvfp4_gemm(M, N, K, a_codes, a_scales, a_tensor_scale, b_codes, b_scales, b_scale_rowdiv,
-               b_tensor_scale, c, ldc, beta, stream=None, raise_on_error=True) -> int:
+               b_tensor_scale, c, ldc, beta, workspace=None, workspace_bytes=None, stream=None,
+               raise_on_error=True) -> int:
+    """`workspace_bytes=None` takes the size of a torch-tensor workspace (0 for
+    a raw address or None)."""
+    if workspace_bytes is None:
+        workspace_bytes = 0 if workspace is None or isinstance(workspace, int) else \
+            workspace.numel() * workspace.element_size()
     st = load_library().nvfp4_gemm(
         M, N, K, _addr(a_codes), _addr(a_scales), _addr(a_tensor_scale), _addr(b_codes),
         _addr(b_scales), b_scale_rowdiv, _addr(b_tensor_scale), _addr(c), ldc, float(beta),
-        _stream(stream))
+        _addr(workspace), int(workspace_bytes), _stream(stream))
     return _check("nvfp4_gemm", st, raise_on_error)
+
+
+def nvfp4_gemm_workspace_size(M, N, K) -> int:
+    """Workspace bytes nvfp4_gemm uses for this shape on the current device."""
+    out = ctypes.c_int64(0)
+    _check("nvfp4_gemm_workspace_size",
+           load_library().nvfp4_gemm_workspace_size(M, N, K, ctypes.byref(out)), True)
+    return out.value

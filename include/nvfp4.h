@@ -29,8 +29,9 @@
  *
  * Conventions for every entry point:
  *   - All tensor pointers are DEVICE pointers owned by the caller.  The library
- *     allocates and frees nothing, keeps no state between calls and is
- *     reentrant; calls on different streams may overlap.
+ *     allocates and frees nothing and is reentrant; calls on different streams
+ *     may overlap (but not while sharing a GEMM workspace).  Its only state is
+ *     a per-device cache of the compute-unit count.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
  *     work is enqueued asynchronously on it; results are visible after the
  *     caller synchronizes that stream.
@@ -133,12 +134,28 @@ nvfp4_status nvfp4_rht_quantize(const void *x, int dt, int64_t tokens, int64_t c
  *   Products e2m1 * E4M3 are exact in FP16, so the kernel dequantizes the
  *   block-scaled operands exactly and contracts them on FP16 matrix cores with
  *   FP32 accumulation; the two tensor scales are applied in the epilogue.
+ *   workspace, workspace_bytes: optional device scratch (16-byte aligned) of at
+ *   least nvfp4_gemm_workspace_size() bytes.  With it, the output tiles of an
+ *   incomplete last round over the compute units are split along K and their
+ *   FP32 partial sums are added in a fixed order by a second kernel on the
+ *   same stream (deterministic: the result depends only on the shape and the
+ *   inputs).  NULL, or fewer bytes than needed, runs without the split (same
+ *   result up to FP32 summation order).  The workspace is in use until the
+ *   call's work on `stream` completes.
  */
 nvfp4_status nvfp4_gemm(int64_t M, int64_t N, int64_t K, const uint8_t *a_codes,
                         const uint8_t *a_scales, const float *a_tensor_scale,
                         const uint8_t *b_codes, const uint8_t *b_scales, int32_t b_scale_rowdiv,
                         const float *b_tensor_scale, float *c, int64_t ldc, float beta,
-                        void *stream);
+                        void *workspace, int64_t workspace_bytes, void *stream);
+
+/*
+ * nvfp4_gemm_workspace_size -- bytes of workspace nvfp4_gemm uses for an
+ * M x N x K problem on the CURRENT device (0 when that shape needs none; at
+ * most 256 KiB per compute unit).  Shape rules and errors as for nvfp4_gemm;
+ * `bytes` must not be NULL.
+ */
+nvfp4_status nvfp4_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int64_t *bytes);
 
 /* Static, human-readable name of a status code. */
 const char *nvfp4_status_str(int status);

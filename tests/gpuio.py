@@ -84,16 +84,24 @@ def gpu_rht_quantize(x: np.ndarray, sign_mask: int, rnd: int = 0, seed: int = 0)
 
 
 def gpu_gemm(M, N, K, a: dict, b: dict, b_rowdiv: int, c0: np.ndarray | None = None,
-             beta: float = 0.0) -> np.ndarray:
+             beta: float = 0.0, workspace="auto") -> np.ndarray:
     """C = beta*C0 + A.B^T from device-resident quantize outputs a, b (dicts with
-    dev codes/scales/ts as returned above; b may name its transposed copy)."""
+    dev codes/scales/ts as returned above; b may name its transposed copy).
+    workspace: "auto" allocates the size the library asks for, None passes NULL,
+    an int passes a workspace of that many bytes."""
     torch = torch_cuda()
     if c0 is None:
         c = torch.zeros((M, N), dtype=torch.float32, device="cuda")
     else:
         c = to_dev(np.ascontiguousarray(c0, dtype=np.float32))
+    if isinstance(workspace, str):
+        workspace = nv.nvfp4_gemm_workspace_size(M, N, K)
+    ws = None
+    if workspace:
+        # filled with NaN so that a partial tile the kernel failed to write shows
+        ws = torch.full((workspace // 4,), float("nan"), dtype=torch.float32, device="cuda")
     nv.nvfp4_gemm(M, N, K, a["codes"], a["scales"], a["ts"], b["codes"], b["scales"], b_rowdiv,
-                  b["ts"], c, N, beta)
+                  b["ts"], c, N, beta, workspace=ws)
     torch.cuda.synchronize()
     return host(c)
 

@@ -77,6 +77,56 @@ def test_gemm_zero_operand(ora):
     assert not c.any()
 
 
+def _operands(ora, M, N, K, seed):
+    a = synth.f32_to_bf16_bits(synth.student_t(seed, (M, K)))
+    b = synth.f32_to_bf16_bits(synth.normal(seed + 1, (N, K)))
+    ga, gb = gpuio.gpu_quantize(a, nv.NVFP4_ROW_1D), gpuio.gpu_quantize(b, nv.NVFP4_ROW_1D)
+    oa, ob = ora.quantize(a, ora.ROW_1D), ora.quantize(b, ora.ROW_1D)
+    assert np.array_equal(ga["codes"], oa["codes"]) and np.array_equal(gb["codes"], ob["codes"])
+    return ga, gb, ora.gemm_f64(_deq(ora, oa), _deq(ora, ob))
+
+
+@pytest.mark.parametrize("M,N,K", [
+    (512, 512, 4096),     # 4 tiles, all split (16 K stages)
+    (272, 784, 2048),     # ragged 2 x 4 tiles, 8 stages per tile
+    (4336, 4096, 4096),   # 17 x 16 = 272 tiles: one full round + a split tail
+])
+def test_gemm_split_tail(ora, M, N, K):
+    """The split tail path (partial tiles in the workspace, ordered reduction)
+    against the oracle, against the unsplit path, and run to run bit-identical."""
+    ws = nv.nvfp4_gemm_workspace_size(M, N, K)
+    assert ws > 0, "shape chosen to exercise the split"
+    ga, gb, ref = _operands(ora, M, N, K, 111 + M)
+    c1 = gpuio.gpu_gemm(M, N, K, ga["dev"], gb["dev"], 1)
+    c2 = gpuio.gpu_gemm(M, N, K, ga["dev"], gb["dev"], 1)
+    c0 = gpuio.gpu_gemm(M, N, K, ga["dev"], gb["dev"], 1, workspace=None)
+    small = gpuio.gpu_gemm(M, N, K, ga["dev"], gb["dev"], 1, workspace=ws - 16)
+    assert np.isfinite(c1).all()
+    assert c1.tobytes() == c2.tobytes(), "split result not deterministic"
+    assert c0.tobytes() == small.tobytes(), "too small a workspace must fall back to the unsplit path"
+    for c in (c1, c0):
+        assert gpuio.rel_fro(c, ref) <= TOL, gpuio.rel_fro(c, ref)
+
+
+def test_gemm_split_tail_accumulates(ora):
+    M, N, K = 512, 272, 4096
+    ga, gb, ref = _operands(ora, M, N, K, 121)
+    c0 = synth.normal(123, (M, N))
+    assert nv.nvfp4_gemm_workspace_size(M, N, K) > 0
+    c = gpuio.gpu_gemm(M, N, K, ga["dev"], gb["dev"], 1, c0=c0, beta=1.0)
+    assert gpuio.rel_fro(c, ref + c0) <= TOL
+
+
+def test_gemm_workspace_size_bounds():
+    torch = gpuio.torch_cuda()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    for M, N, K in [(256, 256, 64), (8192, 20480, 5120), (8192, 5120, 20480), (20480, 5120, 8192),
+                    (4096, 4096, 65536)]:
+        ws = nv.nvfp4_gemm_workspace_size(M, N, K)
+        assert 0 <= ws <= cus * 256 * 256 * 4
+    assert nv.nvfp4_gemm_workspace_size(256, 256, 64) == 0  # a single short tile is not split
+
+
 def test_linear_step_fprop_dgrad_wgrad(ora):
     """The whole recipe on a small layer with ragged tiles: T=384, IN=320,
     OUT=576; every quantized operand bit-exact, every GEMM within 1e-5."""

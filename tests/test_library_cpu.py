@@ -105,9 +105,20 @@ def g(**kw):
     (dict(a_codes=FAKE + 4), b.NVFP4_EALIGN),
     (dict(c=FAKE + 4), b.NVFP4_EALIGN),
     (dict(ldc=258), b.NVFP4_EALIGN),
+    (dict(workspace=FAKE + 4, workspace_bytes=1 << 20), b.NVFP4_EALIGN),
+    (dict(workspace=FAKE, workspace_bytes=-1), b.NVFP4_ESHAPE),
 ])
 def test_gemm_argument_errors(kw, status):
     assert g(**kw) == status
+
+
+@pytest.mark.parametrize("M,N,K", [(250, 256, 256), (256, 8, 256), (256, 256, 96), (0, 256, 256)])
+def test_gemm_workspace_size_shape_errors(M, N, K):
+    import ctypes
+    out = ctypes.c_int64(-7)
+    assert b.load_library().nvfp4_gemm_workspace_size(M, N, K, ctypes.byref(out)) == b.NVFP4_ESHAPE
+    assert out.value == -7  # untouched on error
+    assert b.load_library().nvfp4_gemm_workspace_size(256, 256, 256, None) == b.NVFP4_EINVAL
 
 
 def test_errors_raise_in_checked_mode():
