@@ -257,9 +257,11 @@ __global__ __launch_bounds__(512, 1) void k_gemm_nvfp4(
   __syncthreads();
   read_quad(lds, 0, qa[0], qb[0], qsa[0], qsb[0]);
 
-  for (int kt = kt0; kt < kt1; kt++) {
-    uint8_t* cur = lds + ((kt - kt0) & 1) * STAGE_BYTES;
-    uint8_t* nxt = lds + ((kt - kt0 + 1) & 1) * STAGE_BYTES;
+  // One stage.  cur and nxt are the two (disjoint) stage buffers; declaring
+  // them restrict lets the compiler see that the fragment reads of cur do not
+  // depend on the direct-to-LDS prefetch into nxt, so it does not wait for
+  // that prefetch before the reads.
+  auto stage = [&](int kt, const uint8_t* __restrict__ cur, uint8_t* __restrict__ nxt) {
     const bool more = kt + 1 < kt1;
     if (more) issue_stage(kt + 1, nxt);
     // quads 0..2: read the following quad of this stage while computing
@@ -284,6 +286,11 @@ __global__ __launch_bounds__(512, 1) void k_gemm_nvfp4(
     }
     quad(1);
     __syncthreads();
+  };
+  for (int kt = kt0; kt < kt1; kt++) {
+    uint8_t* cur = lds + ((kt - kt0) & 1) * STAGE_BYTES;
+    uint8_t* nxt = lds + ((kt - kt0 + 1) & 1) * STAGE_BYTES;
+    stage(kt, cur, nxt);
   }
 
   if (part != nullptr) {

@@ -93,29 +93,28 @@ __host__ __device__ __forceinline__ uint32_t pcg_host(uint32_t v) {
   return (word >> 22u) ^ word;
 }
 
-// Stochastic rounding of a scaled value v to a 4-bit E2M1 code with 16
-// random bits r16: with a = min(|v|, 6), lo the largest E2M1 magnitude <= a
-// and hi the next one, round up iff r16 < (a - lo) / (hi - lo) * 65536.
-//   a >= 1  : lo is a with the FP32 mantissa cut to one bit, and the fraction
-//             times 2^22 is the 22 mantissa bits below it;
-//   a < 1   : step 0.5; for a >= 0.5 the fraction times 2^23 is the mantissa,
-//             below 0.5 the fraction is 2a (compared in FP32, exactly).
+// Stochastic rounding of a scaled value v to a 4-bit E2M1 code: with
+// a = min(|v|, 6), lo the largest E2M1 magnitude <= a and hi the next one,
+// round up iff r16 < (a - lo) / (hi - lo) * 65536.  Takes rc = 65535 - r16.
+//   a >= 1: the grid index is (bits(a) >> 22) - 252 and the fraction times
+//           2^22 is m22, the 22 mantissa bits below the grid bit.  r16 * 64 <
+//           m22 exactly when m22 + rc * 64 + 63 carries out of those 22 bits,
+//           so adding rc * 64 + 63 to bits(a) rounds up or down by itself.
+//   a < 1 : step 0.5; with T = ceil(a * 2^17) (exact), r16 < frac * 65536 is
+//           r16 < T for a < 0.5 and r16 < T - 65536 for a >= 0.5, so the index
+//           is (T + rc) >> 16 (0, 1 or 2).
+// Both forms are computed and one is selected, without branches.
+__device__ __forceinline__ uint32_t sr_code_c(float v, uint32_t rc) {
+  const float a = fminf(fabsf(v), 6.0f);  // v is finite
+  const uint32_t b = __float_as_uint(a);
+  const uint32_t i_hi = (b + (rc << 6) + (63u - (252u << 22))) >> 22;
+  const uint32_t i_lo = ((uint32_t)__builtin_ceilf(a * 131072.0f) + rc) >> 16;
+  const uint32_t idx = __builtin_unpredictable(b >= 0x3F800000u) ? i_hi : i_lo;
+  return ((__float_as_uint(v) >> 28) & 8u) | idx;
+}
+
 __device__ __forceinline__ uint32_t sr_code(float v, uint32_t r16) {
-  uint32_t bits = __float_as_uint(v);
-  uint32_t sign = (bits >> 28) & 8u;
-  uint32_t b = bits & 0x7FFFFFFFu;
-  uint32_t idx;
-  if (b >= 0x40C00000u) {  // |v| >= 6 (or inf): saturate
-    idx = 7u;
-  } else if (b >= 0x3F800000u) {  // [1, 6)
-    uint32_t k = (b >> 22) - 252u;
-    idx = k + ((r16 << 6) < (b & 0x3FFFFFu) ? 1u : 0u);
-  } else if (b >= 0x3F000000u) {  // [0.5, 1)
-    idx = 1u + ((r16 << 7) < (b & 0x7FFFFFu) ? 1u : 0u);
-  } else {  // [0, 0.5)
-    idx = ((float)r16 < __uint_as_float(b) * 131072.0f) ? 1u : 0u;
-  }
-  return sign | idx;
+  return sr_code_c(v, r16 ^ 0xFFFFu);
 }
 
 // Random bits of the SR hash: key = pcg(lo32(seed) ^ pcg(hi32(seed))); one

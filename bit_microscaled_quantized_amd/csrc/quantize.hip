@@ -121,9 +121,9 @@ __device__ __forceinline__ uint32_t encode8(const float* v, uint32_t key, uint32
     uint32_t w = 0u;
 #pragma unroll
     for (int p = 0; p < 4; p++) {
-      uint32_t h = pcg(key ^ (pair0 + p));
-      uint32_t c0 = sr_code(v[2 * p], h & 0xFFFFu);
-      uint32_t c1 = sr_code(v[2 * p + 1], h >> 16);
+      const uint32_t nh = ~pcg(key ^ (pair0 + p));  // 65535 - r16 in each half
+      uint32_t c0 = sr_code_c(v[2 * p], nh & 0xFFFFu);
+      uint32_t c1 = sr_code_c(v[2 * p + 1], nh >> 16);
       w |= (c0 | (c1 << 4)) << (8 * p);
     }
     return w;
