@@ -40,10 +40,15 @@ MFMA_FP4_PEAK = 10100.0        # dense FP4 MFMA, TFLOP/s (context)
 
 TOKENS, D_IN, D_OUT = 8192, 5120, 20480
 
-# HBM traffic of one GEMM launch from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE,
-# each scaled by the same counter's reading for a plain copy kernel of known
-# size; valid only for the kernel source it was measured on.
-GEMM_TRAFFIC = None  # dict(src_sha256=..., bytes_per_launch=...) once measured
+# HBM bytes per k_gemm_nvfp4 launch (mean over the Fprop, Dgrad and Wgrad
+# launches of this workload) from two rocprofv3 --pmc runs of
+#   bench.py --steps 3 --warmup 1 --no-cpu-baseline --copy-probe-mib 1024
+# FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0 (KiB -> bytes): the factors are what the
+# same counters read for the 1 GiB read + 1 GiB write elementwise probe
+# (FETCH_SIZE 512 MiB, WRITE_SIZE 1024 MiB).  Valid only for the gemm.hip
+# source with this hash; any other source reports null.
+GEMM_TRAFFIC = dict(src_sha256="f7cdfac03b59402b6a492bd5c5780e714ceb0b07ac150cf74eaedf62f83fad16",
+                    bytes_per_launch=1.1573e+09, fetch_bytes=7.0980e+08, write_bytes=4.4755e+08)
 
 
 def _src_sha(path: str) -> str:
@@ -55,7 +60,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--cpu-sample-tokens", type=int, default=1024)
+    p.add_argument("--cpu-sample-tokens", type=int, default=8192)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-probe-mib", type=int, default=0,
                    help="also run one plain device copy of this many MiB (calibrates "
@@ -204,11 +209,13 @@ def main():
     ms_step, per = gpu_bench(inp, args.steps, args.warmup)
     if args.copy_probe_mib:
         import torch
+        # an elementwise kernel (not a DMA copy, which no counter sees) that
+        # reads and writes exactly n bytes
         n = args.copy_probe_mib << 20
-        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
-        dst.copy_(src)
+        torch.neg(src, out=dst)
         torch.cuda.synchronize()
         del src, dst
     ms_step *= 1e3

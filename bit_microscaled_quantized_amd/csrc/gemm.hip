@@ -40,7 +40,9 @@
 // clamped in-row addresses; past K the scales are zeroed (exact 0
 // contribution), past M/N the outputs are never stored.  Workgroups are
 // remapped so that each XCD's share of the grid is a contiguous, grouped range
-// of output tiles (shared L2).
+// of output tiles (shared L2).  The FP32 output is written with non-temporal
+// stores: it is not read again by the next kernels of the step, and leaving it
+// dirty in the 256 MB Infinity Cache would make them pay for its write-back.
 //
 // Grid tail: with one 256 x 256 tile per CU, a tile count that is not a
 // multiple of the CU count leaves the last round partly idle (8192 x 5120
@@ -320,7 +322,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_nvfp4(
           float* p = c + (int64_t)m * ldc + n;
           float v = alpha * acc[i][j][r];
           if (accumulate) v += *p;
-          *p = v;
+          __builtin_nontemporal_store(v, p);
         }
       }
     }
@@ -355,7 +357,10 @@ __global__ __launch_bounds__(256) void k_gemm_split_reduce(int M, int N, int ful
     const float4 old = *dst;
     o.x += old.x; o.y += old.y; o.z += old.z; o.w += old.w;
   }
-  *dst = o;
+  __builtin_nontemporal_store(o.x, &dst->x);
+  __builtin_nontemporal_store(o.y, &dst->y);
+  __builtin_nontemporal_store(o.z, &dst->z);
+  __builtin_nontemporal_store(o.w, &dst->w);
 }
 
 namespace {
