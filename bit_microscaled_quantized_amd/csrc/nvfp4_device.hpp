@@ -29,15 +29,14 @@ __device__ __forceinline__ float encode_scale(float amax_t) {
 // E4M3 code of sb >= 0: nearest finite value, ties to the even code,
 // saturating at 448 (0x7E).  Subnormal codes k * 2^-9 (k <= 8, code 8 being
 // the smallest normal 2^-6) come from rounding sb * 2^9 to an integer; normal
-// codes from rounding the FP32 mantissa to 3 bits.
+// codes from rounding the FP32 mantissa to 3 bits.  Both are computed and one
+// is selected (no branches).
 __device__ __forceinline__ uint32_t e4m3_encode(float sb) {
-  if (!(sb > 0.0f)) return 0u;
-  if (sb >= 448.0f) return 0x7Eu;
-  if (sb < 0.015625f) return (uint32_t)__builtin_rintf(sb * 512.0f);
-  uint32_t b = __float_as_uint(sb);
-  uint32_t r = b + 0x7FFFFu + ((b >> 20) & 1u);
-  uint32_t code = (r >> 20) - (120u << 3);
-  return code < 0x7Eu ? code : 0x7Eu;
+  const uint32_t b = __float_as_uint(sb);
+  const uint32_t r = b + 0x7FFFFu + ((b >> 20) & 1u);
+  const uint32_t normal = min((r >> 20) - (120u << 3), 0x7Eu);
+  const uint32_t sub = (uint32_t)__builtin_rintf(sb * 512.0f);
+  return __builtin_unpredictable(sb < 0.015625f) ? sub : normal;
 }
 
 // Value of a finite non-negative E4M3 code.
@@ -53,12 +52,31 @@ __device__ __forceinline__ float element_scale(uint32_t e_b, float s_enc) {
   return fminf(s_enc / e4m3_decode(e_b), kFltMax);
 }
 
+// x / 6, correctly rounded.  For x >= 2^-100 the product with RN(1/6) plus one
+// FMA correction of the exact residual is correctly rounded (checked against
+// the IEEE division on every such FP32 value); below, where the quotient can
+// be subnormal and that shortcut is not, the division itself runs.
+__device__ __forceinline__ float div6(float x) {
+  if (__builtin_expect(x < 0x1p-100f, 0)) return x / 6.0f;
+  const float c = 0x1.555556p-3f;  // RN(1/6)
+  const float q0 = x * c;
+  return __builtin_fmaf(__builtin_fmaf(-q0, 6.0f, x), c, q0);
+}
+
+// Per-workgroup table of element_scale(e, s_enc) for every code e < 128, so a
+// block needs one LDS read instead of a division.  Threads 0..127 fill it;
+// the caller synchronizes before the first lookup.
+__device__ __forceinline__ void fill_scale_table(float* tab, float s_enc) {
+  if (threadIdx.x < 128) tab[threadIdx.x] = element_scale(threadIdx.x, s_enc);
+}
+
 // Block scale code and element multiplier from a block amax.
-__device__ __forceinline__ void block_scale(float amax_b, float s_enc, uint32_t& e_b, float& r_b) {
-  float t = amax_b / 6.0f;
-  float sb = t * s_enc;
+__device__ __forceinline__ void block_scale(float amax_b, float s_enc, const float* tab, uint32_t& e_b,
+                                            float& r_b) {
+  const float t = div6(amax_b);
+  const float sb = t * s_enc;
   e_b = e4m3_encode(sb);
-  r_b = element_scale(e_b, s_enc);
+  r_b = tab[e_b];
 }
 
 // Two values to two E2M1 codes, round-to-nearest-even with saturation, placed
@@ -81,10 +99,22 @@ __device__ __forceinline__ uint32_t pack8_rne(const float* v) {
 }
 
 // pcg hash (Jarzynski & Olano, "Hash Functions for GPU Rendering", JCGT 2020).
-__device__ __forceinline__ uint32_t pcg(uint32_t v) {
-  uint32_t state = v * 747796405u + 2891336453u;
-  uint32_t word = ((state >> ((state >> 28u) + 4u)) ^ state) * 277803737u;
+__device__ __forceinline__ uint32_t pcg_tail(uint32_t state) {
+  const uint32_t word = ((state >> ((state >> 28u) + 4u)) ^ state) * 277803737u;
   return (word >> 22u) ^ word;
+}
+
+// pcg(key ^ (pair0 + p)) for p = 0..7, pair0 a multiple of 8.  The xor then
+// only touches the low three bits, so the pcg input is
+// ((key ^ pair0) & ~7) + ((key & 7) ^ p) and its state
+// ((key ^ pair0) & ~7) * C1 + (((key & 7) ^ p) * C1 + C2): one multiply for
+// the eight pairs, the second term being uniform across the wave.
+__device__ __forceinline__ void pcg8(uint32_t key, uint32_t pair0, uint32_t* h) {
+  uint32_t base = ((key ^ pair0) & ~7u) * 747796405u;
+  asm volatile("" : "+v"(base));  // keep the shared product: one multiply, eight adds
+#pragma unroll
+  for (int p = 0; p < 8; p++)
+    h[p] = pcg_tail(base + ((((key & 7u) ^ (uint32_t)p) * 747796405u) + 2891336453u));
 }
 
 __host__ __device__ __forceinline__ uint32_t pcg_host(uint32_t v) {

@@ -9,9 +9,11 @@
 // scaling) and 4 (stochastic rounding for gradients only).
 //
 // Every pass is bound by HBM bandwidth: loads are 16 bytes per lane and
-// contiguous across a wave, block maxima are reduced in registers (1D row:
-// with the partner lane through DPP), and the column and tile casts stage
-// their outputs through LDS so the transposed stores stay contiguous.
+// contiguous across a wave, block maxima are reduced in registers, and the
+// column and tile casts stage their outputs through LDS so the transposed
+// stores stay contiguous.  Each workgroup first tabulates S_enc / dec(e) for
+// the 127 finite E4M3 codes in LDS, so a block scale costs one division by 6
+// (a multiply and two FMAs) and one table read.
 #include "nvfp4_device.hpp"
 #include "nvfp4_launch.hpp"
 
@@ -111,34 +113,32 @@ __device__ __forceinline__ void load8<float>(const float* p, float* v) {
   v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
 }
 
-// Encode 8 scaled values: RNE through the hardware conversion, SR in
-// software with pcg bits for output elements idx0 .. idx0 + 7 (idx0 even).
+// Encode 16 scaled values (one block): RNE through the hardware conversion,
+// SR in software with pcg bits of output elements 2 pair0 .. 2 pair0 + 15
+// (pair0 a multiple of 8).  Element 0 lands in the low nibble of x.
 template <int RND>
-__device__ __forceinline__ uint32_t encode8(const float* v, uint32_t key, uint32_t pair0) {
+__device__ __forceinline__ uint2 encode16(const float* v, uint32_t key, uint32_t pair0) {
   if constexpr (RND == 0) {
-    return pack8_rne(v);
+    return make_uint2(pack8_rne(v), pack8_rne(v + 8));
   } else {
-    uint32_t w = 0u;
+    uint32_t h[8];
+    pcg8(key, pair0, h);
+    uint32_t w[2] = {0u, 0u};
 #pragma unroll
-    for (int p = 0; p < 4; p++) {
-      const uint32_t nh = ~pcg(key ^ (pair0 + p));  // 65535 - r16 in each half
-      uint32_t c0 = sr_code_c(v[2 * p], nh & 0xFFFFu);
-      uint32_t c1 = sr_code_c(v[2 * p + 1], nh >> 16);
-      w |= (c0 | (c1 << 4)) << (8 * p);
+    for (int p = 0; p < 8; p++) {
+      const uint32_t nh = ~h[p];  // 65535 - r16 in each half
+      const uint32_t c0 = sr_code_c(v[2 * p], nh & 0xFFFFu);
+      const uint32_t c1 = sr_code_c(v[2 * p + 1], nh >> 16);
+      w[p >> 2] |= (c0 | (c1 << 4)) << (8 * (p & 3));
     }
-    return w;
+    return make_uint2(w[0], w[1]);
   }
 }
 
-__device__ __forceinline__ float dpp_swap_pair(float x) {
-  // quad_perm [1,0,3,2]: exchange with the neighbouring lane
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));
-}
-
 // ---------------------------------------------------------------------------
-// 1D row cast: blocks of 16 along a row.  Lane pairs hold one block (8
-// elements each); UNROLL half-blocks per lane per round, contiguous across the
-// workgroup.  codes [rows][cols/2], scales [rows][cols/16].
+// 1D row cast: blocks of 16 along a row; each lane owns whole blocks (two
+// 16-byte loads for bf16), UNROLL blocks per lane per round, contiguous
+// across the workgroup.  codes [rows][cols/2], scales [rows][cols/16].
 // ---------------------------------------------------------------------------
 template <typename T, int RND, int UNROLL>
 __global__ __launch_bounds__(256) void k_cast_row1d(const T* __restrict__ x, int64_t rows,
@@ -147,44 +147,46 @@ __global__ __launch_bounds__(256) void k_cast_row1d(const T* __restrict__ x, int
                                                     uint8_t* __restrict__ codes,
                                                     uint8_t* __restrict__ scales,
                                                     float* __restrict__ tensor_scale, uint32_t key) {
+  __shared__ float rtab[128];
   const float s_enc = encode_scale(amax[0]);
   if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) tensor_scale[0] = 1.0f / s_enc;
-  const int64_t items = cols / 8;  // half-blocks per row
+  fill_scale_table(rtab, s_enc);
+  __syncthreads();
+  const int64_t items = cols / 16;  // blocks per row
   for (int64_t r = blockIdx.y; r < rows; r += gridDim.y) {
     const T* row = x + r * ld;
-    uint32_t* crow = reinterpret_cast<uint32_t*>(codes + r * (cols / 2));
+    uint2* crow = reinterpret_cast<uint2*>(codes + r * (cols / 2));
     uint8_t* srow = scales + r * (cols / 16);
     const uint32_t row_index = (uint32_t)(r * cols);
     for (int64_t base = (int64_t)blockIdx.x * 256 * UNROLL; base < items;
          base += (int64_t)gridDim.x * 256 * UNROLL) {
-      float v[UNROLL][8];
+      float v[UNROLL][16];
 #pragma unroll
       for (int j = 0; j < UNROLL; j++) {
-        int64_t it = base + j * 256 + threadIdx.x;
+        const int64_t it = base + j * 256 + threadIdx.x;
         if (it < items) {
-          load8<T>(row + it * 8, v[j]);
+          load8<T>(row + it * 16, v[j]);
+          load8<T>(row + it * 16 + 8, v[j] + 8);
         } else {
 #pragma unroll
-          for (int e = 0; e < 8; e++) v[j][e] = 0.0f;
+          for (int e = 0; e < 16; e++) v[j][e] = 0.0f;
         }
       }
 #pragma unroll
       for (int j = 0; j < UNROLL; j++) {
-        int64_t it = base + j * 256 + threadIdx.x;
+        const int64_t it = base + j * 256 + threadIdx.x;
         float am = 0.0f;
 #pragma unroll
-        for (int e = 0; e < 8; e++) am = fmaxf(am, fabsf(v[j][e]));
-        am = fmaxf(am, dpp_swap_pair(am));
+        for (int e = 0; e < 16; e++) am = fmaxf(am, fabsf(v[j][e]));
         uint32_t e_b;
         float r_b;
-        block_scale(am, s_enc, e_b, r_b);
-        float s[8];
+        block_scale(am, s_enc, rtab, e_b, r_b);
+        float sv[16];
 #pragma unroll
-        for (int e = 0; e < 8; e++) s[e] = v[j][e] * r_b;
+        for (int e = 0; e < 16; e++) sv[e] = v[j][e] * r_b;
         if (it < items) {
-          uint32_t pair0 = (row_index + (uint32_t)(it * 8)) >> 1;
-          crow[it] = encode8<RND>(s, key, pair0);
-          if ((threadIdx.x & 1) == 0) srow[it >> 1] = (uint8_t)e_b;
+          crow[it] = encode16<RND>(sv, key, (row_index + (uint32_t)(it * 16)) >> 1);
+          srow[it] = (uint8_t)e_b;
         }
       }
     }
@@ -217,8 +219,11 @@ __global__ __launch_bounds__(256) void k_cast_col1d(const T* __restrict__ x, int
                                                     float* __restrict__ tensor_scale, uint32_t key) {
   __shared__ __align__(16) uint8_t lcodes[kColCols][kColTok / 2];
   __shared__ __align__(16) uint8_t lscales[kColCols][kColTok / 16];
+  __shared__ float rtab[128];
   const float s_enc = encode_scale(amax[0]);
   if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) tensor_scale[0] = 1.0f / s_enc;
+  fill_scale_table(rtab, s_enc);
+  __syncthreads();
 
   const int64_t t0 = (int64_t)blockIdx.y * kColTok;
   const int64_t c0 = (int64_t)blockIdx.x * kColCols;
@@ -248,13 +253,13 @@ __global__ __launch_bounds__(256) void k_cast_col1d(const T* __restrict__ x, int
 #pragma unroll
       for (int j = 0; j < 16; j++) am = fmaxf(am, fabsf(u[k][j]));
       float r_b;
-      block_scale(am, s_enc, e_b, r_b);
+      block_scale(am, s_enc, rtab, e_b, r_b);
       float s[16];
 #pragma unroll
       for (int j = 0; j < 16; j++) s[j] = u[k][j] * r_b;
-      uint32_t pair0 = (uint32_t)((cc + k) * rows + tg) >> 1;
-      w0 = encode8<RND>(s, key, pair0);
-      w1 = encode8<RND>(s + 8, key, pair0 + 4);
+      const uint2 w = encode16<RND>(s, key, (uint32_t)((cc + k) * rows + tg) >> 1);
+      w0 = w.x;
+      w1 = w.y;
     }
     *reinterpret_cast<uint2*>(&lcodes[8 * co + k][8 * g]) = make_uint2(w0, w1);
     lscales[8 * co + k][g] = (uint8_t)e_b;
@@ -350,8 +355,11 @@ __global__ __launch_bounds__(256) void k_cast_tile2d(const T* __restrict__ x, in
                                                      uint8_t* __restrict__ scales_t,
                                                      float* __restrict__ tensor_scale, uint32_t key) {
   __shared__ __align__(16) uint8_t lt[64][64 + 16];  // [local col][local row], padded
+  __shared__ float rtab[128];
   const float s_enc = encode_scale(amax[0]);
   if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) tensor_scale[0] = 1.0f / s_enc;
+  fill_scale_table(rtab, s_enc);
+  __syncthreads();
 
   const int64_t r0 = (int64_t)blockIdx.y * 64;
   const int64_t c0 = (int64_t)blockIdx.x * 64;
@@ -379,13 +387,12 @@ __global__ __launch_bounds__(256) void k_cast_tile2d(const T* __restrict__ x, in
   for (int off = 1; off < 16; off <<= 1) am = fmaxf(am, __shfl_xor(am, off));
   uint32_t e_b;
   float r_b;
-  block_scale(am, s_enc, e_b, r_b);
+  block_scale(am, s_enc, rtab, e_b, r_b);
   float s[16];
 #pragma unroll
   for (int e = 0; e < 16; e++) s[e] = v[e] * r_b;
-  const uint32_t pair0 = (uint32_t)(r * cols + c) >> 1;
-  uint32_t w0 = encode8<RND>(s, key, pair0);
-  uint32_t w1 = encode8<RND>(s + 8, key, pair0 + 4);
+  const uint2 w = encode16<RND>(s, key, (uint32_t)(r * cols + c) >> 1);
+  const uint32_t w0 = w.x, w1 = w.y;
   if (tile_valid) {
     *reinterpret_cast<uint2*>(codes + r * (cols / 2) + c / 2) = make_uint2(w0, w1);
     if (rr == 0) {
@@ -442,7 +449,11 @@ static hipError_t launch_amax(const void* x, int64_t rows, int64_t cols, int64_t
     rows = 1;
   }
   int64_t cpr = cols / EPC;
-  dim3 grid(grid_cap((cpr + 256 * UNROLL - 1) / (256 * UNROLL), 2048), grid_cap(rows, 65535));
+  // at most 2048 workgroups (each one reads the running maximum once), with
+  // the rounds balanced so that no workgroup idles in a partial last round
+  const int64_t units = (cpr + 256 * UNROLL - 1) / (256 * UNROLL);
+  const int64_t rounds = (units + 2047) / 2048;
+  dim3 grid(grid_cap((units + rounds - 1) / rounds, 2048), grid_cap(rows, 65535));
   k_amax<T, UNROLL><<<grid, 256, 0, s>>>(static_cast<const T*>(x), rows, cols, ld, amax);
   return hipGetLastError();
 }
@@ -457,15 +468,15 @@ hipError_t launch_quantize(const void* x, int dt, int64_t rows, int64_t cols, in
   if (e != hipSuccess) return e;
   const uint32_t key = sr_key(seed);
   if (layout == 0) {
-    constexpr int UNROLL = 4;
+    constexpr int UNROLL = 2;
     int64_t r = rows, c = cols, l = ld;
     if (ld == cols) {
       c = rows * cols;
       l = c;
       r = 1;
     }
-    int64_t items = c / 8;
-    dim3 grid(grid_cap((items + 256 * UNROLL - 1) / (256 * UNROLL), 8192), grid_cap(r, 65535));
+    int64_t items = c / 16;
+    dim3 grid(grid_cap((items + 256 * UNROLL - 1) / (256 * UNROLL), 1 << 20), grid_cap(r, 65535));
 #define ROW_LAUNCH(T, R)                                                                        \
   k_cast_row1d<T, R, UNROLL><<<grid, 256, 0, s>>>(static_cast<const T*>(x), r, c, l, amax, codes, \
                                                   scales, tensor_scale, key)
