@@ -1,0 +1,118 @@
+"""CPU pins of two exact shortcuts the HIP kernels take, each checked against
+the plain rule it replaces on every FP32 input in its range (the kernels' own
+formulas are restated here in C; the reference side is IEEE division and the
+oracle's stochastic-rounding rule).
+
+* Division by 6 of a block amax: RN(1/6) * x followed by one FMA correction of
+  the exact residual equals the correctly rounded x / 6 for every FP32
+  x >= 2^-100 (the kernels divide directly below that).
+* Stochastic rounding: with rc = 65535 - r16, the carry form
+  (bits(a) + 64 rc + 63 - 252 * 2^22) >> 22 for a >= 1 and
+  (ceil(a * 2^17) + rc) >> 16 for a < 1 gives the oracle's code for every FP32
+  v with |v| <= 6.5 (and a sweep beyond), at r16 values on both sides of each
+  input's rounding threshold and at a pseudo-random r16.
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+C_SRC = r"""
+#include <math.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+int ora_e2m1_sr(float v, uint32_t r16);
+static float f_of(uint32_t u) { float x; memcpy(&x, &u, 4); return x; }
+static uint32_t u_of(float x) { uint32_t v; memcpy(&v, &x, 4); return v; }
+
+static float div6_fast(float x) {
+  const float c = 0x1.555556p-3f;
+  float q0 = x * c;
+  return fmaf(fmaf(-q0, 6.0f, x), c, q0);
+}
+
+static uint32_t sr_kernel(float v, uint32_t r16) {
+  uint32_t rc = r16 ^ 0xFFFFu;
+  float a = fminf(fabsf(v), 6.0f);
+  uint32_t b = u_of(a);
+  uint32_t i_hi = (b + (rc << 6) + (63u - (252u << 22))) >> 22;
+  uint32_t i_lo = ((uint32_t)ceilf(a * 131072.0f) + rc) >> 16;
+  uint32_t idx = b >= 0x3F800000u ? i_hi : i_lo;
+  return ((u_of(v) >> 28) & 8u) | idx;
+}
+
+static const double MAG[8] = {0, 0.5, 1, 1.5, 2, 3, 4, 6};
+
+int main(int argc, char** argv) {
+  long bad_div = 0, bad_sr = 0;
+  if (argv[1][0] == 'd') {
+#pragma omp parallel for reduction(+:bad_div) schedule(static, 1 << 16)
+    for (int64_t i = (int64_t)u_of(0x1p-100f); i <= 0x7F7FFFFF; i++) {
+      float x = f_of((uint32_t)i);
+      if (u_of(div6_fast(x)) != u_of(x / 6.0f)) bad_div++;
+    }
+    printf("%ld\n", bad_div);
+    return 0;
+  }
+  const uint32_t top = u_of(6.5f);
+#pragma omp parallel for reduction(+:bad_sr) schedule(static, 1 << 16)
+  for (int64_t i = 0; i <= (int64_t)top; i++) {
+    float v = f_of((uint32_t)i);
+    double a = fmin(fabs((double)v), 6.0);
+    int k = 0;
+    for (int j = 0; j < 8; j++) if (MAG[j] <= a) k = j;
+    uint32_t rs[4];
+    int n = 0;
+    if (k < 7) {
+      double thr = ceil((a - MAG[k]) / (MAG[k + 1] - MAG[k]) * 65536.0);  /* up iff r16 < thr */
+      if (thr >= 1.0) rs[n++] = (uint32_t)thr - 1u;
+      if (thr <= 65535.0) rs[n++] = (uint32_t)thr;
+    }
+    uint32_t h = (uint32_t)i * 2654435761u;
+    rs[n++] = (h ^ (h >> 15)) & 0xFFFFu;
+    for (int t = 0; t < n; t++) {
+      if (sr_kernel(v, rs[t]) != (uint32_t)ora_e2m1_sr(v, rs[t])) bad_sr++;
+      if (sr_kernel(-v, rs[t]) != (uint32_t)ora_e2m1_sr(-v, rs[t])) bad_sr++;
+    }
+  }
+  /* beyond the clamp: every 4099th pattern up to FLT_MAX */
+  for (int64_t i = top; i <= 0x7F7FFFFF; i += 4099) {
+    float v = f_of((uint32_t)i);
+    for (uint32_t r = 0; r < 65536; r += 4097)
+      if (sr_kernel(v, r) != (uint32_t)ora_e2m1_sr(v, r)) bad_sr++;
+  }
+  printf("%ld\n", bad_sr);
+  return 0;
+}
+"""
+
+
+@pytest.fixture(scope="module")
+def prog(tmp_path_factory):
+    d = tmp_path_factory.mktemp("arith")
+    src = d / "arith.c"
+    src.write_text(C_SRC)
+    exe = d / "arith"
+    cmd = ["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-o", str(exe), str(src),
+           os.path.join(ROOT, "oracle", "nvfp4_oracle.c"), "-lm"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    return str(exe)
+
+
+def _run(prog, mode):
+    r = subprocess.run([prog, mode], capture_output=True, text=True, timeout=600)
+    assert r.returncode == 0, r.stderr
+    return int(r.stdout.strip())
+
+
+def test_division_by_six_shortcut_is_correctly_rounded(prog):
+    assert _run(prog, "div") == 0
+
+
+def test_carry_form_of_stochastic_rounding_matches_the_oracle(prog):
+    assert _run(prog, "sr") == 0
