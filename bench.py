@@ -4,18 +4,19 @@ one MI355X.
 
 A step is the whole hot path over one batch of the FFN up-projection layer
 (X bf16 8192x5120, W bf16 20480x5120 ~N(0, 0.02^2), dY bf16 8192x20480
-~N(0, 1e-3^2)): W 16x16 2D quantize (RNE, with the transposed copy), X row-1D
-RNE, Fprop GEMM, dY row-1D SR, Dgrad GEMM with the same quantized W, random
-Hadamard + column-1D quantize of dY (SR) and X (RNE), Wgrad GEMM.  Inputs are
-resident in HBM before the timed region.
+~N(0, 1e-3^2)): W 16x16 2D quantize (RNE, with the transposed copy); X row-1D
+RNE together with its random Hadamard + column-1D quantization (RNE, the Wgrad
+operand) in one call; Fprop GEMM; dY row-1D SR together with its random
+Hadamard + column-1D SR quantization in one call; Dgrad GEMM with the same
+quantized W; Wgrad GEMM.  Inputs are resident in HBM before the timed region.
 
 Output: one JSON line.  `value` is the step's GEMM work (3 x 2MNK flops)
 divided by the whole step's wall time, so quantization time counts against
 it; the per-component figures (quantize GB/s, GEMM TFLOP/s and their
 fractions of the MI355X peaks) sit beside it.  `roofline` describes the
 dominant kernel (the GEMM) from HIP events around every GEMM launch in the
-timed steps.  `cpu_baseline` times the CPU oracle on a bounded sample of the
-same step (1024 tokens, full weights).
+timed steps.  `cpu_baseline` times the CPU oracle on the same step (all 8192
+tokens by default; --cpu-sample-tokens bounds it).
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
 """
@@ -77,16 +78,15 @@ def make_inputs():
 
 
 def quantize_bytes():
-    """Algorithmic bytes of the five quantize calls of a step: input read once,
+    """Algorithmic bytes of the three quantize calls of a step: input read once,
     codes (0.5 B/elem) and scales (1/16 B/elem, 1/256 B/elem for 2D tiles)
-    written; the 2D call also writes its transposed copy."""
+    written; the 2D call also writes its transposed copy, the row + RHT calls
+    write both a row-1D and an RHT column quantization."""
     T, I, O = TOKENS, D_IN, D_OUT
     w = O * I * 2 + 2 * (O * I // 2 + O * I // 256)
-    x_row = T * I * 2 + T * I // 2 + T * I // 16
-    dy_row = T * O * 2 + T * O // 2 + T * O // 16
-    dy_rht = dy_row
-    x_rht = x_row
-    return dict(w=w, x_row=x_row, dy_row=dy_row, dy_rht=dy_rht, x_rht=x_rht)
+    x = T * I * 2 + 2 * (T * I // 2 + T * I // 16)
+    dy = T * O * 2 + 2 * (T * O // 2 + T * O // 16)
+    return dict(w=w, x=x, dy=dy)
 
 
 def gpu_bench(inp, steps, warmup):
@@ -125,23 +125,18 @@ def gpu_bench(inp, steps, warmup):
         timed("quant_w_2d", lambda: nv.nvfp4_quantize(
             w, bf, O, I, I, nv.NVFP4_TILE_2D, nv.NVFP4_RNE, 0, q.codes, q.scales, q.codes_t,
             q.scales_t, q.ts, q.amax))
-        qx = st.qx
-        timed("quant_x_row", lambda: nv.nvfp4_quantize(
-            x, bf, T, I, I, nv.NVFP4_ROW_1D, nv.NVFP4_RNE, 0, qx.codes, qx.scales, None, None,
-            qx.ts, qx.amax))
+        qx, b_ = st.qx, st.qx_t
+        timed("quant_x_row_rht", lambda: nv.nvfp4_quantize_row_rht(
+            x, bf, T, I, I, nv.NVFP4_RNE, 0, qx.codes, qx.scales, qx.ts, qx.amax, mask,
+            nv.NVFP4_RNE, 0, b_.codes, b_.scales, b_.ts, b_.amax))
         timed("gemm_fprop", lambda: nv.nvfp4_gemm(
             T, O, I, qx.codes, qx.scales, qx.ts, q.codes, q.scales, 16, q.ts, st.y, O, 0.0, workspace=st.ws))
-        qd = st.qdy
-        timed("quant_dy_row_sr", lambda: nv.nvfp4_quantize(
-            dy, bf, T, O, O, nv.NVFP4_ROW_1D, nv.NVFP4_SR, s_row, qd.codes, qd.scales, None, None,
-            qd.ts, qd.amax))
+        qd, a_ = st.qdy, st.qdy_t
+        timed("quant_dy_row_rht_sr", lambda: nv.nvfp4_quantize_row_rht(
+            dy, bf, T, O, O, nv.NVFP4_SR, s_row, qd.codes, qd.scales, qd.ts, qd.amax, mask,
+            nv.NVFP4_SR, s_col, a_.codes, a_.scales, a_.ts, a_.amax))
         timed("gemm_dgrad", lambda: nv.nvfp4_gemm(
             T, I, O, qd.codes, qd.scales, qd.ts, q.codes_t, q.scales_t, 16, q.ts, st.dx, I, 0.0, workspace=st.ws))
-        a_, b_ = st.qdy_t, st.qx_t
-        timed("quant_dy_rht_sr", lambda: nv.nvfp4_rht_quantize(
-            dy, bf, T, O, O, mask, nv.NVFP4_SR, s_col, a_.codes, a_.scales, a_.ts, a_.amax))
-        timed("quant_x_rht", lambda: nv.nvfp4_rht_quantize(
-            x, bf, T, I, I, mask, nv.NVFP4_RNE, 0, b_.codes, b_.scales, b_.ts, b_.amax))
         timed("gemm_wgrad", lambda: nv.nvfp4_gemm(
             O, I, T, a_.codes, a_.scales, a_.ts, b_.codes, b_.scales, 1, b_.ts, st.dw, I, 0.0, workspace=st.ws))
 
@@ -224,8 +219,7 @@ def main():
     gemm_ms = np.mean([per["gemm_fprop"], per["gemm_dgrad"], per["gemm_wgrad"]])
     gemm_tflops = gemm_flops / (gemm_ms * 1e-3) / 1e12
     qb = quantize_bytes()
-    qnames = dict(w="quant_w_2d", x_row="quant_x_row", dy_row="quant_dy_row_sr",
-                  dy_rht="quant_dy_rht_sr", x_rht="quant_x_rht")
+    qnames = dict(w="quant_w_2d", x="quant_x_row_rht", dy="quant_dy_row_rht_sr")
     q_ms = sum(per[qnames[k]] for k in qb)
     q_gbs = sum(qb.values()) / (q_ms * 1e-3) / 1e9
     value = 3 * gemm_flops / (ms_step * 1e-3) / 1e12

@@ -69,6 +69,32 @@ nvfp4_status nvfp4_rht_quantize(const void* x, int dt, int64_t tokens, int64_t c
   return e == hipSuccess ? NVFP4_OK : NVFP4_EHIP;
 }
 
+nvfp4_status nvfp4_quantize_row_rht(const void* x, int dt, int64_t tokens, int64_t cols,
+                                    int64_t ld_x, int row_rnd, uint64_t row_seed,
+                                    uint8_t* row_codes, uint8_t* row_scales,
+                                    float* row_tensor_scale, float* row_amax, uint32_t sign_mask,
+                                    int rht_rnd, uint64_t rht_seed, uint8_t* rht_codes,
+                                    uint8_t* rht_scales, float* rht_tensor_scale, float* rht_amax,
+                                    void* stream) {
+  if (row_codes == nullptr || row_scales == nullptr || row_tensor_scale == nullptr ||
+      row_amax == nullptr || rht_codes == nullptr || rht_scales == nullptr ||
+      rht_tensor_scale == nullptr || rht_amax == nullptr)
+    return NVFP4_EINVAL;
+  if ((row_rnd != NVFP4_RNE && row_rnd != NVFP4_SR) || (rht_rnd != NVFP4_RNE && rht_rnd != NVFP4_SR))
+    return NVFP4_EINVAL;
+  nvfp4_status st = check_tensor(x, dt, tokens, cols, ld_x);
+  if (st != NVFP4_OK) return st;
+  if (!aligned16(row_codes) || !aligned16(row_scales) || !aligned16(rht_codes) ||
+      !aligned16(rht_scales) || !aligned4(row_tensor_scale) || !aligned4(row_amax) ||
+      !aligned4(rht_tensor_scale) || !aligned4(rht_amax))
+    return NVFP4_EALIGN;
+  hipError_t e = nvfp4::launch_quantize_row_rht(
+      x, dt, tokens, cols, ld_x, row_rnd, row_seed, row_codes, row_scales, row_tensor_scale,
+      row_amax, sign_mask, rht_rnd, rht_seed, rht_codes, rht_scales, rht_tensor_scale, rht_amax,
+      static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? NVFP4_OK : NVFP4_EHIP;
+}
+
 nvfp4_status nvfp4_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int64_t* bytes) {
   if (bytes == nullptr) return NVFP4_EINVAL;
   nvfp4_status st = check_gemm_shape(M, N, K);

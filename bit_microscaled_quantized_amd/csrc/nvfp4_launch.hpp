@@ -15,6 +15,13 @@ hipError_t launch_rht_quantize(const void* x, int dt, int64_t tokens, int64_t co
                                uint32_t sign_mask, int rnd, uint64_t seed, uint8_t* codes,
                                uint8_t* scales, float* tensor_scale, float* amax, hipStream_t s);
 
+hipError_t launch_quantize_row_rht(const void* x, int dt, int64_t tokens, int64_t cols, int64_t ld,
+                                   int row_rnd, uint64_t row_seed, uint8_t* row_codes,
+                                   uint8_t* row_scales, float* row_ts, float* row_amax,
+                                   uint32_t sign_mask, int rht_rnd, uint64_t rht_seed,
+                                   uint8_t* rht_codes, uint8_t* rht_scales, float* rht_ts,
+                                   float* rht_amax, hipStream_t s);
+
 hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
                        const uint8_t* a_scales, const float* a_ts, const uint8_t* b_codes,
                        const uint8_t* b_scales, int b_rowdiv, const float* b_ts, float* c,

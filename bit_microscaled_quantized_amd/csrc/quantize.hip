@@ -23,29 +23,45 @@ namespace nvfp4 {
 // Tensor amax
 // ---------------------------------------------------------------------------
 
-__global__ void k_zero_amax(float* amax) {
-  if (threadIdx.x == 0 && blockIdx.x == 0) amax[0] = 0.0f;
+__global__ void k_zero_amax(float* amax, float* amax2) {
+  if (threadIdx.x == 0 && blockIdx.x == 0) {
+    amax[0] = 0.0f;
+    if (amax2 != nullptr) amax2[0] = 0.0f;
+  }
 }
 
-// Per-block maximum of non-negative float bit patterns -> one atomicMax.
-__device__ __forceinline__ void block_atomic_max(uint32_t m, float* amax) {
-  __shared__ uint32_t red[8];
+// Most workgroups find a partial maximum below the running one: read it first
+// (device-coherent) and skip the atomic, so thousands of workgroups do not
+// serialize on one address.  The result is still the exact max.
+__device__ __forceinline__ void atomic_max_if_larger(uint32_t r, float* amax) {
+  unsigned int* a = reinterpret_cast<unsigned int*>(amax);
+  if (r > __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) atomicMax(a, r);
+}
+
+// Per-block maxima of non-negative float bit patterns (m1 only if amax1 is
+// not null) -> one atomicMax each.
+__device__ __forceinline__ void block_atomic_max(uint32_t m0, float* amax0, uint32_t m1 = 0u,
+                                                 float* amax1 = nullptr) {
+  __shared__ uint32_t red[2][8];
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
-    uint32_t o = __shfl_xor(m, off);
-    m = m > o ? m : o;
+    m0 = max(m0, (uint32_t)__shfl_xor(m0, off));
+    if (amax1 != nullptr) m1 = max(m1, (uint32_t)__shfl_xor(m1, off));
   }
-  int wave = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) red[wave] = m;
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    red[0][wave] = m0;
+    red[1][wave] = m1;
+  }
   __syncthreads();
   if (threadIdx.x == 0) {
-    uint32_t r = red[0];
-    for (int w = 1; w < (int)(blockDim.x >> 6); w++) r = r > red[w] ? r : red[w];
-    // Most workgroups find a partial maximum below the running one: read it
-    // first (device-coherent) and skip the atomic, so thousands of workgroups
-    // do not serialize on one address.  The result is still the exact max.
-    unsigned int* a = reinterpret_cast<unsigned int*>(amax);
-    if (r > __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) atomicMax(a, r);
+    uint32_t r0 = red[0][0], r1 = red[1][0];
+    for (int w = 1; w < (int)(blockDim.x >> 6); w++) {
+      r0 = max(r0, red[0][w]);
+      r1 = max(r1, red[1][w]);
+    }
+    atomic_max_if_larger(r0, amax0);
+    if (amax1 != nullptr) atomic_max_if_larger(r1, amax1);
   }
 }
 
@@ -304,18 +320,19 @@ __global__ __launch_bounds__(256) void k_cast_col1d(const T* __restrict__ x, int
   }
 }
 
-// amax of the RHT output: same thread mapping as the column cast, no LDS.
+// amax of the RHT output (and, if amax_plain is not null, of the input itself,
+// from the same read): same thread mapping as the column cast.
 template <typename T>
 __global__ __launch_bounds__(256) void k_rht_amax(const T* __restrict__ x, int64_t rows,
                                                   int64_t cols, int64_t ld, uint32_t sign_mask,
-                                                  float* amax) {
+                                                  float* amax, float* amax_plain) {
   const int64_t t0 = (int64_t)blockIdx.y * kColTok;
   const int64_t c0 = (int64_t)blockIdx.x * kColCols;
   const int co = threadIdx.x & 7;
   const int g = threadIdx.x >> 3;
   const int64_t tg = t0 + 16 * g;
   const int64_t cc = c0 + 8 * co;
-  float am = 0.0f;
+  float am = 0.0f, ap = 0.0f;
   if (tg < rows && cc < cols) {
     float u[8][16];
 #pragma unroll
@@ -327,12 +344,16 @@ __global__ __launch_bounds__(256) void k_rht_amax(const T* __restrict__ x, int64
     }
 #pragma unroll
     for (int k = 0; k < 8; k++) {
+      if (amax_plain != nullptr) {
+#pragma unroll
+        for (int j = 0; j < 16; j++) ap = fmaxf(ap, fabsf(u[k][j]));
+      }
       rht16(u[k], sign_mask);
 #pragma unroll
       for (int j = 0; j < 16; j++) am = fmaxf(am, fabsf(u[k][j]));
     }
   }
-  block_atomic_max(__float_as_uint(am), amax);
+  block_atomic_max(__float_as_uint(am), amax, __float_as_uint(ap), amax_plain);
 }
 
 // ---------------------------------------------------------------------------
@@ -458,14 +479,11 @@ static hipError_t launch_amax(const void* x, int64_t rows, int64_t cols, int64_t
   return hipGetLastError();
 }
 
-hipError_t launch_quantize(const void* x, int dt, int64_t rows, int64_t cols, int64_t ld,
-                           int layout, int rnd, uint64_t seed, uint8_t* codes, uint8_t* scales,
-                           uint8_t* codes_t, uint8_t* scales_t, float* tensor_scale, float* amax,
-                           hipStream_t s) {
-  k_zero_amax<<<1, 64, 0, s>>>(amax);
-  hipError_t e = dt == 0 ? launch_amax<uint16_t>(x, rows, cols, ld, amax, s)
-                         : launch_amax<float>(x, rows, cols, ld, amax, s);
-  if (e != hipSuccess) return e;
+// The cast pass of nvfp4_quantize (amax already final).
+static hipError_t launch_cast(const void* x, int dt, int64_t rows, int64_t cols, int64_t ld,
+                              int layout, int rnd, uint64_t seed, uint8_t* codes, uint8_t* scales,
+                              uint8_t* codes_t, uint8_t* scales_t, float* tensor_scale,
+                              float* amax, hipStream_t s) {
   const uint32_t key = sr_key(seed);
   if (layout == 0) {
     constexpr int UNROLL = 2;
@@ -512,18 +530,25 @@ hipError_t launch_quantize(const void* x, int dt, int64_t rows, int64_t cols, in
   return hipGetLastError();
 }
 
-hipError_t launch_rht_quantize(const void* x, int dt, int64_t tokens, int64_t cols, int64_t ld,
-                               uint32_t sign_mask, int rnd, uint64_t seed, uint8_t* codes,
-                               uint8_t* scales, float* tensor_scale, float* amax, hipStream_t s) {
-  sign_mask &= 0xFFFFu;
-  k_zero_amax<<<1, 64, 0, s>>>(amax);
+// RHT amax pass (plus the plain amax into amax_plain when it is not null).
+static hipError_t launch_rht_amax(const void* x, int dt, int64_t tokens, int64_t cols, int64_t ld,
+                                  uint32_t sign_mask, float* amax, float* amax_plain, hipStream_t s) {
+  k_zero_amax<<<1, 64, 0, s>>>(amax, amax_plain);
   dim3 grid((unsigned)((cols + kColCols - 1) / kColCols), (unsigned)((tokens + kColTok - 1) / kColTok));
   if (dt == 0)
-    k_rht_amax<uint16_t><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(x), tokens, cols, ld, sign_mask, amax);
+    k_rht_amax<uint16_t><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(x), tokens, cols, ld,
+                                              sign_mask, amax, amax_plain);
   else
-    k_rht_amax<float><<<grid, 256, 0, s>>>(static_cast<const float*>(x), tokens, cols, ld, sign_mask, amax);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+    k_rht_amax<float><<<grid, 256, 0, s>>>(static_cast<const float*>(x), tokens, cols, ld, sign_mask,
+                                           amax, amax_plain);
+  return hipGetLastError();
+}
+
+// The cast pass of nvfp4_rht_quantize (amax already final).
+static hipError_t launch_rht_cast(const void* x, int dt, int64_t tokens, int64_t cols, int64_t ld,
+                                  uint32_t sign_mask, int rnd, uint64_t seed, uint8_t* codes,
+                                  uint8_t* scales, float* tensor_scale, float* amax, hipStream_t s) {
+  dim3 grid((unsigned)((cols + kColCols - 1) / kColCols), (unsigned)((tokens + kColTok - 1) / kColTok));
   const uint32_t key = sr_key(seed);
 #define RHT_LAUNCH(T, R)                                                                         \
   k_cast_col1d<T, R, true><<<grid, 256, 0, s>>>(static_cast<const T*>(x), tokens, cols, ld,       \
@@ -535,6 +560,46 @@ hipError_t launch_rht_quantize(const void* x, int dt, int64_t tokens, int64_t co
   }
 #undef RHT_LAUNCH
   return hipGetLastError();
+}
+
+hipError_t launch_quantize(const void* x, int dt, int64_t rows, int64_t cols, int64_t ld,
+                           int layout, int rnd, uint64_t seed, uint8_t* codes, uint8_t* scales,
+                           uint8_t* codes_t, uint8_t* scales_t, float* tensor_scale, float* amax,
+                           hipStream_t s) {
+  k_zero_amax<<<1, 64, 0, s>>>(amax, nullptr);
+  hipError_t e = dt == 0 ? launch_amax<uint16_t>(x, rows, cols, ld, amax, s)
+                         : launch_amax<float>(x, rows, cols, ld, amax, s);
+  if (e != hipSuccess) return e;
+  return launch_cast(x, dt, rows, cols, ld, layout, rnd, seed, codes, scales, codes_t, scales_t,
+                     tensor_scale, amax, s);
+}
+
+hipError_t launch_rht_quantize(const void* x, int dt, int64_t tokens, int64_t cols, int64_t ld,
+                               uint32_t sign_mask, int rnd, uint64_t seed, uint8_t* codes,
+                               uint8_t* scales, float* tensor_scale, float* amax, hipStream_t s) {
+  sign_mask &= 0xFFFFu;
+  hipError_t e = launch_rht_amax(x, dt, tokens, cols, ld, sign_mask, amax, nullptr, s);
+  if (e != hipSuccess) return e;
+  return launch_rht_cast(x, dt, tokens, cols, ld, sign_mask, rnd, seed, codes, scales, tensor_scale,
+                         amax, s);
+}
+
+// Both quantizations of one tensor: one read for the two amaxes, then the
+// row cast and the RHT column cast.
+hipError_t launch_quantize_row_rht(const void* x, int dt, int64_t tokens, int64_t cols, int64_t ld,
+                                   int row_rnd, uint64_t row_seed, uint8_t* row_codes,
+                                   uint8_t* row_scales, float* row_ts, float* row_amax,
+                                   uint32_t sign_mask, int rht_rnd, uint64_t rht_seed,
+                                   uint8_t* rht_codes, uint8_t* rht_scales, float* rht_ts,
+                                   float* rht_amax, hipStream_t s) {
+  sign_mask &= 0xFFFFu;
+  hipError_t e = launch_rht_amax(x, dt, tokens, cols, ld, sign_mask, rht_amax, row_amax, s);
+  if (e != hipSuccess) return e;
+  e = launch_cast(x, dt, tokens, cols, ld, 0, row_rnd, row_seed, row_codes, row_scales, nullptr,
+                  nullptr, row_ts, row_amax, s);
+  if (e != hipSuccess) return e;
+  return launch_rht_cast(x, dt, tokens, cols, ld, sign_mask, rht_rnd, rht_seed, rht_codes,
+                         rht_scales, rht_ts, rht_amax, s);
 }
 
 }  // namespace nvfp4

@@ -8,7 +8,10 @@ summary, Resumo tecnico, 2. Metodologia Proposta):
                       along tokens (one sign vector for both), column-1D;
                       SR on dY, RNE on X                          (techniques 2, 4)
 Shapes: X [T x IN], W [OUT x IN], dY [T x OUT]; Y [T x OUT], dX [T x IN],
-dW [OUT x IN].  Every step is one call into libnvfp4; this module only owns the
+dW [OUT x IN].  X and dY each need a row quantization and an RHT column one;
+both come from one nvfp4_quantize_row_rht call (one read of the tensor for
+the two amaxes): X's in forward (its Wgrad operand is kept for backward), dY's
+in backward.  Every step is one call into libnvfp4; this module only owns the
 device buffers (allocated once, including the GEMM workspace shared by the three
 GEMMs, which therefore must stay on one stream) and the call order.
 """
@@ -72,10 +75,20 @@ class LinearStep:
         nv.nvfp4_quantize(w, dt, self.OUT, self.IN, self.IN, nv.NVFP4_TILE_2D, nv.NVFP4_RNE, 0,
                           q.codes, q.scales, q.codes_t, q.scales_t, q.ts, q.amax, stream)
 
-    def forward(self, x, dt, stream=None):
+    def forward(self, x, dt, sign_mask: int | None = None, stream=None):
+        """Y = X W^T.  With the RHT sign mask, X's Wgrad operand is quantized in
+        the same call and kept for backward."""
         q = self.qx
-        nv.nvfp4_quantize(x, dt, self.T, self.IN, self.IN, nv.NVFP4_ROW_1D, nv.NVFP4_RNE, 0,
-                          q.codes, q.scales, None, None, q.ts, q.amax, stream)
+        if sign_mask is None:
+            nv.nvfp4_quantize(x, dt, self.T, self.IN, self.IN, nv.NVFP4_ROW_1D, nv.NVFP4_RNE, 0,
+                              q.codes, q.scales, None, None, q.ts, q.amax, stream)
+            self._xt_mask = None
+        else:
+            b = self.qx_t
+            nv.nvfp4_quantize_row_rht(x, dt, self.T, self.IN, self.IN, nv.NVFP4_RNE, 0, q.codes,
+                                      q.scales, q.ts, q.amax, sign_mask, nv.NVFP4_RNE, 0, b.codes,
+                                      b.scales, b.ts, b.amax, stream)
+            self._xt_mask = sign_mask & 0xFFFF
         w = self.qw
         nv.nvfp4_gemm(self.T, self.OUT, self.IN, q.codes, q.scales, q.ts, w.codes, w.scales, 16,
                       w.ts, self.y, self.OUT, 0.0, workspace=self.ws, stream=stream)
@@ -83,17 +96,16 @@ class LinearStep:
     def backward(self, x, dy, dt, sign_mask: int, seed_row: int, seed_col: int,
                  accumulate_wgrad: bool = False, stream=None):
         T, IN, OUT = self.T, self.IN, self.OUT
-        q = self.qdy
-        nv.nvfp4_quantize(dy, dt, T, OUT, OUT, nv.NVFP4_ROW_1D, nv.NVFP4_SR, seed_row,
-                          q.codes, q.scales, None, None, q.ts, q.amax, stream)
+        q, a, b = self.qdy, self.qdy_t, self.qx_t
+        nv.nvfp4_quantize_row_rht(dy, dt, T, OUT, OUT, nv.NVFP4_SR, seed_row, q.codes, q.scales,
+                                  q.ts, q.amax, sign_mask, nv.NVFP4_SR, seed_col, a.codes,
+                                  a.scales, a.ts, a.amax, stream)
         w = self.qw
         nv.nvfp4_gemm(T, IN, OUT, q.codes, q.scales, q.ts, w.codes_t, w.scales_t, 16, w.ts,
                       self.dx, IN, 0.0, workspace=self.ws, stream=stream)
-        a, b = self.qdy_t, self.qx_t
-        nv.nvfp4_rht_quantize(dy, dt, T, OUT, OUT, sign_mask, nv.NVFP4_SR, seed_col, a.codes,
-                              a.scales, a.ts, a.amax, stream)
-        nv.nvfp4_rht_quantize(x, dt, T, IN, IN, sign_mask, nv.NVFP4_RNE, 0, b.codes, b.scales,
-                              b.ts, b.amax, stream)
+        if getattr(self, "_xt_mask", None) != (sign_mask & 0xFFFF):
+            nv.nvfp4_rht_quantize(x, dt, T, IN, IN, sign_mask, nv.NVFP4_RNE, 0, b.codes, b.scales,
+                                  b.ts, b.amax, stream)
         nv.nvfp4_gemm(OUT, IN, T, a.codes, a.scales, a.ts, b.codes, b.scales, 1, b.ts, self.dw,
                       IN, 1.0 if accumulate_wgrad else 0.0, workspace=self.ws, stream=stream)
 
@@ -101,5 +113,5 @@ class LinearStep:
              accumulate_wgrad: bool = False, quantize_weight: bool = True, stream=None):
         if quantize_weight:
             self.quantize_weight(w, dt, stream)
-        self.forward(x, dt, stream)
+        self.forward(x, dt, sign_mask, stream)
         self.backward(x, dy, dt, sign_mask, seed_row, seed_col, accumulate_wgrad, stream)

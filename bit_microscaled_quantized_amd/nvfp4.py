@@ -19,8 +19,8 @@ NVFP4_BF16, NVFP4_F32 = 0, 1
 NVFP4_RNE, NVFP4_SR = 0, 1
 NVFP4_ROW_1D, NVFP4_COL_1D, NVFP4_TILE_2D = 0, 1, 2
 
-EXPORTED = ("nvfp4_quantize", "nvfp4_rht_quantize", "nvfp4_gemm", "nvfp4_gemm_workspace_size",
-            "nvfp4_status_str")
+EXPORTED = ("nvfp4_quantize", "nvfp4_rht_quantize", "nvfp4_quantize_row_rht", "nvfp4_gemm",
+            "nvfp4_gemm_workspace_size", "nvfp4_status_str")
 
 _lib = None
 
@@ -50,6 +50,9 @@ def load_library():
     L.nvfp4_quantize.restype = i32
     L.nvfp4_rht_quantize.argtypes = [vp, i32, i64, i64, i64, u32, i32, u64, vp, vp, vp, vp, vp]
     L.nvfp4_rht_quantize.restype = i32
+    L.nvfp4_quantize_row_rht.argtypes = [vp, i32, i64, i64, i64, i32, u64, vp, vp, vp, vp, u32, i32,
+                                         u64, vp, vp, vp, vp, vp]
+    L.nvfp4_quantize_row_rht.restype = i32
     L.nvfp4_gemm.argtypes = [i64, i64, i64, vp, vp, vp, vp, vp, i32, vp, vp, i64, f32, vp, i64, vp]
     L.nvfp4_gemm.restype = i32
     L.nvfp4_gemm_workspace_size.argtypes = [i64, i64, i64, ctypes.POINTER(i64)]
@@ -102,6 +105,18 @@ def nvfp4_rht_quantize(x, dt, tokens, cols, ld_x, sign_mask, rnd, seed, codes, s
         _addr(x), dt, tokens, cols, ld_x, sign_mask & 0xFFFFFFFF, rnd, seed & (2 ** 64 - 1),
         _addr(codes), _addr(scales), _addr(tensor_scale), _addr(amax), _stream(stream))
     return _check("nvfp4_rht_quantize", st, raise_on_error)
+
+
+def nvfp4_quantize_row_rht(x, dt, tokens, cols, ld_x, row_rnd, row_seed, row_codes, row_scales,
+                           row_tensor_scale, row_amax, sign_mask, rht_rnd, rht_seed, rht_codes,
+                           rht_scales, rht_tensor_scale, rht_amax, stream=None,
+                           raise_on_error=True) -> int:
+    st = load_library().nvfp4_quantize_row_rht(
+        _addr(x), dt, tokens, cols, ld_x, row_rnd, row_seed & (2 ** 64 - 1), _addr(row_codes),
+        _addr(row_scales), _addr(row_tensor_scale), _addr(row_amax), sign_mask & 0xFFFFFFFF,
+        rht_rnd, rht_seed & (2 ** 64 - 1), _addr(rht_codes), _addr(rht_scales),
+        _addr(rht_tensor_scale), _addr(rht_amax), _stream(stream))
+    return _check("nvfp4_quantize_row_rht", st, raise_on_error)
 
 
 def nvfp4_gemm(M, N, K, a_codes, a_scales, a_tensor_scale, b_codes, b_scales, b_scale_rowdiv,

@@ -112,6 +112,26 @@ nvfp4_status nvfp4_rht_quantize(const void *x, int dt, int64_t tokens, int64_t c
                                 uint8_t *scales, float *tensor_scale, float *amax, void *stream);
 
 /*
+ * nvfp4_quantize_row_rht -- both quantizations a tensor needs in one linear
+ * layer: the row-1D one (X for Fprop, dY for Dgrad) and the RHT column one
+ * (X, dY for Wgrad).  Its outputs are exactly those of
+ *   nvfp4_quantize(x, dt, tokens, cols, ld_x, NVFP4_ROW_1D, row_rnd, row_seed,
+ *                  row_codes, row_scales, NULL, NULL, row_tensor_scale, row_amax)
+ *   nvfp4_rht_quantize(x, dt, tokens, cols, ld_x, sign_mask, rht_rnd, rht_seed,
+ *                      rht_codes, rht_scales, rht_tensor_scale, rht_amax)
+ * (same layouts, SR indices and errors), but both tensor amaxes (of x and of
+ * its RHT) come from ONE read of x, saving a full pass over the tensor.
+ * The two output sets must not overlap.
+ */
+nvfp4_status nvfp4_quantize_row_rht(const void *x, int dt, int64_t tokens, int64_t cols,
+                                    int64_t ld_x, int row_rnd, uint64_t row_seed,
+                                    uint8_t *row_codes, uint8_t *row_scales,
+                                    float *row_tensor_scale, float *row_amax, uint32_t sign_mask,
+                                    int rht_rnd, uint64_t rht_seed, uint8_t *rht_codes,
+                                    uint8_t *rht_scales, float *rht_tensor_scale, float *rht_amax,
+                                    void *stream);
+
+/*
  * nvfp4_gemm -- block-scaled NVFP4 contraction with FP32 accumulation
  * (the NVFP4 GEMMs of "Suporte de Hardware", part 3 of the same page).
  *

@@ -83,6 +83,28 @@ def gpu_rht_quantize(x: np.ndarray, sign_mask: int, rnd: int = 0, seed: int = 0)
                 amax=float(host(am)[0]), dev=dict(codes=codes, scales=scales, ts=ts))
 
 
+def gpu_quantize_row_rht(x: np.ndarray, sign_mask: int, row_rnd: int, row_seed: int, rht_rnd: int,
+                         rht_seed: int) -> tuple[dict, dict]:
+    """nvfp4_quantize_row_rht: (row-1D outputs, RHT column outputs), both as
+    returned by gpu_quantize / gpu_rht_quantize."""
+    torch = torch_cuda()
+    tokens, cols = x.shape
+    xd = to_dev(x)
+    u8 = dict(dtype=torch.uint8, device="cuda")
+    f32 = dict(dtype=torch.float32, device="cuda")
+    rc, rs = torch.empty((tokens, cols // 2), **u8), torch.empty((tokens, cols // 16), **u8)
+    hc, hs = torch.empty((cols, tokens // 2), **u8), torch.empty((cols, tokens // 16), **u8)
+    rts, ram, hts, ham = (torch.empty(1, **f32) for _ in range(4))
+    nv.nvfp4_quantize_row_rht(xd, dtype_code(x), tokens, cols, cols, row_rnd, row_seed, rc, rs, rts, ram,
+                              sign_mask, rht_rnd, rht_seed, hc, hs, hts, ham)
+    torch.cuda.synchronize()
+    row = dict(codes=host(rc), scales=host(rs), tensor_scale=float(host(rts)[0]), amax=float(host(ram)[0]),
+               dev=dict(codes=rc, scales=rs, ts=rts))
+    rht = dict(codes=host(hc), scales=host(hs), tensor_scale=float(host(hts)[0]), amax=float(host(ham)[0]),
+               dev=dict(codes=hc, scales=hs, ts=hts))
+    return row, rht
+
+
 def gpu_gemm(M, N, K, a: dict, b: dict, b_rowdiv: int, c0: np.ndarray | None = None,
              beta: float = 0.0, workspace="auto") -> np.ndarray:
     """C = beta*C0 + A.B^T from device-resident quantize outputs a, b (dicts with

@@ -119,6 +119,25 @@ def test_rht_parity(ora, shape, rnd, dtype):
     _same(g, o, KEYS)
 
 
+@pytest.mark.parametrize("shape", RHT_SHAPES)
+@pytest.mark.parametrize("rnds", [(nv.NVFP4_RNE, nv.NVFP4_RNE), (nv.NVFP4_SR, nv.NVFP4_SR),
+                                  (nv.NVFP4_RNE, nv.NVFP4_SR)])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_row_rht_parity(ora, shape, rnds, dtype):
+    """The fused call equals the two separate calls bit for bit, and both
+    equal the oracle."""
+    x = _inputs("outliers", shape, 71 + shape[1])
+    if dtype == "bf16":
+        x = synth.f32_to_bf16_bits(x)
+    mask = synth.sign_mask16(shape[1])
+    row_rnd, rht_rnd = rnds
+    g_row, g_rht = gpuio.gpu_quantize_row_rht(x, mask, row_rnd, 21, rht_rnd, 22)
+    _same(g_row, gpuio.gpu_quantize(x, nv.NVFP4_ROW_1D, row_rnd, 21), KEYS)
+    _same(g_rht, gpuio.gpu_rht_quantize(x, mask, rht_rnd, 22), KEYS)
+    _same(g_row, ora.quantize(x, ora.ROW_1D, row_rnd, 21), KEYS)
+    _same(g_rht, ora.rht_quantize(x, mask, rht_rnd, 22), KEYS)
+
+
 # ------------------------------------------------------------------ edge cases
 def test_golden_worked_example_on_gpu(ora):
     g_ = json.load(open(os.path.join(GOLDEN, "row1d_rne_two_blocks.json")))
@@ -177,6 +196,16 @@ def test_edge_cases_rht(ora, name, rnd):
     g = gpuio.gpu_rht_quantize(x, 0x5A5A, rnd, 17)
     o = ora.rht_quantize(x, 0x5A5A, rnd, 17)
     _same(g, o, KEYS)
+
+
+@pytest.mark.parametrize("name", sorted(EDGE))
+def test_edge_cases_row_rht(ora, name):
+    x = EDGE[name]
+    if name == "huge":
+        x = x * np.float32(0.01)
+    g_row, g_rht = gpuio.gpu_quantize_row_rht(x, 0x5A5A, nv.NVFP4_SR, 31, nv.NVFP4_SR, 32)
+    _same(g_row, ora.quantize(x, ora.ROW_1D, ora.SR, 31), KEYS)
+    _same(g_rht, ora.rht_quantize(x, 0x5A5A, ora.SR, 32), KEYS)
 
 
 def test_e2m1_conversion_sweep(ora):

@@ -85,6 +85,24 @@ def test_rht_quantize_argument_errors():
     assert r(scales=FAKE + 1) == b.NVFP4_EALIGN
 
 
+def test_quantize_row_rht_argument_errors():
+    def r(**kw):
+        args = dict(x=FAKE, dt=0, tokens=32, cols=32, ld_x=32, row_rnd=0, row_seed=0, row_codes=FAKE,
+                    row_scales=FAKE, row_tensor_scale=FAKE, row_amax=FAKE, sign_mask=0, rht_rnd=1,
+                    rht_seed=0, rht_codes=FAKE, rht_scales=FAKE, rht_tensor_scale=FAKE, rht_amax=FAKE)
+        args.update(kw)
+        return nv.nvfp4_quantize_row_rht(**args, stream=0, raise_on_error=False)
+    assert r(x=None) == b.NVFP4_EINVAL
+    assert r(rht_codes=None) == b.NVFP4_EINVAL
+    assert r(row_amax=None) == b.NVFP4_EINVAL
+    assert r(row_rnd=2) == b.NVFP4_EINVAL
+    assert r(rht_rnd=-1) == b.NVFP4_EINVAL
+    assert r(tokens=40) == b.NVFP4_ESHAPE
+    assert r(cols=20, ld_x=20) == b.NVFP4_ESHAPE
+    assert r(rht_scales=FAKE + 1) == b.NVFP4_EALIGN
+    assert r(row_tensor_scale=FAKE + 2) == b.NVFP4_EALIGN
+
+
 def g(**kw):
     args = dict(M=256, N=256, K=256, a_codes=FAKE, a_scales=FAKE, a_tensor_scale=FAKE, b_codes=FAKE,
                 b_scales=FAKE, b_scale_rowdiv=1, b_tensor_scale=FAKE, c=FAKE, ldc=256, beta=0.0)
