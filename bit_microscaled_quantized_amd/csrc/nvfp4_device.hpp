@@ -129,18 +129,20 @@ __host__ __device__ __forceinline__ uint32_t pcg_host(uint32_t v) {
 //   a >= 1: the grid index is (bits(a) >> 22) - 252 and the fraction times
 //           2^22 is m22, the 22 mantissa bits below the grid bit.  r16 * 64 <
 //           m22 exactly when m22 + rc * 64 + 63 carries out of those 22 bits,
-//           so adding rc * 64 + 63 to bits(a) rounds up or down by itself.
-//   a < 1 : step 0.5; with T = ceil(a * 2^17) (exact), r16 < frac * 65536 is
-//           r16 < T for a < 0.5 and r16 < T - 65536 for a >= 0.5, so the index
-//           is (T + rc) >> 16 (0, 1 or 2).
-// Both forms are computed and one is selected, without branches.
+//           so the index is (bits(a) + 63 - 252 * 2^22 + 64 rc) >> 22, which
+//           (64 rc being a multiple of 64) is (X + rc) >> 16 with
+//           X = (bits(a) + 63 - 252 * 2^22) >> 6.
+//   a < 1 : step 0.5; with X = ceil(a * 2^17) (exact), r16 < frac * 65536 is
+//           r16 < X for a < 0.5 and r16 < X - 65536 for a >= 0.5, so the index
+//           is (X + rc) >> 16 (0, 1 or 2).
+// X is selected between the two forms without branches.
 __device__ __forceinline__ uint32_t sr_code_c(float v, uint32_t rc) {
   const float a = fminf(fabsf(v), 6.0f);  // v is finite
   const uint32_t b = __float_as_uint(a);
-  const uint32_t i_hi = (b + (rc << 6) + (63u - (252u << 22))) >> 22;
-  const uint32_t i_lo = ((uint32_t)__builtin_ceilf(a * 131072.0f) + rc) >> 16;
-  const uint32_t idx = __builtin_unpredictable(b >= 0x3F800000u) ? i_hi : i_lo;
-  return ((__float_as_uint(v) >> 28) & 8u) | idx;
+  const uint32_t x_hi = (b + (63u - (252u << 22))) >> 6;
+  const uint32_t x_lo = (uint32_t)__builtin_ceilf(a * 131072.0f);
+  const uint32_t x = __builtin_unpredictable(b >= 0x3F800000u) ? x_hi : x_lo;
+  return ((__float_as_uint(v) >> 28) & 8u) | ((x + rc) >> 16);
 }
 
 __device__ __forceinline__ uint32_t sr_code(float v, uint32_t r16) {

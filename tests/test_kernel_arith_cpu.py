@@ -6,9 +6,9 @@ oracle's stochastic-rounding rule).
 * Division by 6 of a block amax: RN(1/6) * x followed by one FMA correction of
   the exact residual equals the correctly rounded x / 6 for every FP32
   x >= 2^-100 (the kernels divide directly below that).
-* Stochastic rounding: with rc = 65535 - r16, the carry form
-  (bits(a) + 64 rc + 63 - 252 * 2^22) >> 22 for a >= 1 and
-  (ceil(a * 2^17) + rc) >> 16 for a < 1 gives the oracle's code for every FP32
+* Stochastic rounding: with rc = 65535 - r16, the carry form (X + rc) >> 16,
+  X = (bits(a) + 63 - 252 * 2^22) >> 6 for a >= 1 and X = ceil(a * 2^17) for
+  a < 1, gives the oracle's code for every FP32
   v with |v| <= 6.5 (and a sweep beyond), at r16 values on both sides of each
   input's rounding threshold and at a pseudo-random r16.
 """
@@ -39,10 +39,10 @@ static uint32_t sr_kernel(float v, uint32_t r16) {
   uint32_t rc = r16 ^ 0xFFFFu;
   float a = fminf(fabsf(v), 6.0f);
   uint32_t b = u_of(a);
-  uint32_t i_hi = (b + (rc << 6) + (63u - (252u << 22))) >> 22;
-  uint32_t i_lo = ((uint32_t)ceilf(a * 131072.0f) + rc) >> 16;
-  uint32_t idx = b >= 0x3F800000u ? i_hi : i_lo;
-  return ((u_of(v) >> 28) & 8u) | idx;
+  uint32_t x_hi = (b + (63u - (252u << 22))) >> 6;
+  uint32_t x_lo = (uint32_t)ceilf(a * 131072.0f);
+  uint32_t x = b >= 0x3F800000u ? x_hi : x_lo;
+  return ((u_of(v) >> 28) & 8u) | ((x + rc) >> 16);
 }
 
 static const double MAG[8] = {0, 0.5, 1, 1.5, 2, 3, 4, 6};
