@@ -221,10 +221,48 @@ __global__ __launch_bounds__(256) void k_cast_row1d(const T* __restrict__ x, int
 constexpr int kColTok = 512;  // tokens per workgroup tile
 constexpr int kColCols = 64;  // columns per workgroup tile
 
+// A thread's 16 rows x 8 columns, kept as loaded (bf16: one 16-byte word per
+// row, 64 VGPRs; fp32: two) and converted one column at a time, which keeps
+// the register footprint (and so the occupancy) of the column kernels low.
 template <typename T>
-__device__ __forceinline__ void load_col8(const T* p, float* v) {
-  load8<T>(p, v);
-}
+struct ColTile;
+
+template <>
+struct ColTile<uint16_t> {
+  uint4 w[16];
+  __device__ __forceinline__ void load(const uint16_t* p, int64_t ld) {
+#pragma unroll
+    for (int j = 0; j < 16; j++) w[j] = *reinterpret_cast<const uint4*>(p + j * ld);
+  }
+  // column k (0..7) of the 16 rows
+  __device__ __forceinline__ void column(int k, float* u) const {
+#pragma unroll
+    for (int j = 0; j < 16; j++) {
+      const uint32_t d = k < 2 ? w[j].x : k < 4 ? w[j].y : k < 6 ? w[j].z : w[j].w;
+      u[j] = (k & 1) ? bf16hi(d) : bf16lo(d);
+    }
+  }
+};
+
+template <>
+struct ColTile<float> {
+  float4 w[16][2];
+  __device__ __forceinline__ void load(const float* p, int64_t ld) {
+#pragma unroll
+    for (int j = 0; j < 16; j++) {
+      w[j][0] = *reinterpret_cast<const float4*>(p + j * ld);
+      w[j][1] = *reinterpret_cast<const float4*>(p + j * ld + 4);
+    }
+  }
+  __device__ __forceinline__ void column(int k, float* u) const {
+#pragma unroll
+    for (int j = 0; j < 16; j++) {
+      const float4 q = w[j][k >> 2];
+      const int e = k & 3;
+      u[j] = e == 0 ? q.x : e == 1 ? q.y : e == 2 ? q.z : q.w;
+    }
+  }
+};
 
 template <typename T, int RND, bool RHT>
 __global__ __launch_bounds__(256) void k_cast_col1d(const T* __restrict__ x, int64_t rows,
@@ -249,30 +287,24 @@ __global__ __launch_bounds__(256) void k_cast_col1d(const T* __restrict__ x, int
   const int64_t cc = c0 + 8 * co;   // first column of the octet
   const bool valid = tg < rows && cc < cols;
 
-  float u[8][16];
-  if (valid) {
-#pragma unroll
-    for (int j = 0; j < 16; j++) {
-      float v[8];
-      load_col8<T>(x + (tg + j) * ld + cc, v);
-#pragma unroll
-      for (int k = 0; k < 8; k++) u[k][j] = v[k];
-    }
-  }
+  ColTile<T> tile;
+  if (valid) tile.load(x + tg * ld + cc, ld);
 #pragma unroll
   for (int k = 0; k < 8; k++) {
     uint32_t e_b = 0u;
     uint32_t w0 = 0u, w1 = 0u;
     if (valid) {
-      if constexpr (RHT) rht16(u[k], sign_mask);
+      float u[16];
+      tile.column(k, u);
+      if constexpr (RHT) rht16(u, sign_mask);
       float am = 0.0f;
 #pragma unroll
-      for (int j = 0; j < 16; j++) am = fmaxf(am, fabsf(u[k][j]));
+      for (int j = 0; j < 16; j++) am = fmaxf(am, fabsf(u[j]));
       float r_b;
       block_scale(am, s_enc, rtab, e_b, r_b);
       float s[16];
 #pragma unroll
-      for (int j = 0; j < 16; j++) s[j] = u[k][j] * r_b;
+      for (int j = 0; j < 16; j++) s[j] = u[j] * r_b;
       const uint2 w = encode16<RND>(s, key, (uint32_t)((cc + k) * rows + tg) >> 1);
       w0 = w.x;
       w1 = w.y;
@@ -334,23 +366,19 @@ __global__ __launch_bounds__(256) void k_rht_amax(const T* __restrict__ x, int64
   const int64_t cc = c0 + 8 * co;
   float am = 0.0f, ap = 0.0f;
   if (tg < rows && cc < cols) {
-    float u[8][16];
-#pragma unroll
-    for (int j = 0; j < 16; j++) {
-      float v[8];
-      load_col8<T>(x + (tg + j) * ld + cc, v);
-#pragma unroll
-      for (int k = 0; k < 8; k++) u[k][j] = v[k];
-    }
+    ColTile<T> tile;
+    tile.load(x + tg * ld + cc, ld);
 #pragma unroll
     for (int k = 0; k < 8; k++) {
+      float u[16];
+      tile.column(k, u);
       if (amax_plain != nullptr) {
 #pragma unroll
-        for (int j = 0; j < 16; j++) ap = fmaxf(ap, fabsf(u[k][j]));
+        for (int j = 0; j < 16; j++) ap = fmaxf(ap, fabsf(u[j]));
       }
-      rht16(u[k], sign_mask);
+      rht16(u, sign_mask);
 #pragma unroll
-      for (int j = 0; j < 16; j++) am = fmaxf(am, fabsf(u[k][j]));
+      for (int j = 0; j < 16; j++) am = fmaxf(am, fabsf(u[j]));
     }
   }
   block_atomic_max(__float_as_uint(am), amax, __float_as_uint(ap), amax_plain);
