@@ -26,8 +26,11 @@
 // are fetched with direct-to-LDS loads (global_load_lds, 16 bytes per lane for
 // codes, 4 for scales) issued one stage ahead, so no registers hold prefetched
 // data and each code load instruction covers eight full cache lines.  Chunk c
-// (16 bytes) of row r lands in slot 8r + (c ^ (r & 7)), which makes the
-// fragment reads (32 consecutive rows, same chunk) bank-conflict free.
+// (16 bytes) of row r lands in slot 8r + (c ^ ((r >> 1) & 7)).  gfx950's LDS
+// serves a 16-byte read for 16 lanes per cycle (64 banks): with 128-byte rows,
+// rows of equal parity share a bank half, so the 16 rows a fragment read
+// touches at once need 8 distinct slots per parity -- (r >> 1) & 7 gives that
+// (measured: 1.8x the read rate of c ^ (r & 7), which conflicts 2-way).
 //
 // Tiling: 512 threads = 8 waves (two per SIMD, so one wave's conversions
 // overlap the other's MFMAs) in a 2 x 4 grid; workgroup tile 256 x 256, wave
@@ -155,19 +158,24 @@ __global__ __launch_bounds__(512, 1) void k_gemm_nvfp4(
   const int64_t kb = K / 2;   // code bytes per row (a multiple of 32)
   const int64_t ks = K / 16;  // scale bytes per row (a multiple of 4)
 
-  // ---- stage fetch.  Code instruction j of a wave: rows 8(4 wave + j) + l/8,
-  // lane l takes chunk (l%8) ^ (row & 7) of its row.  Scale instruction i:
-  // rows 32 wave + 16 i + l/4, lane l takes dword l%4 of the row's 16 bytes.
+  // ---- stage fetch.  Code instruction j of a wave: rows r = 8(4 wave + j) +
+  // l/8; lane l fills slot l%8 of its row, i.e. takes chunk
+  // (l%8) ^ ((r >> 1) & 7) = (l%8) ^ (4 (j & 1) + (l/8) / 2).  Scale
+  // instruction i: rows 32 wave + 16 i + l/4, lane l takes dword l%4 of the
+  // row's 16 bytes.
   const int crow = lane >> 3;
-  const int cchunk = (lane & 7) ^ crow;
+  const int cchunk_e = (lane & 7) ^ (crow >> 1);        // even j
+  const int cchunk_o = (lane & 7) ^ (4 + (crow >> 1));  // odd j
   const int sdw = lane & 3;
   auto issue_stage = [&](int kt, uint8_t* st) {
     // in-row byte offsets, clamped to the row's last chunk / dword
-    const int64_t coff = min((int64_t)kt * (BKS / 2) + 16 * cchunk, kb - 16);
+    const int64_t coff_e = min((int64_t)kt * (BKS / 2) + 16 * cchunk_e, kb - 16);
+    const int64_t coff_o = min((int64_t)kt * (BKS / 2) + 16 * cchunk_o, kb - 16);
     const int64_t soff = min((int64_t)kt * (BKS / 16) + 4 * sdw, ks - 4);
 #pragma unroll
     for (int j = 0; j < 4; j++) {
       const int r = 8 * (4 * wave + j) + crow;
+      const int64_t coff = (j & 1) ? coff_o : coff_e;
       load_lds16(a_codes + (int64_t)min(m0 + r, M - 1) * kb + coff, st + (4 * wave + j) * 1024);
       load_lds16(b_codes + (int64_t)min(n0 + r, N - 1) * kb + coff, st + OFF_B + (4 * wave + j) * 1024);
     }
@@ -190,12 +198,12 @@ __global__ __launch_bounds__(512, 1) void k_gemm_nvfp4(
 
   // ---- fragment reads.  Lane (h, lr) of A tile i reads row wm*128 + 32i + lr
   // (B tile j: row wn*64 + 32j + lr), chunk 4h + g in quad g: slot
-  // 8*row + ((4h + g) ^ (lr & 7)); its two scale bytes (blocks 2(4h + g) and
+  // 8*row + ((4h + g) ^ ((lr >> 1) & 7)); its two scale bytes (blocks 2(4h + g) and
   // 2(4h + g) + 1) sit at row*16 + 2(4h + g).
   const int rowa = wm * 128 + lr;
   const int rowb = wn * 64 + lr;
   auto read_quad = [&](const uint8_t* st, int g, uint4* ca, uint4* cb, uint32_t* sa, uint32_t* sb) {
-    const int sw = ((4 * h + g) ^ (lr & 7)) << 4;
+    const int sw = ((4 * h + g) ^ ((lr >> 1) & 7)) << 4;
 #pragma unroll
     for (int i = 0; i < 4; i++) {
       ca[i] = *reinterpret_cast<const uint4*>(st + (rowa + 32 * i) * 128 + sw);
