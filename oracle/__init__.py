@@ -66,6 +66,10 @@ def lib():
         L.ora_dequant.argtypes, L.ora_dequant.restype = [i64, i64, vp, vp, i32, f32, vp], None
         L.ora_gemm_f64.argtypes, L.ora_gemm_f64.restype = [i64, i64, i64, vp, vp, f64, vp], None
         L.ora_num_threads.argtypes, L.ora_num_threads.restype = [], i32
+        L.ora_mx_scale_exp.argtypes, L.ora_mx_scale_exp.restype = [f32], i32
+        L.ora_mx_quantize_range.argtypes = [vp, i32, i64, i64, i64, i32, i32, u64, vp, vp, i64, i64]
+        L.ora_mx_quantize_range.restype = i32
+        L.ora_mx_dequant.argtypes, L.ora_mx_dequant.restype = [i64, i64, vp, vp, vp], None
         _lib = L
     return _lib
 
@@ -197,6 +201,45 @@ def dequant(codes: np.ndarray, scales: np.ndarray, tensor_scale: float,
     n, k = codes.shape[0], codes.shape[1] * 2
     out = np.empty((n, k), np.float64)
     lib().ora_dequant(n, k, _ptr(codes), _ptr(scales), scale_rowdiv, tensor_scale, _ptr(out))
+    return out
+
+
+def mx_scale_exp(amax_b: float) -> int:
+    """Shared exponent of an MXFP4 block (E8M0 code = e + 127)."""
+    return lib().ora_mx_scale_exp(amax_b)
+
+
+def mx_quantize(x: np.ndarray, layout: int, rnd: int = RNE, seed: int = 0,
+                lines: tuple[int, int] | None = None) -> dict:
+    """MXFP4-quantize a 2D array (bf16 bit patterns or float32): blocks of 32
+    along rows (ROW_1D, codes [rows][cols/2], scales [rows][cols/32]) or along
+    columns, written transposed (COL_1D, codes [cols][rows/2], scales
+    [cols][rows/32]).  Scales are E8M0 codes; there is no tensor scale."""
+    x = np.ascontiguousarray(x)
+    rows, cols = x.shape
+    if layout == COL_1D:
+        codes = np.zeros((cols, rows // 2), np.uint8)
+        scales = np.zeros((cols, rows // 32), np.uint8)
+    elif layout == ROW_1D:
+        codes = np.zeros((rows, cols // 2), np.uint8)
+        scales = np.zeros((rows, cols // 32), np.uint8)
+    else:
+        raise ValueError("MXFP4 layouts are ROW_1D and COL_1D")
+    b, e = lines if lines is not None else (0, 1 << 62)
+    rc = lib().ora_mx_quantize_range(_ptr(x), _dtype_code(x), rows, cols, cols, layout, rnd,
+                                     seed & ((1 << 64) - 1), _ptr(codes), _ptr(scales), b, e)
+    if rc != 0:
+        raise ValueError(f"oracle mx_quantize rejected shape {x.shape} layout {layout}")
+    return dict(codes=codes, scales=scales)
+
+
+def mx_dequant(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """Exact FP64 values of n x k MXFP4 codes (k contiguous), scales [n][k/32]."""
+    codes = np.ascontiguousarray(codes)
+    scales = np.ascontiguousarray(scales)
+    n, k = codes.shape[0], codes.shape[1] * 2
+    out = np.empty((n, k), np.float64)
+    lib().ora_mx_dequant(n, k, _ptr(codes), _ptr(scales), _ptr(out))
     return out
 
 

@@ -25,6 +25,8 @@
  *   [PCG]    M. Jarzynski, M. Olano, "Hash Functions for GPU Rendering",
  *            JCGT 9(3), 2020: the "pcg" 32-bit hash.
  *   [FWHT]   the radix-2 fast Walsh-Hadamard transform (Sylvester ordering).
+ *   MXFP4, the comparison format of [NV-SUM] parts 1 and 2: blocks of 32,
+ *            power-of-two (UE8M0) scales; conversion rule from [OCP-MX].
  *
  * Where the pages are silent the oracle follows these readings (all FP32
  * arithmetic is IEEE binary32, round-to-nearest-even, no contraction, in the
@@ -490,6 +492,122 @@ int ora_num_threads(void)
 #else
     return 1;
 #endif
+}
+
+/* ------------------------------------------------------------------ */
+/* MXFP4, the comparison format                                       */
+/* ------------------------------------------------------------------ */
+
+/* [NV-SUM] part 1 ("Limitacoes de Formatos Existentes") and part 2
+ * ("Fatores de Escala Precisos") describe MXFP4 as FP4 values in blocks of 32
+ * with a power-of-two UE8M0 scale.  [OCP-MX], conversion from FP32 to MX:
+ * the shared exponent is floor(log2(max |V_i|)) - emax_elem, emax_elem = 2 for
+ * E2M1 (6 = 1.5 * 2^2), clamped to the E8M0 range [-127, 127]; each element
+ * is V_i / 2^e rounded to E2M1, values beyond the largest E2M1 magnitude
+ * clamped to it.  There is no tensor-level scale.  An all-zero block takes the
+ * smallest scale (2^-127, code 0). */
+
+/* Shared exponent e of a block with maximum magnitude amax_b. */
+int ora_mx_scale_exp(float amax_b)
+{
+    int ex, e;
+    if (!(amax_b > 0.0f))
+        return -127;
+    frexpf(amax_b, &ex); /* amax_b = m * 2^ex, m in [0.5, 1): floor(log2) = ex - 1 */
+    e = (ex - 1) - 2;
+    if (e < -127)
+        e = -127;
+    if (e > 127)
+        e = 127;
+    return e;
+}
+
+/* E2M1 code of y in a block with shared exponent e: v = y * 2^-e (one FP32
+ * multiply by the exact power of two), then RNE or SR as for NVFP4. */
+static int mx_encode(float y, int e, int rnd, uint64_t seed, uint64_t out_index)
+{
+    float mul = (float)ldexp(1.0, -e);
+    return encode(y, mul, rnd, seed, out_index);
+}
+
+/* Quantize a rows x cols tensor to MXFP4 (no tensor scale).
+ *   ROW_1D: blocks of 32 along a row; codes [rows][cols/2], scales (E8M0
+ *           codes, e + 127) [rows][cols/32]; output index i = r*cols + c.
+ *   COL_1D: blocks of 32 along a column; codes [cols][rows/2], scales
+ *           [cols][rows/32]; output index i = c*rows + r.
+ * Only the lines in [begin, end) (rows for ROW_1D, columns for COL_1D) are
+ * written.  The block dimension must be a multiple of 32, the other of 16.
+ * Returns 0 or -1. */
+int ora_mx_quantize_range(const void *x, int dtype, int64_t rows, int64_t cols, int64_t ld,
+                          int layout, int rnd, uint64_t seed, uint8_t *codes, uint8_t *scales,
+                          int64_t begin, int64_t end)
+{
+    int64_t line;
+    if (rows <= 0 || cols <= 0 || rows % 16 || cols % 16 || ld < cols || begin < 0)
+        return -1;
+    if (layout != ORA_ROW_1D && layout != ORA_COL_1D)
+        return -1;
+    if ((layout == ORA_ROW_1D && cols % 32) || (layout == ORA_COL_1D && rows % 32))
+        return -1;
+    if (layout == ORA_ROW_1D) {
+        if (end > rows)
+            end = rows;
+#pragma omp parallel for schedule(static)
+        for (line = begin; line < end; line++) {
+            int64_t b;
+            for (b = 0; b < cols / 32; b++) {
+                float amax_b = 0.0f;
+                int j, e;
+                for (j = 0; j < 32; j++) {
+                    float a = fabsf(load(x, dtype, ld, line, 32 * b + j));
+                    if (a > amax_b)
+                        amax_b = a;
+                }
+                e = ora_mx_scale_exp(amax_b);
+                scales[line * (cols / 32) + b] = (uint8_t)(e + 127);
+                for (j = 0; j < 32; j++) {
+                    uint64_t i = (uint64_t)line * cols + 32 * b + j;
+                    put_nibble(codes, i, mx_encode(load(x, dtype, ld, line, 32 * b + j), e, rnd, seed, i));
+                }
+            }
+        }
+    } else {
+        if (end > cols)
+            end = cols;
+#pragma omp parallel for schedule(static)
+        for (line = begin; line < end; line++) {
+            int64_t b;
+            for (b = 0; b < rows / 32; b++) {
+                float amax_b = 0.0f;
+                int j, e;
+                for (j = 0; j < 32; j++) {
+                    float a = fabsf(load(x, dtype, ld, 32 * b + j, line));
+                    if (a > amax_b)
+                        amax_b = a;
+                }
+                e = ora_mx_scale_exp(amax_b);
+                scales[line * (rows / 32) + b] = (uint8_t)(e + 127);
+                for (j = 0; j < 32; j++) {
+                    uint64_t i = (uint64_t)line * rows + 32 * b + j;
+                    put_nibble(codes, i, mx_encode(load(x, dtype, ld, 32 * b + j, line), e, rnd, seed, i));
+                }
+            }
+        }
+    }
+    return 0;
+}
+
+/* Dequantize n x k MXFP4 codes (k contiguous) to FP64: e2m1(code) * 2^(s - 127),
+ * scales [n][k/32].  Exact. */
+void ora_mx_dequant(int64_t n, int64_t k, const uint8_t *codes, const uint8_t *scales, double *out)
+{
+    int64_t r, c;
+    for (r = 0; r < n; r++)
+        for (c = 0; c < k; c++) {
+            int code = (codes[(r * k + c) >> 1] >> (((r * k + c) & 1) * 4)) & 15;
+            int s = scales[r * (k / 32) + c / 32];
+            out[r * k + c] = ldexp(ora_e2m1_value(code), s - 127);
+        }
 }
 
 /* ------------------------------------------------------------------ */

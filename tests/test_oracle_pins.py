@@ -453,3 +453,96 @@ def test_gemm_on_dequantized_operands_is_exact_rational(ora):
         for n in range(0, 16, 3):
             exact = sum(Fraction(A[m, k]) * Fraction(B[n, k]) for k in range(32))
             assert Fraction(C[m, n]) == exact
+
+
+# ------------------------------------------------ MXFP4, the comparison format
+# [NV-SUM] parts 1-2: blocks of 32, power-of-two (UE8M0) scales; the shared
+# exponent rule is the OCP MX v1.0 conversion (floor(log2 max) - 2 for E2M1).
+def test_mx_scale_exponent_closed_form(ora):
+    for k in range(-120, 126):
+        for m in (1.0, 1.25, 1.5, 1.999):
+            a = f32(m * 2.0 ** k)
+            assert ora.mx_scale_exp(a) == k - 2
+    assert ora.mx_scale_exp(0.0) == -127                      # all-zero block: smallest scale
+    assert ora.mx_scale_exp(f32(2.0 ** -140)) == -127          # clamped to the E8M0 range
+    assert ora.mx_scale_exp(3.4028234663852886e38) == 125
+
+
+def test_mx_block_roundtrip_of_representable_values(ora):
+    """A block whose values are E2M1 magnitudes times 2^e, with 4 or 6 as its
+    largest magnitude, is reproduced exactly (the scale is 2^e)."""
+    rng = np.random.default_rng(31)
+    for e in (-20, -3, 0, 5, 60):
+        for top in (4.0, 6.0):
+            v = rng.choice(E2M1[:7 if top == 6.0 else 7], (16, 32)) * rng.choice([-1, 1], (16, 32))
+            v[:, 0] = top
+            x = (v * 2.0 ** e).astype(np.float32)
+            q = ora.mx_quantize(x, ora.ROW_1D)
+            assert (q["scales"] == e + 127).all()
+            assert np.array_equal(ora.mx_dequant(q["codes"], q["scales"]), x.astype(np.float64))
+
+
+def test_mx_saturates_near_the_block_max(ora):
+    """The power-of-two scale maps the block max into [4, 8), so a max in
+    (6, 8) times 2^e is clamped to 6 * 2^e: relative error up to 1/4 -- the
+    saturation the pages attribute to MXFP4 -- where NVFP4's E4M3 block scale
+    keeps the block max within 1/16."""
+    worst_mx = worst_nv = 0.0
+    for amax in np.linspace(6.01, 7.99, 40, dtype=np.float32):
+        x = np.zeros((16, 32), np.float32)
+        x[:, 0] = amax
+        x[:, 1] = 1.0
+        d = ora.mx_dequant(*ora.mx_quantize(x, ora.ROW_1D).values())
+        assert d[0, 0] == 6.0 and d[0, 1] == 1.0
+        worst_mx = max(worst_mx, abs(d[0, 0] - amax) / amax)
+        q = ora.quantize(x, ora.ROW_1D)
+        dn = ora.dequant(q["codes"], q["scales"], q["tensor_scale"])
+        worst_nv = max(worst_nv, abs(dn[0, 0] - amax) / amax)
+    assert 0.24 < worst_mx < 0.25 and worst_nv <= 1 / 16
+
+
+def test_mx_layouts_and_zero_blocks(ora):
+    rng = np.random.default_rng(32)
+    x = (rng.standard_normal((64, 96)) * np.exp(rng.uniform(-8, 8, (64, 96)))).astype(np.float32)
+    x[:, 32:64] = 0.0
+    row = ora.mx_quantize(x, ora.ROW_1D)
+    assert (row["scales"][:, 1] == 0).all() and not row["codes"][:, 16:32].any()
+    col = ora.mx_quantize(x, ora.COL_1D)
+    colT = ora.mx_quantize(np.ascontiguousarray(x.T), ora.ROW_1D)
+    assert np.array_equal(col["codes"], colT["codes"]) and np.array_equal(col["scales"], colT["scales"])
+    # every element is the nearest E2M1 point of x / 2^e, ties to the even
+    # index, clamped at 6 (brute force over the 8 magnitudes)
+    d = ora.mx_dequant(row["codes"], row["scales"])
+    e = row["scales"].astype(np.int64).repeat(32, axis=1) - 127
+    y = x.astype(np.float64) / np.exp2(e)
+    grid = np.array(E2M1)
+    dist = np.abs(np.minimum(np.abs(y), 6.0)[..., None] - grid)
+    best = dist.min(-1, keepdims=True)
+    ties = dist == best
+    idx = np.where(ties.sum(-1) > 1, np.argmax(ties & (np.arange(8) % 2 == 0), -1), dist.argmin(-1))
+    assert np.array_equal(d / np.exp2(e), grid[idx] * np.sign(y))
+
+
+def test_mx_sr_is_unbiased(ora):
+    x = np.full((16, 32), 0.3, np.float32)
+    x[:, 0] = 6.0
+    means = []
+    for seed in range(200):
+        d = ora.mx_dequant(*ora.mx_quantize(x, ora.ROW_1D, ora.SR, seed).values())
+        means.append(d[:, 1:].mean())
+    m = float(np.mean(means))
+    sd = 0.5 * math.sqrt(0.6 * 0.4) / math.sqrt(200 * 16 * 31)
+    assert abs(m - 0.3) < 5 * sd
+
+
+def test_nvfp4_beats_mxfp4_on_gaussian_blocks(ora):
+    """The pages' comparison (NVFP4 needs fewer tokens than MXFP4 because of its
+    finer scales): on the same N(0,1) tensor NVFP4's mean squared quantization
+    error is below MXFP4's."""
+    x = synth.normal(33, (256, 1024))
+    q = ora.quantize(x, ora.ROW_1D)
+    nv = ora.dequant(q["codes"], q["scales"], q["tensor_scale"])
+    mx = ora.mx_dequant(*ora.mx_quantize(x, ora.ROW_1D).values())
+    err_nv = float(((nv - x) ** 2).mean())
+    err_mx = float(((mx - x) ** 2).mean())
+    assert err_nv < 0.8 * err_mx
