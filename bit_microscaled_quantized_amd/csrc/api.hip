@@ -2,6 +2,7 @@
 // argument validation on the host, then asynchronous launches on the caller's
 // stream.  No allocation; the only state is a per-device cache of the compute
 // unit count.
+#include "../../include/mxfp4.h"
 #include "../../include/nvfp4.h"
 #include "nvfp4_launch.hpp"
 
@@ -124,6 +125,43 @@ nvfp4_status nvfp4_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
                                     b_scale_rowdiv, b_tensor_scale, c, ldc, beta == 1.0f ? 1 : 0,
                                     workspace, workspace == nullptr ? 0 : workspace_bytes,
                                     static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? NVFP4_OK : NVFP4_EHIP;
+}
+
+nvfp4_status mxfp4_quantize(const void* x, int dt, int64_t rows, int64_t cols, int64_t ld_x,
+                            int layout, int rnd, uint64_t seed, uint8_t* codes, uint8_t* scales,
+                            void* stream) {
+  if (codes == nullptr || scales == nullptr) return NVFP4_EINVAL;
+  if (layout != NVFP4_ROW_1D && layout != NVFP4_COL_1D) return NVFP4_EINVAL;
+  if (rnd != NVFP4_RNE && rnd != NVFP4_SR) return NVFP4_EINVAL;
+  nvfp4_status st = check_tensor(x, dt, rows, cols, ld_x);
+  if (st != NVFP4_OK) return st;
+  if ((layout == NVFP4_ROW_1D && cols % 32 != 0) || (layout == NVFP4_COL_1D && rows % 32 != 0))
+    return NVFP4_ESHAPE;
+  if (!aligned16(codes) || !aligned4(scales)) return NVFP4_EALIGN;
+  hipError_t e = nvfp4::launch_mx_quantize(x, dt, rows, cols, ld_x, layout, rnd, seed, codes, scales,
+                                           static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? NVFP4_OK : NVFP4_EHIP;
+}
+
+nvfp4_status mxfp4_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
+                        const uint8_t* a_scales, const uint8_t* b_codes, const uint8_t* b_scales,
+                        float* c, int64_t ldc, float beta, void* workspace, int64_t workspace_bytes,
+                        void* stream) {
+  if (a_codes == nullptr || a_scales == nullptr || b_codes == nullptr || b_scales == nullptr ||
+      c == nullptr)
+    return NVFP4_EINVAL;
+  if (beta != 0.0f && beta != 1.0f) return NVFP4_EINVAL;
+  nvfp4_status st = check_gemm_shape(M, N, K);
+  if (st != NVFP4_OK) return st;
+  if (K % 128 != 0 || ldc < N || workspace_bytes < 0) return NVFP4_ESHAPE;
+  if (!aligned16(a_codes) || !aligned16(b_codes) || !aligned4(a_scales) || !aligned4(b_scales) ||
+      !aligned16(c) || ldc % 4 != 0 || !aligned16(workspace))
+    return NVFP4_EALIGN;
+  hipError_t e = nvfp4::launch_mx_gemm(M, N, K, a_codes, a_scales, b_codes, b_scales, c, ldc,
+                                       beta == 1.0f ? 1 : 0, workspace,
+                                       workspace == nullptr ? 0 : workspace_bytes,
+                                       static_cast<hipStream_t>(stream));
   return e == hipSuccess ? NVFP4_OK : NVFP4_EHIP;
 }
 

@@ -28,7 +28,16 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
                        int64_t ldc, int accumulate, void* workspace, int64_t workspace_bytes,
                        hipStream_t s);
 
-// Workspace bytes launch_gemm uses for this shape on the current device
+hipError_t launch_mx_quantize(const void* x, int dt, int64_t rows, int64_t cols, int64_t ld,
+                              int layout, int rnd, uint64_t seed, uint8_t* codes, uint8_t* scales,
+                              hipStream_t s);
+
+hipError_t launch_mx_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
+                          const uint8_t* a_scales, const uint8_t* b_codes, const uint8_t* b_scales,
+                          float* c, int64_t ldc, int accumulate, void* workspace,
+                          int64_t workspace_bytes, hipStream_t s);
+
+// Workspace bytes launch_gemm (and launch_mx_gemm) uses for this shape on the current device
 // (0: no split).
 int64_t gemm_workspace_size(int64_t M, int64_t N, int64_t K);
 

@@ -20,7 +20,7 @@ NVFP4_RNE, NVFP4_SR = 0, 1
 NVFP4_ROW_1D, NVFP4_COL_1D, NVFP4_TILE_2D = 0, 1, 2
 
 EXPORTED = ("nvfp4_quantize", "nvfp4_rht_quantize", "nvfp4_quantize_row_rht", "nvfp4_gemm",
-            "nvfp4_gemm_workspace_size", "nvfp4_status_str")
+            "nvfp4_gemm_workspace_size", "nvfp4_status_str", "mxfp4_quantize", "mxfp4_gemm")
 
 _lib = None
 
@@ -53,6 +53,10 @@ def load_library():
     L.nvfp4_quantize_row_rht.argtypes = [vp, i32, i64, i64, i64, i32, u64, vp, vp, vp, vp, u32, i32,
                                          u64, vp, vp, vp, vp, vp]
     L.nvfp4_quantize_row_rht.restype = i32
+    L.mxfp4_quantize.argtypes = [vp, i32, i64, i64, i64, i32, i32, u64, vp, vp, vp]
+    L.mxfp4_quantize.restype = i32
+    L.mxfp4_gemm.argtypes = [i64, i64, i64, vp, vp, vp, vp, vp, i64, f32, vp, i64, vp]
+    L.mxfp4_gemm.restype = i32
     L.nvfp4_gemm.argtypes = [i64, i64, i64, vp, vp, vp, vp, vp, i32, vp, vp, i64, f32, vp, i64, vp]
     L.nvfp4_gemm.restype = i32
     L.nvfp4_gemm_workspace_size.argtypes = [i64, i64, i64, ctypes.POINTER(i64)]
@@ -140,3 +144,22 @@ def nvfp4_gemm_workspace_size(M, N, K) -> int:
     _check("nvfp4_gemm_workspace_size",
            load_library().nvfp4_gemm_workspace_size(M, N, K, ctypes.byref(out)), True)
     return out.value
+
+
+def mxfp4_quantize(x, dt, rows, cols, ld_x, layout, rnd, seed, codes, scales, stream=None,
+                   raise_on_error=True) -> int:
+    st = load_library().mxfp4_quantize(_addr(x), dt, rows, cols, ld_x, layout, rnd,
+                                       seed & (2 ** 64 - 1), _addr(codes), _addr(scales),
+                                       _stream(stream))
+    return _check("mxfp4_quantize", st, raise_on_error)
+
+
+def mxfp4_gemm(M, N, K, a_codes, a_scales, b_codes, b_scales, c, ldc, beta, workspace=None,
+               workspace_bytes=None, stream=None, raise_on_error=True) -> int:
+    if workspace_bytes is None:
+        workspace_bytes = 0 if workspace is None or isinstance(workspace, int) else \
+            workspace.numel() * workspace.element_size()
+    st = load_library().mxfp4_gemm(M, N, K, _addr(a_codes), _addr(a_scales), _addr(b_codes),
+                                   _addr(b_scales), _addr(c), ldc, float(beta), _addr(workspace),
+                                   int(workspace_bytes), _stream(stream))
+    return _check("mxfp4_gemm", st, raise_on_error)

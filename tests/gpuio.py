@@ -105,6 +105,36 @@ def gpu_quantize_row_rht(x: np.ndarray, sign_mask: int, row_rnd: int, row_seed: 
     return row, rht
 
 
+def gpu_mx_quantize(x: np.ndarray, layout: int, rnd: int = 0, seed: int = 0) -> dict:
+    """mxfp4_quantize of x (rows x cols; bf16 bits or fp32) on the GPU."""
+    torch = torch_cuda()
+    rows, cols = x.shape
+    xd = to_dev(x)
+    u8 = dict(dtype=torch.uint8, device="cuda")
+    if layout == nv.NVFP4_COL_1D:
+        codes = torch.empty((cols, rows // 2), **u8)
+        scales = torch.empty((cols, rows // 32), **u8)
+    else:
+        codes = torch.empty((rows, cols // 2), **u8)
+        scales = torch.empty((rows, cols // 32), **u8)
+    nv.mxfp4_quantize(xd, dtype_code(x), rows, cols, cols, layout, rnd, seed, codes, scales)
+    torch.cuda.synchronize()
+    return dict(codes=host(codes), scales=host(scales), dev=dict(codes=codes, scales=scales))
+
+
+def gpu_mx_gemm(M, N, K, a: dict, b: dict, c0: np.ndarray | None = None, beta: float = 0.0,
+                workspace="auto") -> np.ndarray:
+    torch = torch_cuda()
+    c = torch.zeros((M, N), dtype=torch.float32, device="cuda") if c0 is None else \
+        to_dev(np.ascontiguousarray(c0, dtype=np.float32))
+    if isinstance(workspace, str):
+        workspace = nv.nvfp4_gemm_workspace_size(M, N, K)
+    ws = torch.full((workspace // 4,), float("nan"), dtype=torch.float32, device="cuda") if workspace else None
+    nv.mxfp4_gemm(M, N, K, a["codes"], a["scales"], b["codes"], b["scales"], c, N, beta, workspace=ws)
+    torch.cuda.synchronize()
+    return host(c)
+
+
 def gpu_gemm(M, N, K, a: dict, b: dict, b_rowdiv: int, c0: np.ndarray | None = None,
              beta: float = 0.0, workspace="auto") -> np.ndarray:
     """C = beta*C0 + A.B^T from device-resident quantize outputs a, b (dicts with

@@ -16,8 +16,10 @@ FAKE = 1 << 20  # a 16-byte aligned non-null address that is never dereferenced
 
 
 def declared_symbols():
-    text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:nvfp4_status|const char \*)\s*(nvfp4_\w+)\s*\(", text, re.M)))
+    text = "".join(open(os.path.join(os.path.dirname(HEADER), f)).read()
+                   for f in sorted(os.listdir(os.path.dirname(HEADER))) if f.endswith(".h"))
+    return sorted(set(re.findall(r"^\s*(?:nvfp4_status|const char \*)\s*((?:nvfp4|mxfp4)_\w+)\s*\(",
+                                 text, re.M)))
 
 
 def test_header_declares_the_entry_points():
@@ -31,8 +33,36 @@ def test_library_exports_every_declared_symbol():
     out = subprocess.run(["nm", "-D", "--defined-only", nv.library_path()], capture_output=True,
                          text=True, check=True).stdout
     exported_c = sorted({line.split()[-1] for line in out.splitlines()
-                         if line.split()[-1].startswith("nvfp4_")})
+                         if line.split()[-1].startswith(("nvfp4_", "mxfp4_"))})
     assert exported_c == declared_symbols()
+
+
+def test_mxfp4_argument_errors():
+    def q(**kw):
+        args = dict(x=FAKE, dt=0, rows=32, cols=64, ld_x=64, layout=0, rnd=0, seed=0, codes=FAKE,
+                    scales=FAKE)
+        args.update(kw)
+        return nv.mxfp4_quantize(**args, stream=0, raise_on_error=False)
+    assert q(codes=None) == b.NVFP4_EINVAL
+    assert q(layout=2) == b.NVFP4_EINVAL                 # no 2D layout for MXFP4
+    assert q(rnd=3) == b.NVFP4_EINVAL
+    assert q(cols=48, ld_x=48) == b.NVFP4_ESHAPE         # row blocks need cols % 32
+    assert q(layout=1, rows=48) == b.NVFP4_ESHAPE        # column blocks need rows % 32
+    assert q(codes=FAKE + 4) == b.NVFP4_EALIGN
+    assert q(scales=FAKE + 2) == b.NVFP4_EALIGN
+
+    def g(**kw):
+        args = dict(M=256, N=256, K=256, a_codes=FAKE, a_scales=FAKE, b_codes=FAKE, b_scales=FAKE,
+                    c=FAKE, ldc=256, beta=0.0)
+        args.update(kw)
+        return nv.mxfp4_gemm(**args, stream=0, raise_on_error=False)
+    assert g(b_scales=None) == b.NVFP4_EINVAL
+    assert g(beta=2.0) == b.NVFP4_EINVAL
+    assert g(K=64) == b.NVFP4_ESHAPE                     # K must be a multiple of 128
+    assert g(M=8) == b.NVFP4_ESHAPE
+    assert g(ldc=100) == b.NVFP4_ESHAPE
+    assert g(a_scales=FAKE + 1) == b.NVFP4_EALIGN
+    assert g(c=FAKE + 8) == b.NVFP4_EALIGN
 
 
 def test_status_strings():
