@@ -415,7 +415,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mxfp4(
   const int cchunk_e = (lane & 7) ^ (crow >> 1);
   const int cchunk_o = (lane & 7) ^ (4 + (crow >> 1));
   const int sdw = lane & 1;
-  auto issue_stage = [&](int kt, uint8_t* st) {
+  auto issue_stage = [&](int kt, uint8_t* st) __attribute__((always_inline)) {
     const int64_t coff_e = min((int64_t)kt * (BKS / 2) + 16 * cchunk_e, kb - 16);
     const int64_t coff_o = min((int64_t)kt * (BKS / 2) + 16 * cchunk_o, kb - 16);
     const int64_t soff = min((int64_t)kt * (BKS / 32) + 4 * sdw, ks - 4);
@@ -436,7 +436,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mxfp4(
   // In a stage that ends past K (K is a multiple of 128, so only its second
   // half can be past the end), zero the codes of the last 128 K-elements
   // (chunks 4..7) of every row: exact zero contributions whatever the scale.
-  auto fix_partial = [&](int kt, uint8_t* st) {
+  auto fix_partial = [&](int kt, uint8_t* st) __attribute__((always_inline)) {
     if ((int64_t)(kt + 1) * BKS <= K) return;
     const int f = (tid >> 1) & 7;  // row tid of A and of B
 #pragma unroll
@@ -450,7 +450,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mxfp4(
   const int rowa = wm * 128 + lr;
   const int rowb = wn * 128 + lr;
   const int fsw = (lr >> 1) & 7;
-  auto read_step = [&](const uint8_t* st, int s, uint4* ca, uint4* cb) {
+  auto read_step = [&](const uint8_t* __restrict__ st, int s, uint4* ca, uint4* cb) __attribute__((always_inline)) {
     const int sw = ((2 * s + h) ^ fsw) << 4;
 #pragma unroll
     for (int i = 0; i < 4; i++) {
@@ -460,7 +460,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mxfp4(
   };
   // this lane's scale dword for each of its rows: byte s = block 2s + h
   const uint32_t psel = h ? 0x07050301u : 0x06040200u;
-  auto read_scales = [&](const uint8_t* st, uint32_t* sa, uint32_t* sb) {
+  auto read_scales = [&](const uint8_t* __restrict__ st, uint32_t* sa, uint32_t* sb) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < 4; i++) {
       const uint2 wa = *reinterpret_cast<const uint2*>(st + MX_OFF_SA + (rowa + 32 * i) * 8);
@@ -511,6 +511,12 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mxfp4(
     MX_MFMAS(1, 1)
     read_step(cur, 3, qa[1], qb[1]);
     MX_MFMAS(0, 2)
+    // keep these MFMAs above the barrier (the compiler would otherwise sink
+    // them past it, leaving the matrix core idle through the barrier wait)
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+      for (int j = 0; j < 4; j++) asm volatile("" : "+a"(acc[i][j]));
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (more) {
