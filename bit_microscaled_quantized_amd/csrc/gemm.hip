@@ -363,8 +363,7 @@ constexpr int MX_LDS_BYTES = 2 * MX_STAGE_BYTES;                     // 136 KB
 typedef int int4v_t __attribute__((ext_vector_type(4)));
 typedef int int8v_t __attribute__((ext_vector_type(8)));
 
-__device__ __forceinline__ int8v_t fp4_operand(const uint4& q) {
-  const int4v_t v = {(int)q.x, (int)q.y, (int)q.z, (int)q.w};
+__device__ __forceinline__ int8v_t fp4_operand(const int4v_t& v) {
   return __builtin_shufflevector(v, v, 0, 1, 2, 3, -1, -1, -1, -1);  // FP4 reads 4 registers
 }
 }  // namespace
@@ -450,12 +449,15 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mxfp4(
   const int rowa = wm * 128 + lr;
   const int rowb = wn * 128 + lr;
   const int fsw = (lr >> 1) & 7;
-  auto read_step = [&](const uint8_t* __restrict__ st, int s, uint4* ca, uint4* cb) __attribute__((always_inline)) {
+  // (native vector loads: one load per fragment whose address derives from
+  // the stage buffer alone, so it keeps that buffer's alias scope and is not
+  // made to wait for the prefetch into the other buffer)
+  auto read_step = [&](const uint8_t* __restrict__ st, int s, int4v_t* ca, int4v_t* cb) __attribute__((always_inline)) {
     const int sw = ((2 * s + h) ^ fsw) << 4;
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-      ca[i] = *reinterpret_cast<const uint4*>(st + (rowa + 32 * i) * 128 + sw);
-      cb[i] = *reinterpret_cast<const uint4*>(st + OFF_B + (rowb + 32 * i) * 128 + sw);
+      ca[i] = *reinterpret_cast<const int4v_t*>(st + (rowa + 32 * i) * 128 + sw);
+      cb[i] = *reinterpret_cast<const int4v_t*>(st + OFF_B + (rowb + 32 * i) * 128 + sw);
     }
   };
   // this lane's scale dword for each of its rows: byte s = block 2s + h
@@ -478,7 +480,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mxfp4(
 #pragma unroll
       for (int r = 0; r < 16; r++) acc[i][j][r] = 0.0f;
 
-  uint4 qa[2][4], qb[2][4];
+  int4v_t qa[2][4], qb[2][4];
   uint32_t sa[2][4], sb[2][4];  // scale dwords of the current / next stage
 
 // 16 MFMAs of step S on fragment buffer P; the scheduling barrier keeps the
