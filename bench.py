@@ -18,6 +18,11 @@ dominant kernel (the GEMM) from HIP events around every GEMM launch in the
 timed steps.  `cpu_baseline` times the CPU oracle on the same step (all 8192
 tokens by default; --cpu-sample-tokens bounds it).
 
+`components.mxfp4` times the comparison format on the same tensors after the
+NVFP4 step (not part of `value`): MXFP4 (32-element blocks, E8M0 scales, no
+tensor scale, no Hadamard) row and column quantization of W, X (RNE) and dY
+(SR), then the same three GEMMs on the block-scaled FP4 matrix instruction.
+
     python bench.py [--steps K] [--warmup W] [--gpus 1]
 """
 from __future__ import annotations
@@ -46,14 +51,20 @@ TOKENS, D_IN, D_OUT = 8192, 5120, 20480
 #   bench.py --steps 3 --warmup 1 --no-cpu-baseline --copy-probe-mib 1024
 # FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0 (KiB -> bytes): the factors are what the
 # same counters read for the 1 GiB read + 1 GiB write elementwise probe
-# (FETCH_SIZE 512 MiB, WRITE_SIZE 1024 MiB).  Valid only for the gemm.hip
-# source with this hash; any other source reports null.
-GEMM_TRAFFIC = dict(src_sha256="f7cdfac03b59402b6a492bd5c5780e714ceb0b07ac150cf74eaedf62f83fad16",
-                    bytes_per_launch=1.1573e+09, fetch_bytes=7.0980e+08, write_bytes=4.4755e+08)
+# (FETCH_SIZE 512 MiB, WRITE_SIZE 1024 MiB).  Valid only for the kernel
+# sources (gemm.hip + gemm_tiling.hpp) with this hash; any other source
+# reports null.
+GEMM_TRAFFIC = dict(src_sha256="a912034815f6f042db30e5a8111380afefb5ccfac7baf0515980562d9bdb811f",
+                    bytes_per_launch=1.1573e+09, fetch_bytes=7.0976e+08, write_bytes=4.4749e+08)
+GEMM_SOURCES = ("gemm.hip", "gemm_tiling.hpp")
 
 
-def _src_sha(path: str) -> str:
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()
+def gemm_src_sha() -> str:
+    """SHA-256 over the NVFP4 GEMM kernel's sources, in GEMM_SOURCES order."""
+    h = hashlib.sha256()
+    for f in GEMM_SOURCES:
+        h.update(open(os.path.join(ROOT, "bit_microscaled_quantized_amd", "csrc", f), "rb").read())
+    return h.hexdigest()
 
 
 def parse():
@@ -160,7 +171,86 @@ def gpu_bench(inp, steps, warmup):
     per = {}
     for name, a, b in rec:
         per.setdefault(name, []).append(a.elapsed_time(b))
-    return wall / steps, {k: float(np.mean(v)) for k, v in per.items()}
+    per = {k: float(np.mean(v)) for k, v in per.items()}
+    mx = mx_bench(x, w, dy, s_row, s_col, steps, warmup)
+    return wall / steps, per, mx
+
+
+def mx_quantize_bytes():
+    """Algorithmic bytes of each MXFP4 quantize call of the comparison step:
+    bf16 input read once, codes (0.5 B/elem) and E8M0 scales (1/32 B/elem)
+    written."""
+    def one(n):
+        return n * 2 + n // 2 + n // 32
+    T, I, O = TOKENS, D_IN, D_OUT
+    return dict(w_row=one(O * I), w_col=one(O * I), x_row=one(T * I), x_col=one(T * I),
+                dy_row_sr=one(T * O), dy_col_sr=one(T * O))
+
+
+def mx_bench(x, w, dy, s_row, s_col, steps, warmup):
+    """The MXFP4 comparison step on the same device tensors: each of the six
+    quantize calls and three GEMMs timed with HIP events on the current
+    stream, averaged over `steps` steps after `warmup` untimed ones."""
+    import torch
+    import bit_microscaled_quantized_amd as nv
+    dev = x.device
+    T, I, O = TOKENS, D_IN, D_OUT
+    bf = nv.NVFP4_BF16
+    u8 = dict(dtype=torch.uint8, device=dev)
+
+    def buf(rows, cols):  # codes and scales of `rows` lines of `cols` elements
+        return torch.empty((rows, cols // 2), **u8), torch.empty((rows, cols // 32), **u8)
+    w_r, w_c = buf(O, I), buf(I, O)
+    x_r, x_c = buf(T, I), buf(I, T)
+    d_r, d_c = buf(T, O), buf(O, T)
+    y = torch.empty((T, O), dtype=torch.float32, device=dev)
+    dx = torch.empty((T, I), dtype=torch.float32, device=dev)
+    dw = torch.empty((O, I), dtype=torch.float32, device=dev)
+    ws = torch.empty((max(nv.nvfp4_gemm_workspace_size(T, O, I), nv.nvfp4_gemm_workspace_size(T, I, O),
+                          nv.nvfp4_gemm_workspace_size(O, I, T), 4) // 4,), dtype=torch.float32, device=dev)
+    R, C, RNE, SR = nv.NVFP4_ROW_1D, nv.NVFP4_COL_1D, nv.NVFP4_RNE, nv.NVFP4_SR
+    calls = [
+        ("w_row", lambda: nv.mxfp4_quantize(w, bf, O, I, I, R, RNE, 0, *w_r)),
+        ("w_col", lambda: nv.mxfp4_quantize(w, bf, O, I, I, C, RNE, 0, *w_c)),
+        ("x_row", lambda: nv.mxfp4_quantize(x, bf, T, I, I, R, RNE, 0, *x_r)),
+        ("x_col", lambda: nv.mxfp4_quantize(x, bf, T, I, I, C, RNE, 0, *x_c)),
+        ("gemm_fprop", lambda: nv.mxfp4_gemm(T, O, I, *x_r, *w_r, y, O, 0.0, workspace=ws)),
+        ("dy_row_sr", lambda: nv.mxfp4_quantize(dy, bf, T, O, O, R, SR, s_row, *d_r)),
+        ("dy_col_sr", lambda: nv.mxfp4_quantize(dy, bf, T, O, O, C, SR, s_col, *d_c)),
+        ("gemm_dgrad", lambda: nv.mxfp4_gemm(T, I, O, *d_r, *w_c, dx, I, 0.0, workspace=ws)),
+        ("gemm_wgrad", lambda: nv.mxfp4_gemm(O, I, T, *d_c, *x_c, dw, I, 0.0, workspace=ws)),
+    ]
+    for _ in range(warmup):
+        for _, fn in calls:
+            fn()
+    torch.cuda.synchronize()
+    rec = []
+    for _ in range(steps):
+        for name, fn in calls:
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            rec.append((name, a, b))
+    torch.cuda.synchronize()
+    per = {}
+    for name, a, b in rec:
+        per.setdefault(name, []).append(a.elapsed_time(b))
+    per = {k: float(np.mean(v)) for k, v in per.items()}
+    qb = mx_quantize_bytes()
+    q_ms = sum(per[k] for k in qb)
+    g_ms = float(np.mean([per["gemm_fprop"], per["gemm_dgrad"], per["gemm_wgrad"]]))
+    g_tf = 2.0 * T * I * O / (g_ms * 1e-3) / 1e12
+    q_gbs = sum(qb.values()) / (q_ms * 1e-3) / 1e9
+    return {
+        "quantize_GBps": round(q_gbs, 1),
+        "quantize_frac_hbm": round(q_gbs / HBM_PEAK_GBS, 4),
+        "gemm_TFLOPs": round(g_tf, 2),
+        "gemm_frac_mfma_fp4": round(g_tf / MFMA_FP4_PEAK, 4),
+        "step_ms": round(sum(per.values()), 4),
+        "per_call_ms": {k: round(v, 4) for k, v in per.items()},
+        "quantize_bytes": qb,
+    }
 
 
 def cpu_baseline(inp, tokens):
@@ -201,7 +291,7 @@ def main():
               "(the sharded path is a design, not built)", file=sys.stderr)
         sys.exit(2)
     inp = make_inputs()
-    ms_step, per = gpu_bench(inp, args.steps, args.warmup)
+    ms_step, per, mx = gpu_bench(inp, args.steps, args.warmup)
     if args.copy_probe_mib:
         import torch
         # an elementwise kernel (not a DMA copy, which no counter sees) that
@@ -225,8 +315,7 @@ def main():
     value = 3 * gemm_flops / (ms_step * 1e-3) / 1e12
 
     traffic = None
-    if GEMM_TRAFFIC is not None and GEMM_TRAFFIC["src_sha256"] == _src_sha(
-            os.path.join(ROOT, "bit_microscaled_quantized_amd", "csrc", "gemm.hip")):
+    if GEMM_TRAFFIC is not None and GEMM_TRAFFIC["src_sha256"] == gemm_src_sha():
         traffic = GEMM_TRAFFIC["bytes_per_launch"]
 
     out = {
@@ -267,6 +356,7 @@ def main():
             "gemm_frac_mfma_fp4": round(gemm_tflops / MFMA_FP4_PEAK, 4),
             "per_call_ms": {k: round(v, 4) for k, v in per.items()},
             "quantize_bytes": qb,
+            "mxfp4": mx,
         },
     }
     if not args.no_cpu_baseline:
