@@ -29,6 +29,31 @@ nvfp4_status check_gemm_shape(int64_t M, int64_t N, int64_t K) {
   return NVFP4_OK;
 }
 
+nvfp4_status gemm_common(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
+                         const uint8_t* a_scales, const float* a_tensor_scale,
+                         const uint8_t* b_codes, const uint8_t* b_scales, int32_t b_scale_rowdiv,
+                         const float* b_tensor_scale, void* c, int c_bf16, int64_t ldc, float beta,
+                         void* workspace, int64_t workspace_bytes, void* stream) {
+  if (a_codes == nullptr || a_scales == nullptr || a_tensor_scale == nullptr ||
+      b_codes == nullptr || b_scales == nullptr || b_tensor_scale == nullptr || c == nullptr)
+    return NVFP4_EINVAL;
+  if (b_scale_rowdiv != 1 && b_scale_rowdiv != 16) return NVFP4_EINVAL;
+  if (beta != 0.0f && beta != 1.0f) return NVFP4_EINVAL;
+  nvfp4_status st = check_gemm_shape(M, N, K);
+  if (st != NVFP4_OK) return st;
+  if (ldc < N || workspace_bytes < 0) return NVFP4_ESHAPE;
+  if (!aligned16(a_codes) || !aligned16(b_codes) || !aligned4(a_scales) || !aligned4(b_scales) ||
+      !aligned4(a_tensor_scale) || !aligned4(b_tensor_scale) || !aligned16(c) ||
+      ldc % (c_bf16 ? 8 : 4) != 0 || !aligned16(workspace))
+    return NVFP4_EALIGN;
+  hipError_t e = nvfp4::launch_gemm(M, N, K, a_codes, a_scales, a_tensor_scale, b_codes, b_scales,
+                                    b_scale_rowdiv, b_tensor_scale, c, c_bf16, ldc,
+                                    beta == 1.0f ? 1 : 0, workspace,
+                                    workspace == nullptr ? 0 : workspace_bytes,
+                                    static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? NVFP4_OK : NVFP4_EHIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -109,22 +134,37 @@ nvfp4_status nvfp4_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
                         const uint8_t* b_codes, const uint8_t* b_scales, int32_t b_scale_rowdiv,
                         const float* b_tensor_scale, float* c, int64_t ldc, float beta,
                         void* workspace, int64_t workspace_bytes, void* stream) {
-  if (a_codes == nullptr || a_scales == nullptr || a_tensor_scale == nullptr ||
-      b_codes == nullptr || b_scales == nullptr || b_tensor_scale == nullptr || c == nullptr)
+  return gemm_common(M, N, K, a_codes, a_scales, a_tensor_scale, b_codes, b_scales, b_scale_rowdiv,
+                     b_tensor_scale, c, 0, ldc, beta, workspace, workspace_bytes, stream);
+}
+
+nvfp4_status nvfp4_gemm_bf16(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
+                             const uint8_t* a_scales, const float* a_tensor_scale,
+                             const uint8_t* b_codes, const uint8_t* b_scales,
+                             int32_t b_scale_rowdiv, const float* b_tensor_scale, uint16_t* c,
+                             int64_t ldc, float beta, void* workspace, int64_t workspace_bytes,
+                             void* stream) {
+  return gemm_common(M, N, K, a_codes, a_scales, a_tensor_scale, b_codes, b_scales, b_scale_rowdiv,
+                     b_tensor_scale, c, 1, ldc, beta, workspace, workspace_bytes, stream);
+}
+
+nvfp4_status nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, int32_t scale_rowdiv,
+                              const float* tensor_scale, int64_t rows, int64_t cols, int out_dt,
+                              void* out, int64_t ld_out, void* stream) {
+  if (codes == nullptr || scales == nullptr || tensor_scale == nullptr || out == nullptr)
     return NVFP4_EINVAL;
-  if (b_scale_rowdiv != 1 && b_scale_rowdiv != 16) return NVFP4_EINVAL;
-  if (beta != 0.0f && beta != 1.0f) return NVFP4_EINVAL;
-  nvfp4_status st = check_gemm_shape(M, N, K);
-  if (st != NVFP4_OK) return st;
-  if (ldc < N || workspace_bytes < 0) return NVFP4_ESHAPE;
-  if (!aligned16(a_codes) || !aligned16(b_codes) || !aligned4(a_scales) || !aligned4(b_scales) ||
-      !aligned4(a_tensor_scale) || !aligned4(b_tensor_scale) || !aligned16(c) || ldc % 4 != 0 ||
-      !aligned16(workspace))
+  if (scale_rowdiv != 1 && scale_rowdiv != 16) return NVFP4_EINVAL;
+  if (out_dt != NVFP4_BF16 && out_dt != NVFP4_F32) return NVFP4_EINVAL;
+  if (rows <= 0 || cols <= 0 || cols % 16 != 0 || rows % scale_rowdiv != 0 || ld_out < cols)
+    return NVFP4_ESHAPE;
+  if (rows > ((int64_t(1) << 32) - 1) / cols || (rows - 1) * ld_out + cols >= (int64_t(1) << 40))
+    return NVFP4_ESHAPE;
+  const int64_t esize = out_dt == NVFP4_BF16 ? 2 : 4;
+  if (!aligned16(codes) || !aligned4(tensor_scale) || !aligned16(out) || (ld_out * esize) % 16 != 0)
     return NVFP4_EALIGN;
-  hipError_t e = nvfp4::launch_gemm(M, N, K, a_codes, a_scales, a_tensor_scale, b_codes, b_scales,
-                                    b_scale_rowdiv, b_tensor_scale, c, ldc, beta == 1.0f ? 1 : 0,
-                                    workspace, workspace == nullptr ? 0 : workspace_bytes,
-                                    static_cast<hipStream_t>(stream));
+  hipError_t e = nvfp4::launch_dequantize(codes, scales, scale_rowdiv, tensor_scale, rows, cols, out,
+                                          out_dt == NVFP4_BF16 ? 1 : 0, ld_out,
+                                          static_cast<hipStream_t>(stream));
   return e == hipSuccess ? NVFP4_OK : NVFP4_EHIP;
 }
 

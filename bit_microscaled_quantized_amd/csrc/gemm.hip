@@ -90,11 +90,14 @@ __device__ __forceinline__ uint32_t dw(const uint4& q, int i) {
 
 }  // namespace
 
+// OutT: float (FP32 output) or uint16_t (BF16 bits, rounded to nearest even
+// once, after alpha and beta are applied in FP32).
+template <typename OutT>
 __global__ __launch_bounds__(512, 1) void k_gemm_nvfp4(
     int M, int N, int K, const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
     const float* __restrict__ a_ts, const uint8_t* __restrict__ b_codes,
     const uint8_t* __restrict__ b_scales, int b_rowdiv, const float* __restrict__ b_ts,
-    float* __restrict__ c, int64_t ldc, int accumulate, int full_tiles, int split,
+    OutT* __restrict__ c, int64_t ldc, int accumulate, int full_tiles, int split,
     float* __restrict__ partial) {
   extern __shared__ __align__(16) uint8_t lds[];
 
@@ -301,10 +304,10 @@ __global__ __launch_bounds__(512, 1) void k_gemm_nvfp4(
       for (int r = 0; r < 16; r++) {
         const int m = m0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
         if (m < M && n < N) {
-          float* p = c + (int64_t)m * ldc + n;
+          OutT* p = c + (int64_t)m * ldc + n;
           float v = alpha * acc[i][j][r];
-          if (accumulate) v += *p;
-          __builtin_nontemporal_store(v, p);
+          if (accumulate) v += OutElem<OutT>::load(p);
+          OutElem<OutT>::store_nt(p, v);
         }
       }
     }
@@ -313,11 +316,12 @@ __global__ __launch_bounds__(512, 1) void k_gemm_nvfp4(
 // Sum of the S partial tiles of each split tail tile in the order 0 .. S-1,
 // then C = alpha * sum (+ C).  Block (x, t): tail tile t, rows 4x .. 4x + 3;
 // thread: one row, four consecutive columns.
+template <typename OutT>
 __global__ __launch_bounds__(256) void k_gemm_split_reduce(int M, int N, int full_tiles, int split,
                                                            const float* __restrict__ partial,
                                                            const float* __restrict__ a_ts,
                                                            const float* __restrict__ b_ts,
-                                                           float* __restrict__ c, int64_t ldc,
+                                                           OutT* __restrict__ c, int64_t ldc,
                                                            int accumulate) {
   const int t = blockIdx.y;
   int pm, pn;
@@ -333,16 +337,29 @@ __global__ __launch_bounds__(256) void k_gemm_split_reduce(int M, int N, int ful
     v.x += w.x; v.y += w.y; v.z += w.z; v.w += w.w;
   }
   const float alpha = a_ts != nullptr ? a_ts[0] * b_ts[0] : 1.0f;  // null: no tensor scales (MXFP4)
-  float4* dst = reinterpret_cast<float4*>(c + (int64_t)m * ldc + n);
   float4 o = make_float4(alpha * v.x, alpha * v.y, alpha * v.z, alpha * v.w);
-  if (accumulate) {
-    const float4 old = *dst;
-    o.x += old.x; o.y += old.y; o.z += old.z; o.w += old.w;
+  OutT* dst = c + (int64_t)m * ldc + n;
+  if constexpr (sizeof(OutT) == 4) {
+    float4* d4 = reinterpret_cast<float4*>(dst);
+    if (accumulate) {
+      const float4 old = *d4;
+      o.x += old.x; o.y += old.y; o.z += old.z; o.w += old.w;
+    }
+    __builtin_nontemporal_store(o.x, &d4->x);
+    __builtin_nontemporal_store(o.y, &d4->y);
+    __builtin_nontemporal_store(o.z, &d4->z);
+    __builtin_nontemporal_store(o.w, &d4->w);
+  } else {
+    uint2* d2 = reinterpret_cast<uint2*>(dst);  // four BF16 values
+    if (accumulate) {
+      const uint2 old = *d2;
+      o.x += bf16lo(old.x); o.y += bf16hi(old.x); o.z += bf16lo(old.y); o.w += bf16hi(old.y);
+    }
+    const uint32_t lo = bf16_rne(o.x) | (bf16_rne(o.y) << 16);
+    const uint32_t hi = bf16_rne(o.z) | (bf16_rne(o.w) << 16);
+    __builtin_nontemporal_store(lo, &d2->x);
+    __builtin_nontemporal_store(hi, &d2->y);
   }
-  __builtin_nontemporal_store(o.x, &dst->x);
-  __builtin_nontemporal_store(o.y, &dst->y);
-  __builtin_nontemporal_store(o.z, &dst->z);
-  __builtin_nontemporal_store(o.w, &dst->w);
 }
 
 namespace {
@@ -386,24 +403,33 @@ SplitPlan plan_split(int64_t M, int64_t N, int64_t K) {
 }
 
 hipError_t launch_split_reduce(int64_t M, int64_t N, const SplitPlan& p, const float* partial,
-                               const float* a_ts, const float* b_ts, float* c, int64_t ldc,
-                               int accumulate, hipStream_t s) {
-  k_gemm_split_reduce<<<dim3(BM * BN / 4 / 256, (unsigned)(p.tiles - p.full)), 256, 0, s>>>(
-      (int)M, (int)N, (int)p.full, p.split, partial, a_ts, b_ts, c, ldc, accumulate);
+                               const float* a_ts, const float* b_ts, void* c, int c_bf16,
+                               int64_t ldc, int accumulate, hipStream_t s) {
+  const dim3 grid(BM * BN / 4 / 256, (unsigned)(p.tiles - p.full));
+  if (c_bf16)
+    k_gemm_split_reduce<uint16_t><<<grid, 256, 0, s>>>((int)M, (int)N, (int)p.full, p.split, partial,
+                                                       a_ts, b_ts, static_cast<uint16_t*>(c), ldc,
+                                                       accumulate);
+  else
+    k_gemm_split_reduce<float><<<grid, 256, 0, s>>>((int)M, (int)N, (int)p.full, p.split, partial,
+                                                    a_ts, b_ts, static_cast<float*>(c), ldc, accumulate);
   return hipGetLastError();
 }
 
 int64_t gemm_workspace_size(int64_t M, int64_t N, int64_t K) { return plan_split(M, N, K).bytes; }
 
-hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
-                       const uint8_t* a_scales, const float* a_ts, const uint8_t* b_codes,
-                       const uint8_t* b_scales, int b_rowdiv, const float* b_ts, float* c,
-                       int64_t ldc, int accumulate, void* workspace, int64_t workspace_bytes,
-                       hipStream_t s) {
+namespace {
+
+template <typename OutT>
+hipError_t launch_gemm_t(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
+                         const uint8_t* a_scales, const float* a_ts, const uint8_t* b_codes,
+                         const uint8_t* b_scales, int b_rowdiv, const float* b_ts, OutT* c,
+                         int64_t ldc, int accumulate, void* workspace, int64_t workspace_bytes,
+                         hipStream_t s) {
   static std::once_flag once;
   static hipError_t attr_err = hipSuccess;
   std::call_once(once, [] {
-    attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_nvfp4),
+    attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_nvfp4<OutT>),
                                    hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
   });
   if (attr_err != hipSuccess) return attr_err;
@@ -415,12 +441,26 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
   const int64_t tail = p.tiles - p.full;
   const int64_t grid = p.full + tail * p.split;
   float* partial = static_cast<float*>(p.split > 1 ? workspace : nullptr);
-  k_gemm_nvfp4<<<(unsigned)grid, 512, LDS_BYTES, s>>>(
+  k_gemm_nvfp4<OutT><<<(unsigned)grid, 512, LDS_BYTES, s>>>(
       (int)M, (int)N, (int)K, a_codes, a_scales, a_ts, b_codes, b_scales, b_rowdiv, b_ts, c, ldc,
       accumulate, (int)p.full, p.split, partial);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.split == 1) return e;
-  return launch_split_reduce(M, N, p, partial, a_ts, b_ts, c, ldc, accumulate, s);
+  return launch_split_reduce(M, N, p, partial, a_ts, b_ts, c, sizeof(OutT) == 2, ldc, accumulate, s);
+}
+
+}  // namespace
+
+hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
+                       const uint8_t* a_scales, const float* a_ts, const uint8_t* b_codes,
+                       const uint8_t* b_scales, int b_rowdiv, const float* b_ts, void* c, int c_bf16,
+                       int64_t ldc, int accumulate, void* workspace, int64_t workspace_bytes,
+                       hipStream_t s) {
+  if (c_bf16)
+    return launch_gemm_t(M, N, K, a_codes, a_scales, a_ts, b_codes, b_scales, b_rowdiv, b_ts,
+                         static_cast<uint16_t*>(c), ldc, accumulate, workspace, workspace_bytes, s);
+  return launch_gemm_t(M, N, K, a_codes, a_scales, a_ts, b_codes, b_scales, b_rowdiv, b_ts,
+                       static_cast<float*>(c), ldc, accumulate, workspace, workspace_bytes, s);
 }
 
 }  // namespace nvfp4

@@ -53,9 +53,10 @@ struct SplitPlan {
 SplitPlan plan_split(int64_t M, int64_t N, int64_t K);
 
 // C = alpha * (sum of the p.split partial tiles of each tail tile) (+ C),
-// alpha = a_ts[0] * b_ts[0], or 1 when a_ts is null.
+// alpha = a_ts[0] * b_ts[0], or 1 when a_ts is null; c is FP32, or BF16 bits
+// when c_bf16 is set.
 hipError_t launch_split_reduce(int64_t M, int64_t N, const SplitPlan& p, const float* partial,
-                               const float* a_ts, const float* b_ts, float* c, int64_t ldc,
-                               int accumulate, hipStream_t s);
+                               const float* a_ts, const float* b_ts, void* c, int c_bf16,
+                               int64_t ldc, int accumulate, hipStream_t s);
 
 }  // namespace nvfp4

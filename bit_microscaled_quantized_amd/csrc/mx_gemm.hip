@@ -277,7 +277,7 @@ hipError_t launch_mx_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_code
                                                          (int)p.full, p.split, partial);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.split == 1) return e;
-  return launch_split_reduce(M, N, p, partial, nullptr, nullptr, c, ldc, accumulate, s);
+  return launch_split_reduce(M, N, p, partial, nullptr, nullptr, c, 0, ldc, accumulate, s);
 }
 
 }  // namespace nvfp4

@@ -166,6 +166,29 @@ __device__ __forceinline__ uint32_t absmax_bf16x2(uint32_t acc, uint32_t w) {
 __device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
+// FP32 -> BF16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t bf16_rne(float v) {
+  const uint32_t u = __float_as_uint(v);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// One output element of a GEMM or a dequantization: FP32 as is, BF16 rounded
+// to nearest even; load() reads one back as FP32.
+template <typename OutT>
+struct OutElem;
+template <>
+struct OutElem<float> {
+  static __device__ __forceinline__ float load(const float* p) { return *p; }
+  static __device__ __forceinline__ void store_nt(float* p, float v) { __builtin_nontemporal_store(v, p); }
+};
+template <>
+struct OutElem<uint16_t> {
+  static __device__ __forceinline__ float load(const uint16_t* p) { return __uint_as_float((uint32_t)*p << 16); }
+  static __device__ __forceinline__ void store_nt(uint16_t* p, float v) {
+    __builtin_nontemporal_store((uint16_t)bf16_rne(v), p);
+  }
+};
+
 // Radix-2 Walsh-Hadamard butterflies over 16 values with sign flips first and
 // the 1/4 normalization last: y = (1/4) H16 diag(d) x, Sylvester ordering.
 __device__ __forceinline__ void rht16(float* u, uint32_t sign_mask) {

@@ -22,11 +22,18 @@ hipError_t launch_quantize_row_rht(const void* x, int dt, int64_t tokens, int64_
                                    uint8_t* rht_codes, uint8_t* rht_scales, float* rht_ts,
                                    float* rht_amax, hipStream_t s);
 
+// c: FP32, or BF16 bits when c_bf16 is set.
 hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
                        const uint8_t* a_scales, const float* a_ts, const uint8_t* b_codes,
-                       const uint8_t* b_scales, int b_rowdiv, const float* b_ts, float* c,
+                       const uint8_t* b_scales, int b_rowdiv, const float* b_ts, void* c, int c_bf16,
                        int64_t ldc, int accumulate, void* workspace, int64_t workspace_bytes,
                        hipStream_t s);
+
+// out[r][c] = e2m1(code) * dec(scale of (r / scale_rowdiv, c / 16)) * tensor_scale,
+// FP32, or BF16 bits (that FP32 value rounded to nearest even) when out_bf16.
+hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* scales, int scale_rowdiv,
+                             const float* tensor_scale, int64_t rows, int64_t cols, void* out,
+                             int out_bf16, int64_t ld_out, hipStream_t s);
 
 hipError_t launch_mx_quantize(const void* x, int dt, int64_t rows, int64_t cols, int64_t ld,
                               int layout, int rnd, uint64_t seed, uint8_t* codes, uint8_t* scales,

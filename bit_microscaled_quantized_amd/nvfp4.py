@@ -20,7 +20,8 @@ NVFP4_RNE, NVFP4_SR = 0, 1
 NVFP4_ROW_1D, NVFP4_COL_1D, NVFP4_TILE_2D = 0, 1, 2
 
 EXPORTED = ("nvfp4_quantize", "nvfp4_rht_quantize", "nvfp4_quantize_row_rht", "nvfp4_gemm",
-            "nvfp4_gemm_workspace_size", "nvfp4_status_str", "mxfp4_quantize", "mxfp4_gemm")
+            "nvfp4_gemm_bf16", "nvfp4_dequantize", "nvfp4_gemm_workspace_size", "nvfp4_status_str",
+            "mxfp4_quantize", "mxfp4_gemm")
 
 _lib = None
 
@@ -59,6 +60,11 @@ def load_library():
     L.mxfp4_gemm.restype = i32
     L.nvfp4_gemm.argtypes = [i64, i64, i64, vp, vp, vp, vp, vp, i32, vp, vp, i64, f32, vp, i64, vp]
     L.nvfp4_gemm.restype = i32
+    L.nvfp4_gemm_bf16.argtypes = [i64, i64, i64, vp, vp, vp, vp, vp, i32, vp, vp, i64, f32, vp, i64,
+                                  vp]
+    L.nvfp4_gemm_bf16.restype = i32
+    L.nvfp4_dequantize.argtypes = [vp, vp, i32, vp, i64, i64, i32, vp, i64, vp]
+    L.nvfp4_dequantize.restype = i32
     L.nvfp4_gemm_workspace_size.argtypes = [i64, i64, i64, ctypes.POINTER(i64)]
     L.nvfp4_gemm_workspace_size.restype = i32
     L.nvfp4_status_str.argtypes = [i32]
@@ -136,6 +142,28 @@ def nvfp4_gemm(M, N, K, a_codes, a_scales, a_tensor_scale, b_codes, b_scales, b_
         _addr(b_scales), b_scale_rowdiv, _addr(b_tensor_scale), _addr(c), ldc, float(beta),
         _addr(workspace), int(workspace_bytes), _stream(stream))
     return _check("nvfp4_gemm", st, raise_on_error)
+
+
+def nvfp4_gemm_bf16(M, N, K, a_codes, a_scales, a_tensor_scale, b_codes, b_scales, b_scale_rowdiv,
+                    b_tensor_scale, c, ldc, beta, workspace=None, workspace_bytes=None, stream=None,
+                    raise_on_error=True) -> int:
+    """nvfp4_gemm with c holding BF16 (a torch.bfloat16 tensor or its address)."""
+    if workspace_bytes is None:
+        workspace_bytes = 0 if workspace is None or isinstance(workspace, int) else \
+            workspace.numel() * workspace.element_size()
+    st = load_library().nvfp4_gemm_bf16(
+        M, N, K, _addr(a_codes), _addr(a_scales), _addr(a_tensor_scale), _addr(b_codes),
+        _addr(b_scales), b_scale_rowdiv, _addr(b_tensor_scale), _addr(c), ldc, float(beta),
+        _addr(workspace), int(workspace_bytes), _stream(stream))
+    return _check("nvfp4_gemm_bf16", st, raise_on_error)
+
+
+def nvfp4_dequantize(codes, scales, scale_rowdiv, tensor_scale, rows, cols, out_dt, out, ld_out,
+                     stream=None, raise_on_error=True) -> int:
+    st = load_library().nvfp4_dequantize(_addr(codes), _addr(scales), scale_rowdiv,
+                                         _addr(tensor_scale), rows, cols, out_dt, _addr(out),
+                                         ld_out, _stream(stream))
+    return _check("nvfp4_dequantize", st, raise_on_error)
 
 
 def nvfp4_gemm_workspace_size(M, N, K) -> int:

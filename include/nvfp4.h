@@ -170,6 +170,48 @@ nvfp4_status nvfp4_gemm(int64_t M, int64_t N, int64_t K, const uint8_t *a_codes,
                         void *workspace, int64_t workspace_bytes, void *stream);
 
 /*
+ * nvfp4_gemm_bf16 -- nvfp4_gemm with a BF16 output: every argument as for
+ * nvfp4_gemm except c, which holds BF16 bit patterns [M][ldc] (ldc a multiple
+ * of 8, c 16-byte aligned).  Each output is computed in FP32 exactly as by
+ * nvfp4_gemm (alpha * accumulated sum, plus the BF16 value already in c
+ * widened to FP32 when beta = 1) and rounded to BF16 once, to nearest even.
+ * The pages' recipe keeps the rest of the model in BF16 (same page, part 2,
+ * technique 1, the layers left in BF16), so a linear layer's result returns
+ * to BF16; the rounding taken is the plain nearest-even one of the FP32
+ * result.
+ */
+nvfp4_status nvfp4_gemm_bf16(int64_t M, int64_t N, int64_t K, const uint8_t *a_codes,
+                             const uint8_t *a_scales, const float *a_tensor_scale,
+                             const uint8_t *b_codes, const uint8_t *b_scales,
+                             int32_t b_scale_rowdiv, const float *b_tensor_scale, uint16_t *c,
+                             int64_t ldc, float beta, void *workspace, int64_t workspace_bytes,
+                             void *stream);
+
+/*
+ * nvfp4_dequantize -- NVFP4 codes back to FP32 or BF16 (the value definition
+ * of "Formato NVFP4", part 2 of the same page: E2M1 element x E4M3 block scale
+ * x FP32 tensor scale).
+ *
+ *   out[r][c] = RN32( e2m1(code[r][c]) * dec(scales[r / scale_rowdiv][c / 16])
+ *                     * tensor_scale[0] )
+ *   rows x cols is the shape of the code array as stored: codes [rows][cols/2]
+ *   (the even element in the low nibble); scales [rows][cols/16] with
+ *   scale_rowdiv 1 (row-1D, column-1D and RHT outputs, read in their stored,
+ *   transposed orientation) or [rows/16][cols/16] with scale_rowdiv 16 (the
+ *   2D tile grid; codes_t / scales_t of a 2D quantization dequantize the same
+ *   way).  e2m1 * dec is exact in FP32, so the only rounding is the multiply
+ *   by the tensor scale (RN32, nearest even); out_dt NVFP4_BF16 rounds that
+ *   FP32 value to BF16, nearest even.  out [rows][ld_out] of out_dt, 16-byte
+ *   aligned rows (ld_out * element size a multiple of 16); ld_out >= cols.
+ *   cols a positive multiple of 16, rows a positive multiple of scale_rowdiv,
+ *   rows * cols < 2^32.  Scale bytes must be finite E4M3 codes (0x00..0x7E,
+ *   what the quantize calls produce); codes 0x7F/0xFF give unspecified values.
+ */
+nvfp4_status nvfp4_dequantize(const uint8_t *codes, const uint8_t *scales, int32_t scale_rowdiv,
+                              const float *tensor_scale, int64_t rows, int64_t cols, int out_dt,
+                              void *out, int64_t ld_out, void *stream);
+
+/*
  * nvfp4_gemm_workspace_size -- bytes of workspace nvfp4_gemm uses for an
  * M x N x K problem on the CURRENT device (0 when that shape needs none; at
  * most 256 KiB per compute unit).  Shape rules and errors as for nvfp4_gemm;

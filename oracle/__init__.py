@@ -64,6 +64,10 @@ def lib():
                                              vp, i64, i64]
         L.ora_rht_quantize_range.restype = i32
         L.ora_dequant.argtypes, L.ora_dequant.restype = [i64, i64, vp, vp, i32, f32, vp], None
+        L.ora_dequant_f32.argtypes, L.ora_dequant_f32.restype = [i64, i64, vp, vp, i32, f32, vp], None
+        L.ora_dequant_bf16.argtypes, L.ora_dequant_bf16.restype = [i64, i64, vp, vp, i32, f32, vp], None
+        L.ora_bf16_rne.argtypes, L.ora_bf16_rne.restype = [f32], ctypes.c_uint16
+        L.ora_bf16_rne_array.argtypes, L.ora_bf16_rne_array.restype = [i64, vp, vp], None
         L.ora_gemm_f64.argtypes, L.ora_gemm_f64.restype = [i64, i64, i64, vp, vp, f64, vp], None
         L.ora_num_threads.argtypes, L.ora_num_threads.restype = [], i32
         L.ora_mx_scale_exp.argtypes, L.ora_mx_scale_exp.restype = [f32], i32
@@ -201,6 +205,37 @@ def dequant(codes: np.ndarray, scales: np.ndarray, tensor_scale: float,
     n, k = codes.shape[0], codes.shape[1] * 2
     out = np.empty((n, k), np.float64)
     lib().ora_dequant(n, k, _ptr(codes), _ptr(scales), scale_rowdiv, tensor_scale, _ptr(out))
+    return out
+
+
+def dequant_f32(codes: np.ndarray, scales: np.ndarray, tensor_scale: float,
+                scale_rowdiv: int = 1) -> np.ndarray:
+    """FP32 values of n x k NVFP4 codes: the exact value rounded once."""
+    codes = np.ascontiguousarray(codes)
+    scales = np.ascontiguousarray(scales)
+    n, k = codes.shape[0], codes.shape[1] * 2
+    out = np.empty((n, k), np.float32)
+    lib().ora_dequant_f32(n, k, _ptr(codes), _ptr(scales), scale_rowdiv, tensor_scale, _ptr(out))
+    return out
+
+
+def dequant_bf16(codes: np.ndarray, scales: np.ndarray, tensor_scale: float,
+                 scale_rowdiv: int = 1) -> np.ndarray:
+    """BF16 bit patterns (uint16) of n x k NVFP4 codes: the FP32 value of
+    dequant_f32 rounded to BF16, nearest even."""
+    codes = np.ascontiguousarray(codes)
+    scales = np.ascontiguousarray(scales)
+    n, k = codes.shape[0], codes.shape[1] * 2
+    out = np.empty((n, k), np.uint16)
+    lib().ora_dequant_bf16(n, k, _ptr(codes), _ptr(scales), scale_rowdiv, tensor_scale, _ptr(out))
+    return out
+
+
+def bf16_rne(x) -> np.ndarray:
+    """BF16 bit patterns of FP32 values, nearest even (elementwise)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x.shape, np.uint16)
+    lib().ora_bf16_rne_array(x.size, _ptr(x), _ptr(out))
     return out
 
 

@@ -629,6 +629,67 @@ void ora_dequant(int64_t n, int64_t k, const uint8_t *codes, const uint8_t *scal
         }
 }
 
+/* Working-precision outputs of the layer: the NVFP4 -> FP32 / BF16
+ * dequantization, and the rounding of a GEMM result to BF16 (the model
+ * around the NVFP4 layers runs in BF16, [NV-SUM] 2, technique 1).
+ *   FP32: the exact FP64 value of ora_dequant converted to float, nearest even
+ *         (one rounding).
+ *   BF16: a float rounded to 8 significant bits, nearest even: the value is
+ *         divided by its BF16 spacing (2^(E-7) for |x| in [2^E, 2^(E+1)),
+ *         E >= -126; 2^-133 below), rounded to an integer with ties to even,
+ *         and multiplied back; magnitudes that round past the largest finite
+ *         BF16 value become infinity. */
+uint16_t ora_bf16_rne(float x)
+{
+    double ax, unit, q;
+    int ex;
+    float y;
+    uint32_t bits;
+    ax = fabs((double)x);
+    if (ax == 0.0) {
+        memcpy(&bits, &x, 4);
+        return (uint16_t)(bits >> 16); /* +0 or -0 */
+    }
+    frexp(ax, &ex); /* ax = m * 2^ex, m in [0.5, 1): E = ex - 1 */
+    unit = (ex - 1 >= -126) ? ldexp(1.0, ex - 8) : ldexp(1.0, -133);
+    q = nearbyint(ax / unit) * unit; /* default rounding mode: ties to even */
+    y = (float)(x < 0.0f ? -q : q);  /* exact (or +-inf past the BF16 range) */
+    memcpy(&bits, &y, 4);
+    return (uint16_t)(bits >> 16);
+}
+
+void ora_bf16_rne_array(int64_t n, const float *x, uint16_t *out)
+{
+    int64_t i;
+    for (i = 0; i < n; i++)
+        out[i] = ora_bf16_rne(x[i]);
+}
+
+void ora_dequant_f32(int64_t n, int64_t k, const uint8_t *codes, const uint8_t *scales,
+                     int scale_rowdiv, float s_t, float *out)
+{
+    int64_t r, c;
+    for (r = 0; r < n; r++)
+        for (c = 0; c < k; c++) {
+            int code = (codes[(r * k + c) >> 1] >> (((r * k + c) & 1) * 4)) & 15;
+            int e = scales[(r / scale_rowdiv) * (k / 16) + c / 16];
+            out[r * k + c] = (float)(ora_e2m1_value(code) * ora_e4m3_value(e) * (double)s_t);
+        }
+}
+
+void ora_dequant_bf16(int64_t n, int64_t k, const uint8_t *codes, const uint8_t *scales,
+                      int scale_rowdiv, float s_t, uint16_t *out)
+{
+    int64_t r, c;
+    for (r = 0; r < n; r++)
+        for (c = 0; c < k; c++) {
+            int code = (codes[(r * k + c) >> 1] >> (((r * k + c) & 1) * 4)) & 15;
+            int e = scales[(r / scale_rowdiv) * (k / 16) + c / 16];
+            float v = (float)(ora_e2m1_value(code) * ora_e4m3_value(e) * (double)s_t);
+            out[r * k + c] = ora_bf16_rne(v);
+        }
+}
+
 /* C[m][n] = beta * C[m][n] + sum_k A[m][k] * B[n][k], all FP64, triple loop
  * (for tiny shapes; large shapes use a BLAS dgemm on ora_dequant output). */
 void ora_gemm_f64(int64_t M, int64_t N, int64_t K, const double *A, const double *B,

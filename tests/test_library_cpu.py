@@ -180,3 +180,36 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(b, "_LIB_PATH", str(tmp_path / "libnvfp4.so"))
     with pytest.raises(RuntimeError, match="missing"):
         b.load_library()
+
+
+def test_dequantize_argument_errors():
+    def d(**kw):
+        args = dict(codes=FAKE, scales=FAKE, scale_rowdiv=1, tensor_scale=FAKE, rows=32, cols=64,
+                    out_dt=b.NVFP4_BF16, out=FAKE, ld_out=64)
+        args.update(kw)
+        return nv.nvfp4_dequantize(**args, stream=0, raise_on_error=False)
+    assert d(codes=None) == b.NVFP4_EINVAL
+    assert d(out=None) == b.NVFP4_EINVAL
+    assert d(scale_rowdiv=4) == b.NVFP4_EINVAL
+    assert d(out_dt=7) == b.NVFP4_EINVAL
+    assert d(cols=40, ld_out=40) == b.NVFP4_ESHAPE        # cols % 16
+    assert d(rows=24, scale_rowdiv=16) == b.NVFP4_ESHAPE  # 2D tile grid needs rows % 16
+    assert d(ld_out=32) == b.NVFP4_ESHAPE
+    assert d(rows=0) == b.NVFP4_ESHAPE
+    assert d(codes=FAKE + 8) == b.NVFP4_EALIGN
+    assert d(out=FAKE + 4) == b.NVFP4_EALIGN
+    assert d(ld_out=68) == b.NVFP4_EALIGN                 # 136-byte BF16 rows
+
+
+def test_gemm_bf16_argument_errors():
+    def g16(**kw):
+        args = dict(M=256, N=256, K=256, a_codes=FAKE, a_scales=FAKE, a_tensor_scale=FAKE,
+                    b_codes=FAKE, b_scales=FAKE, b_scale_rowdiv=1, b_tensor_scale=FAKE, c=FAKE,
+                    ldc=256, beta=0.0)
+        args.update(kw)
+        return nv.nvfp4_gemm_bf16(**args, stream=0, raise_on_error=False)
+    assert g16(c=None) == b.NVFP4_EINVAL
+    assert g16(beta=0.5) == b.NVFP4_EINVAL
+    assert g16(K=96) == b.NVFP4_ESHAPE
+    assert g16(ldc=260) == b.NVFP4_EALIGN                 # BF16 rows must be 16-byte multiples
+    assert g16(c=FAKE + 8) == b.NVFP4_EALIGN

@@ -546,3 +546,44 @@ def test_nvfp4_beats_mxfp4_on_gaussian_blocks(ora):
     err_nv = float(((nv - x) ** 2).mean())
     err_mx = float(((mx - x) ** 2).mean())
     assert err_nv < 0.8 * err_mx
+
+
+# --- working-precision outputs (FP32 / BF16 dequantization, BF16 GEMM result)
+
+def _bf16_torch(x: np.ndarray) -> np.ndarray:
+    """BF16 bits of FP32 values by torch's CPU conversion (nearest even)."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def test_bf16_rounding_matches_torch(ora):
+    """The oracle's BF16 rounding (integer rounding at the BF16 spacing) against
+    torch's conversion, over every exponent, exact ties, their neighbours,
+    subnormals and values that overflow to infinity."""
+    rng = np.random.default_rng(41)
+    u = rng.integers(0, 0x7F800000, 200000, dtype=np.uint32)
+    u |= rng.integers(0, 2, u.size, dtype=np.uint32) << 31
+    hi = rng.integers(0, 0x7F80, 4000, dtype=np.uint32) | (rng.integers(0, 2, 4000, dtype=np.uint32) << 15)
+    ties = (hi << 16) | 0x8000  # finite values exactly halfway between two BF16 values
+    near = np.concatenate([ties - 1, ties + 1])
+    special = np.array([0, 0x80000000, 1, 0x8000, 0x18000, 0x7F7FFFFF, 0x7F7F8000, 0x7F7F7FFF,
+                        0xFF7FFFFF, 0x00800000, 0x007FFFFF, 0x3F808000, 0x3F818000], np.uint32)
+    x = np.concatenate([u, ties, near, special]).view(np.float32)
+    assert np.array_equal(ora.bf16_rne(x), _bf16_torch(x))
+
+
+@pytest.mark.parametrize("rowdiv", [1, 16])
+def test_dequant_f32_is_the_exact_value_rounded_once(ora, rowdiv):
+    """dequant_f32 = numpy's nearest-even FP64 -> FP32 conversion of the exact
+    FP64 value; tensor scales include tiny ones whose products are subnormal."""
+    rng = np.random.default_rng(42 + rowdiv)
+    n, k = 64, 96
+    codes = rng.integers(0, 256, (n, k // 2), dtype=np.uint8)
+    scales = rng.integers(0, 127, (n // rowdiv, k // 16), dtype=np.uint8)
+    for ts in (1.0, 0.1234567, 3.7e-3, 2.0 ** -120, 1e-40, 7.5e33):
+        ts = float(np.float32(ts))
+        got = ora.dequant_f32(codes, scales, ts, rowdiv)
+        want = ora.dequant(codes, scales, ts, rowdiv).astype(np.float32)
+        assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), ts
+        assert np.array_equal(ora.dequant_bf16(codes, scales, ts, rowdiv), _bf16_torch(want)), ts
