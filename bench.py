@@ -22,6 +22,9 @@ tokens by default; --cpu-sample-tokens bounds it).
 NVFP4 step (not part of `value`): MXFP4 (32-element blocks, E8M0 scales, no
 tensor scale, no Hadamard) row and column quantization of W, X (RNE) and dY
 (SR), then the same three GEMMs on the block-scaled FP4 matrix instruction.
+`components.linear_module` times the autograd layer (NVFP4Linear forward +
+backward with BF16 outputs) against the same layer kept in BF16, and the
+NVFP4 -> BF16 dequantization of W.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
 """
@@ -173,7 +176,57 @@ def gpu_bench(inp, steps, warmup):
         per.setdefault(name, []).append(a.elapsed_time(b))
     per = {k: float(np.mean(v)) for k, v in per.items()}
     mx = mx_bench(x, w, dy, s_row, s_col, steps, warmup)
-    return wall / steps, per, mx
+    mod = module_bench(x, w, dy, st, steps, warmup)
+    return wall / steps, per, mx, mod
+
+
+def _events_ms(torch, fn, steps, warmup):
+    """Mean HIP-event time of fn() on the current stream."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps
+
+
+def module_bench(x, w, dy, st, steps, warmup):
+    """The autograd layer on the same tensors: NVFP4Linear forward + backward
+    (quantize, Fprop, Dgrad, Wgrad, BF16 outputs) against the same layer kept
+    in BF16 (torch's BF16 matmul); and NVFP4 -> BF16 dequantization of W."""
+    import torch
+    import bit_microscaled_quantized_amd as nv
+    from bit_microscaled_quantized_amd.module import NVFP4Linear
+    T, I, O = TOKENS, D_IN, D_OUT
+    xb = x.view(torch.bfloat16)
+    dyb = dy.view(torch.bfloat16)
+    out = {}
+    for name, bypass in (("nvfp4", False), ("bf16", True)):
+        layer = NVFP4Linear(I, O, bf16=bypass, seed=1, device=x.device)
+        with torch.no_grad():
+            layer.weight.copy_(w.view(torch.bfloat16))
+        xi = xb.detach().clone().requires_grad_(True)
+
+        def fwd_bwd():
+            layer.weight.grad = None
+            xi.grad = None
+            layer(xi).backward(dyb)
+        ms = _events_ms(torch, fwd_bwd, steps, warmup)
+        out[f"{name}_fwd_bwd_ms"] = round(ms, 4)
+        out[f"{name}_TFLOPs"] = round(3 * 2.0 * T * I * O / (ms * 1e-3) / 1e12, 2)
+    q = st.qw  # W quantized by the NVFP4 step above
+    wd = torch.empty((O, I), dtype=torch.bfloat16, device=x.device)
+    ms = _events_ms(torch, lambda: nv.nvfp4_dequantize(q.codes, q.scales, 16, q.ts, O, I, nv.NVFP4_BF16,
+                                                       wd, I), steps, warmup)
+    nbytes = O * I // 2 + O * I // 256 + O * I * 2
+    out["dequant_w_bf16_ms"] = round(ms, 4)
+    out["dequant_w_bf16_GBps"] = round(nbytes / (ms * 1e-3) / 1e9, 1)
+    out["dequant_frac_hbm"] = round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+    return out
 
 
 def mx_quantize_bytes():
@@ -291,7 +344,7 @@ def main():
               "(the sharded path is a design, not built)", file=sys.stderr)
         sys.exit(2)
     inp = make_inputs()
-    ms_step, per, mx = gpu_bench(inp, args.steps, args.warmup)
+    ms_step, per, mx, mod = gpu_bench(inp, args.steps, args.warmup)
     if args.copy_probe_mib:
         import torch
         # an elementwise kernel (not a DMA copy, which no counter sees) that
@@ -357,6 +410,7 @@ def main():
             "per_call_ms": {k: round(v, 4) for k, v in per.items()},
             "quantize_bytes": qb,
             "mxfp4": mx,
+            "linear_module": mod,
         },
     }
     if not args.no_cpu_baseline:
