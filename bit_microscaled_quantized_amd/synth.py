@@ -44,6 +44,17 @@ def normal_with_outliers(seed: int, shape, frac: float = 1e-3, mag: float = 100.
     return x
 
 
+def token_outliers(seed: int, shape, frac: float = 1.0 / 64, mag: float = 32.0) -> np.ndarray:
+    """N(0,1) rows (tokens) with round(frac*rows) distinct rows scaled by mag:
+    outliers concentrated in a few tokens across every feature."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal(shape, dtype=np.float32)
+    k = int(round(frac * shape[0]))
+    rows = rng.choice(shape[0], size=k, replace=False)
+    x[rows] *= np.float32(mag)
+    return x
+
+
 def student_t(seed: int, shape, nu: float = 3.0) -> np.ndarray:
     return np.random.default_rng(seed).standard_t(nu, size=shape).astype(np.float32)
 
