@@ -117,6 +117,16 @@ __device__ __forceinline__ void pcg8(uint32_t key, uint32_t pair0, uint32_t* h) 
     h[p] = pcg_tail(base + ((((key & 7u) ^ (uint32_t)p) * 747796405u) + 2891336453u));
 }
 
+// pcg(key ^ (pair0 + p)) for p = 0..3, pair0 a multiple of 4 (the same
+// shared-multiply form as pcg8, over the two low bits).
+__device__ __forceinline__ void pcg4(uint32_t key, uint32_t pair0, uint32_t* h) {
+  uint32_t base = ((key ^ pair0) & ~3u) * 747796405u;
+  asm volatile("" : "+v"(base));
+#pragma unroll
+  for (int p = 0; p < 4; p++)
+    h[p] = pcg_tail(base + ((((key & 3u) ^ (uint32_t)p) * 747796405u) + 2891336453u));
+}
+
 __host__ __device__ __forceinline__ uint32_t pcg_host(uint32_t v) {
   uint32_t state = v * 747796405u + 2891336453u;
   uint32_t word = ((state >> ((state >> 28u) + 4u)) ^ state) * 277803737u;

@@ -151,6 +151,28 @@ __device__ __forceinline__ uint2 encode16(const float* v, uint32_t key, uint32_t
   }
 }
 
+// Encode 8 scaled values (half a block) into one dword, element 0 in the low
+// nibble: RNE in hardware, SR with pcg bits of output elements 2 pair0 ..
+// 2 pair0 + 7 (pair0 a multiple of 4).
+template <int RND>
+__device__ __forceinline__ uint32_t encode8(const float* v, uint32_t key, uint32_t pair0) {
+  if constexpr (RND == 0) {
+    return pack8_rne(v);
+  } else {
+    uint32_t h[4];
+    pcg4(key, pair0, h);
+    uint32_t w = 0u;
+#pragma unroll
+    for (int p = 0; p < 4; p++) {
+      const uint32_t nh = ~h[p];
+      const uint32_t c0 = sr_code_c(v[2 * p], nh & 0xFFFFu);
+      const uint32_t c1 = sr_code_c(v[2 * p + 1], nh >> 16);
+      w |= (c0 | (c1 << 4)) << (8 * p);
+    }
+    return w;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // 1D row cast: blocks of 16 along a row; each lane owns whole blocks (two
 // 16-byte loads for bf16), UNROLL blocks per lane per round, contiguous
@@ -242,6 +264,11 @@ struct ColTile<uint16_t> {
       u[j] = (k & 1) ? bf16hi(d) : bf16lo(d);
     }
   }
+  // the 8 values of row j
+  __device__ __forceinline__ void row(int j, float* v) const {
+    v[0] = bf16lo(w[j].x); v[1] = bf16hi(w[j].x); v[2] = bf16lo(w[j].y); v[3] = bf16hi(w[j].y);
+    v[4] = bf16lo(w[j].z); v[5] = bf16hi(w[j].z); v[6] = bf16lo(w[j].w); v[7] = bf16hi(w[j].w);
+  }
 };
 
 template <>
@@ -262,33 +289,20 @@ struct ColTile<float> {
       u[j] = e == 0 ? q.x : e == 1 ? q.y : e == 2 ? q.z : q.w;
     }
   }
+  __device__ __forceinline__ void row(int j, float* v) const {
+    v[0] = w[j][0].x; v[1] = w[j][0].y; v[2] = w[j][0].z; v[3] = w[j][0].w;
+    v[4] = w[j][1].x; v[5] = w[j][1].y; v[6] = w[j][1].z; v[7] = w[j][1].w;
+  }
 };
 
+// The column encoding of a tile (transform, block scale, encode) into the LDS
+// staging arrays, and the contiguous stores of the staged codes and scales.
 template <typename T, int RND, bool RHT>
-__global__ __launch_bounds__(256) void k_cast_col1d(const T* __restrict__ x, int64_t rows,
-                                                    int64_t cols, int64_t ld, uint32_t sign_mask,
-                                                    const float* __restrict__ amax,
-                                                    uint8_t* __restrict__ codes,
-                                                    uint8_t* __restrict__ scales,
-                                                    float* __restrict__ tensor_scale, uint32_t key) {
-  __shared__ __align__(16) uint8_t lcodes[kColCols][kColTok / 2];
-  __shared__ __align__(16) uint8_t lscales[kColCols][kColTok / 16];
-  __shared__ float rtab[128];
-  const float s_enc = encode_scale(amax[0]);
-  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) tensor_scale[0] = 1.0f / s_enc;
-  fill_scale_table(rtab, s_enc);
-  __syncthreads();
-
-  const int64_t t0 = (int64_t)blockIdx.y * kColTok;
-  const int64_t c0 = (int64_t)blockIdx.x * kColCols;
-  const int co = threadIdx.x & 7;   // column octet
-  const int g = threadIdx.x >> 3;   // 16-token group within the tile
-  const int64_t tg = t0 + 16 * g;   // first token of the group
-  const int64_t cc = c0 + 8 * co;   // first column of the octet
-  const bool valid = tg < rows && cc < cols;
-
-  ColTile<T> tile;
-  if (valid) tile.load(x + tg * ld + cc, ld);
+__device__ __forceinline__ void col_encode(const ColTile<T>& tile, bool valid, int64_t rows, int64_t tg,
+                                           int64_t cc, int g, int co, uint32_t sign_mask, float s_enc,
+                                           const float* rtab, uint32_t key,
+                                           uint8_t (*lcodes)[kColTok / 2],
+                                           uint8_t (*lscales)[kColTok / 16]) {
 #pragma unroll
   for (int k = 0; k < 8; k++) {
     uint32_t e_b = 0u;
@@ -312,8 +326,12 @@ __global__ __launch_bounds__(256) void k_cast_col1d(const T* __restrict__ x, int
     *reinterpret_cast<uint2*>(&lcodes[8 * co + k][8 * g]) = make_uint2(w0, w1);
     lscales[8 * co + k][g] = (uint8_t)e_b;
   }
-  __syncthreads();
+}
 
+__device__ __forceinline__ void col_store(int64_t rows, int64_t cols, int64_t t0, int64_t c0,
+                                          const uint8_t (*lcodes)[kColTok / 2],
+                                          const uint8_t (*lscales)[kColTok / 16], uint8_t* codes,
+                                          uint8_t* scales) {
   // codes: 64 rows of 256 bytes; 16 threads per row, 16 bytes each
   const int64_t row_bytes = rows / 2;
   for (int pass = 0; pass < 4; pass++) {
@@ -350,6 +368,111 @@ __global__ __launch_bounds__(256) void k_cast_col1d(const T* __restrict__ x, int
       }
     }
   }
+}
+
+template <typename T, int RND, bool RHT>
+__global__ __launch_bounds__(256) void k_cast_col1d(const T* __restrict__ x, int64_t rows,
+                                                    int64_t cols, int64_t ld, uint32_t sign_mask,
+                                                    const float* __restrict__ amax,
+                                                    uint8_t* __restrict__ codes,
+                                                    uint8_t* __restrict__ scales,
+                                                    float* __restrict__ tensor_scale, uint32_t key) {
+  __shared__ __align__(16) uint8_t lcodes[kColCols][kColTok / 2];
+  __shared__ __align__(16) uint8_t lscales[kColCols][kColTok / 16];
+  __shared__ float rtab[128];
+  const float s_enc = encode_scale(amax[0]);
+  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) tensor_scale[0] = 1.0f / s_enc;
+  fill_scale_table(rtab, s_enc);
+  __syncthreads();
+
+  const int64_t t0 = (int64_t)blockIdx.y * kColTok;
+  const int64_t c0 = (int64_t)blockIdx.x * kColCols;
+  const int co = threadIdx.x & 7;   // column octet
+  const int g = threadIdx.x >> 3;   // 16-token group within the tile
+  const int64_t tg = t0 + 16 * g;   // first token of the group
+  const int64_t cc = c0 + 8 * co;   // first column of the octet
+  const bool valid = tg < rows && cc < cols;
+
+  ColTile<T> tile;
+  if (valid) tile.load(x + tg * ld + cc, ld);
+  col_encode<T, RND, RHT>(tile, valid, rows, tg, cc, g, co, sign_mask, s_enc, rtab, key, lcodes, lscales);
+  __syncthreads();
+  col_store(rows, cols, t0, c0, lcodes, lscales, codes, scales);
+}
+
+// Row-1D copy and RHT column copy of the same tensor from ONE read (the two
+// quantizations a training step needs from X or dY), with the column cast's
+// tile mapping.  The row block of 16 columns spans the lane pair (co, co^1):
+// each lane holds 8 of its values, one shuffle combines the two half maxima,
+// and each lane encodes its 8 values (4 code bytes per row).
+template <typename T, int RR, int RH>
+__global__ __launch_bounds__(256) void k_cast_row_rht(
+    const T* __restrict__ x, int64_t rows, int64_t cols, int64_t ld, uint32_t sign_mask,
+    const float* __restrict__ row_amax, uint8_t* __restrict__ row_codes,
+    uint8_t* __restrict__ row_scales, float* __restrict__ row_ts, uint32_t row_key,
+    const float* __restrict__ rht_amax, uint8_t* __restrict__ rht_codes,
+    uint8_t* __restrict__ rht_scales, float* __restrict__ rht_ts, uint32_t rht_key) {
+  __shared__ __align__(16) uint8_t lcodes[kColCols][kColTok / 2];
+  __shared__ __align__(16) uint8_t lscales[kColCols][kColTok / 16];
+  __shared__ float rtab_row[128];
+  __shared__ float rtab_rht[128];
+  const float s_row = encode_scale(row_amax[0]);
+  const float s_rht = encode_scale(rht_amax[0]);
+  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
+    row_ts[0] = 1.0f / s_row;
+    rht_ts[0] = 1.0f / s_rht;
+  }
+  if (threadIdx.x < 128)
+    rtab_row[threadIdx.x] = element_scale(threadIdx.x, s_row);
+  else
+    rtab_rht[threadIdx.x - 128] = element_scale(threadIdx.x - 128, s_rht);
+  __syncthreads();
+
+  const int64_t t0 = (int64_t)blockIdx.y * kColTok;
+  const int64_t c0 = (int64_t)blockIdx.x * kColCols;
+  const int co = threadIdx.x & 7;
+  const int g = threadIdx.x >> 3;
+  const int64_t tg = t0 + 16 * g;
+  const int64_t cc = c0 + 8 * co;
+  const bool valid = tg < rows && cc < cols;  // the lane pair (co, co^1) agrees (cols % 16 == 0)
+
+  ColTile<T> tile;
+  if (valid) tile.load(x + tg * ld + cc, ld);
+
+  // row copy: rows tg .. tg + 15, columns cc .. cc + 7 of this lane
+  const int64_t rbytes = cols / 2, rscales = cols / 16;
+#pragma unroll
+  for (int j = 0; j < 16; j++) {
+    float v[8];
+    if (valid) {
+      tile.row(j, v);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; e++) v[e] = 0.0f;
+    }
+    float am = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; e++) am = fmaxf(am, fabsf(v[e]));
+    am = fmaxf(am, __shfl_xor(am, 1));
+    uint32_t e_b;
+    float r_b;
+    block_scale(am, s_row, rtab_row, e_b, r_b);
+    float sv[8];
+#pragma unroll
+    for (int e = 0; e < 8; e++) sv[e] = v[e] * r_b;
+    const int64_t r = tg + j;
+    const uint32_t w = encode8<RR>(sv, row_key, (uint32_t)(r * cols + cc) >> 1);
+    if (valid) {
+      *reinterpret_cast<uint32_t*>(row_codes + r * rbytes + cc / 2) = w;
+      if ((co & 1) == 0) row_scales[r * rscales + cc / 16] = (uint8_t)e_b;
+    }
+  }
+
+  // RHT column copy
+  col_encode<T, RH, true>(tile, valid, rows, tg, cc, g, co, sign_mask, s_rht, rtab_rht, rht_key, lcodes,
+                          lscales);
+  __syncthreads();
+  col_store(rows, cols, t0, c0, lcodes, lscales, rht_codes, rht_scales);
 }
 
 // amax of the RHT output (and, if amax_plain is not null, of the input itself,
@@ -623,11 +746,27 @@ hipError_t launch_quantize_row_rht(const void* x, int dt, int64_t tokens, int64_
   sign_mask &= 0xFFFFu;
   hipError_t e = launch_rht_amax(x, dt, tokens, cols, ld, sign_mask, rht_amax, row_amax, s);
   if (e != hipSuccess) return e;
-  e = launch_cast(x, dt, tokens, cols, ld, 0, row_rnd, row_seed, row_codes, row_scales, nullptr,
-                  nullptr, row_ts, row_amax, s);
-  if (e != hipSuccess) return e;
-  return launch_rht_cast(x, dt, tokens, cols, ld, sign_mask, rht_rnd, rht_seed, rht_codes,
-                         rht_scales, rht_ts, rht_amax, s);
+  // both casts from one read of x
+  dim3 grid((unsigned)((cols + kColCols - 1) / kColCols), (unsigned)((tokens + kColTok - 1) / kColTok));
+  const uint32_t row_key = sr_key(row_seed), rht_key = sr_key(rht_seed);
+#define ROW_RHT_LAUNCH(T, RR, RH)                                                                   \
+  k_cast_row_rht<T, RR, RH><<<grid, 256, 0, s>>>(static_cast<const T*>(x), tokens, cols, ld, sign_mask, \
+                                                 row_amax, row_codes, row_scales, row_ts, row_key,  \
+                                                 rht_amax, rht_codes, rht_scales, rht_ts, rht_key)
+#define ROW_RHT_RND(T)                                             \
+  if (row_rnd == 0) {                                              \
+    if (rht_rnd == 0) ROW_RHT_LAUNCH(T, 0, 0); else ROW_RHT_LAUNCH(T, 0, 1); \
+  } else {                                                         \
+    if (rht_rnd == 0) ROW_RHT_LAUNCH(T, 1, 0); else ROW_RHT_LAUNCH(T, 1, 1); \
+  }
+  if (dt == 0) {
+    ROW_RHT_RND(uint16_t)
+  } else {
+    ROW_RHT_RND(float)
+  }
+#undef ROW_RHT_RND
+#undef ROW_RHT_LAUNCH
+  return hipGetLastError();
 }
 
 }  // namespace nvfp4
