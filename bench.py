@@ -57,8 +57,8 @@ TOKENS, D_IN, D_OUT = 8192, 5120, 20480
 # (FETCH_SIZE 512 MiB, WRITE_SIZE 1024 MiB).  Valid only for the kernel
 # sources (gemm.hip + gemm_tiling.hpp) with this hash; any other source
 # reports null.
-GEMM_TRAFFIC = dict(src_sha256="a912034815f6f042db30e5a8111380afefb5ccfac7baf0515980562d9bdb811f",
-                    bytes_per_launch=1.1573e+09, fetch_bytes=7.0976e+08, write_bytes=4.4749e+08)
+GEMM_TRAFFIC = dict(src_sha256="7f5129de35e8b9ad04365ffe4c4513d0af42b458f3627081da41d50d0cf589c6",
+                    bytes_per_launch=1.1573e+09, fetch_bytes=7.0980e+08, write_bytes=4.4751e+08)
 GEMM_SOURCES = ("gemm.hip", "gemm_tiling.hpp")
 
 
