@@ -508,15 +508,80 @@ __global__ __launch_bounds__(256) void k_rht_amax(const T* __restrict__ x, int64
 }
 
 // ---------------------------------------------------------------------------
-// 2D tile cast: one scale per 16x16 tile.  A workgroup covers 64 x 64
-// elements; wave w takes rows 16w..16w+15, lane l holds row l%16 of tile
-// column l/16 (16 elements).  The tile amax is reduced over the 16 lanes of
+// 2D tile cast: one scale per 16x16 tile.  A workgroup covers 256 rows x 64
+// columns in four passes; in pass j wave w takes tile row 4j + w, lane l holds
+// row l%16 of tile column l/16 (16 elements).  The tile amax is reduced over the 16 lanes of
 // a tile.  Row-major codes go straight out (8 bytes per lane, 4 lanes per
-// 32-byte row piece); the transposed codes are rebuilt from an LDS copy of
-// the unpacked codes in column-major order.
+// 32-byte row piece).  The transposed codes are the same codes (one scale per
+// tile) read down the columns: the 16 lanes of a tile transpose their 16 x 16
+// nibble matrix in registers (below), and the packed columns are staged in LDS
+// so that each row of codes_t gets a whole 128-byte line per workgroup.
 // codes [rows][cols/2], scales [rows/16][cols/16],
 // codes_t [cols][rows/2], scales_t [cols/16][rows/16].
 // ---------------------------------------------------------------------------
+
+// Lane-xor exchange within each group of 32 lanes (ds_swizzle bit mode).
+template <int XOR>
+__device__ __forceinline__ uint32_t swz_xor(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, (XOR << 10) | 0x1F);
+}
+
+// Transpose of a 16 x 16 matrix of nibbles held by 16 consecutive lanes: on
+// entry lane r holds row r (nibble c of the 64-bit w1:w0 = column c), on exit
+// column r.  Four butterfly stages exchange ever smaller blocks between lanes
+// r and r ^ d (d = 8, 4, 2, 1): the upper-right block of each pair of rows
+// swaps with the lower-left one.
+__device__ __forceinline__ void transpose16x16_nibbles(uint32_t& w0, uint32_t& w1, int r) {
+  // d = 8: 8 x 8 blocks (whole words)
+  {
+    const bool hi = r & 8;
+    const uint32_t got = swz_xor<8>(hi ? w0 : w1);
+    if (hi) w0 = got; else w1 = got;
+  }
+  // d = 4: 4 x 4 blocks (16-bit halves of both words)
+  {
+    const bool hi = r & 4;
+    const uint32_t send = hi ? ((w0 & 0xFFFFu) | (w1 << 16)) : ((w0 >> 16) | (w1 & 0xFFFF0000u));
+    const uint32_t got = swz_xor<4>(send);
+    if (hi) {
+      w0 = (w0 & 0xFFFF0000u) | (got & 0xFFFFu);
+      w1 = (w1 & 0xFFFF0000u) | (got >> 16);
+    } else {
+      w0 = (w0 & 0xFFFFu) | (got << 16);
+      w1 = (w1 & 0xFFFFu) | (got & 0xFFFF0000u);
+    }
+  }
+  // d = 2: 2 x 2 blocks (bytes 1, 3 of the low lane <-> bytes 0, 2 of the high)
+  {
+    const bool hi = r & 2;
+    // v_perm(a, b, sel): selector byte values 0..3 take b's bytes, 4..7 a's
+    const uint32_t send = hi ? __builtin_amdgcn_perm(w1, w0, 0x06040200u)   // w0.b0, w0.b2, w1.b0, w1.b2
+                             : __builtin_amdgcn_perm(w1, w0, 0x07050301u);  // w0.b1, w0.b3, w1.b1, w1.b3
+    const uint32_t got = swz_xor<2>(send);  // the partner's four bytes, same order
+    if (hi) {
+      w0 = __builtin_amdgcn_perm(w0, got, 0x07010500u);  // got.b0, w0.b1, got.b1, w0.b3
+      w1 = __builtin_amdgcn_perm(w1, got, 0x07030502u);  // got.b2, w1.b1, got.b3, w1.b3
+    } else {
+      w0 = __builtin_amdgcn_perm(got, w0, 0x05020400u);  // w0.b0, got.b0, w0.b2, got.b1
+      w1 = __builtin_amdgcn_perm(got, w1, 0x07020600u);  // w1.b0, got.b2, w1.b2, got.b3
+    }
+  }
+  // d = 1: single nibbles (high nibbles of the even lane <-> low nibbles of the odd)
+  {
+    const bool hi = r & 1;
+    const uint32_t lo4 = 0x0F0F0F0Fu;
+    const uint32_t send = hi ? ((w0 & lo4) | ((w1 & lo4) << 4)) : (((w0 >> 4) & lo4) | (w1 & ~lo4));
+    const uint32_t got = swz_xor<1>(send);
+    if (hi) {
+      w0 = (w0 & ~lo4) | (got & lo4);
+      w1 = (w1 & ~lo4) | ((got >> 4) & lo4);
+    } else {
+      w0 = (w0 & lo4) | ((got & lo4) << 4);
+      w1 = (w1 & lo4) | (got & ~lo4);
+    }
+  }
+}
+
 template <typename T, int RND>
 __global__ __launch_bounds__(256) void k_cast_tile2d(const T* __restrict__ x, int64_t rows,
                                                      int64_t cols, int64_t ld,
@@ -526,78 +591,82 @@ __global__ __launch_bounds__(256) void k_cast_tile2d(const T* __restrict__ x, in
                                                      uint8_t* __restrict__ codes_t,
                                                      uint8_t* __restrict__ scales_t,
                                                      float* __restrict__ tensor_scale, uint32_t key) {
-  __shared__ __align__(16) uint8_t lt[64][64 + 16];  // [local col][local row], padded
+  __shared__ __align__(16) uint8_t lt[64][128];  // [local column][packed codes of the 256 rows]
   __shared__ float rtab[128];
   const float s_enc = encode_scale(amax[0]);
   if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) tensor_scale[0] = 1.0f / s_enc;
   fill_scale_table(rtab, s_enc);
   __syncthreads();
 
-  const int64_t r0 = (int64_t)blockIdx.y * 64;
-  const int64_t c0 = (int64_t)blockIdx.x * 64;
+  // consecutive workgroups take consecutive row regions of one column strip,
+  // so the transposed rows they write are contiguous in codes_t
+  const int64_t r0 = (int64_t)blockIdx.x * 256;
+  const int64_t c0 = (int64_t)blockIdx.y * 64;
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const int tc = lane >> 4;  // tile column in the region
   const int rr = lane & 15;  // row within the tile
-  const int lr = 16 * wave + rr;  // local row
-  const int64_t r = r0 + lr;
   const int64_t c = c0 + 16 * tc;
-  const bool tile_valid = (r0 + 16 * wave) < rows && c < cols;  // whole tile in or out
 
-  float v[16];
-  if (tile_valid) {
-    load8<T>(x + r * ld + c, v);
-    load8<T>(x + r * ld + c + 8, v + 8);
-  } else {
+  // tile rows 4j + wave of the region (16 rows each), one per iteration
+#pragma unroll 2
+  for (int j = 0; j < 4; j++) {
+    const int tr = 4 * j + wave;
+    const int64_t r = r0 + 16 * tr + rr;
+    const bool tile_valid = (r0 + 16 * tr) < rows && c < cols;  // whole tile in or out
+    float v[16];
+    if (tile_valid) {
+      load8<T>(x + r * ld + c, v);
+      load8<T>(x + r * ld + c + 8, v + 8);
+    } else {
 #pragma unroll
-    for (int e = 0; e < 16; e++) v[e] = 0.0f;
-  }
-  float am = 0.0f;
+      for (int e = 0; e < 16; e++) v[e] = 0.0f;
+    }
+    float am = 0.0f;
 #pragma unroll
-  for (int e = 0; e < 16; e++) am = fmaxf(am, fabsf(v[e]));
+    for (int e = 0; e < 16; e++) am = fmaxf(am, fabsf(v[e]));
 #pragma unroll
-  for (int off = 1; off < 16; off <<= 1) am = fmaxf(am, __shfl_xor(am, off));
-  uint32_t e_b;
-  float r_b;
-  block_scale(am, s_enc, rtab, e_b, r_b);
-  float s[16];
+    for (int off = 1; off < 16; off <<= 1) am = fmaxf(am, __shfl_xor(am, off));
+    uint32_t e_b;
+    float r_b;
+    block_scale(am, s_enc, rtab, e_b, r_b);
+    float sv[16];
 #pragma unroll
-  for (int e = 0; e < 16; e++) s[e] = v[e] * r_b;
-  const uint2 w = encode16<RND>(s, key, (uint32_t)(r * cols + c) >> 1);
-  const uint32_t w0 = w.x, w1 = w.y;
-  if (tile_valid) {
-    *reinterpret_cast<uint2*>(codes + r * (cols / 2) + c / 2) = make_uint2(w0, w1);
-    if (rr == 0) {
-      scales[(r / 16) * (cols / 16) + c / 16] = (uint8_t)e_b;
-      if (scales_t) scales_t[(c / 16) * (rows / 16) + r / 16] = (uint8_t)e_b;
+    for (int e = 0; e < 16; e++) sv[e] = v[e] * r_b;
+    const uint2 w = encode16<RND>(sv, key, (uint32_t)(r * cols + c) >> 1);
+    uint32_t w0 = w.x, w1 = w.y;
+    if (tile_valid) {
+      *reinterpret_cast<uint2*>(codes + r * (cols / 2) + c / 2) = make_uint2(w0, w1);
+      if (rr == 0) {
+        scales[(r / 16) * (cols / 16) + c / 16] = (uint8_t)e_b;
+        if (scales_t) scales_t[(c / 16) * (rows / 16) + r / 16] = (uint8_t)e_b;
+      }
+    }
+    if (codes_t != nullptr) {
+      // every lane of the wave takes part in the exchange (invalid tiles carry zeros)
+      transpose16x16_nibbles(w0, w1, rr);
+      // lane (tc, rr) now holds column c + rr of the tile's 16 rows
+      *reinterpret_cast<uint2*>(&lt[16 * tc + rr][8 * tr]) = make_uint2(w0, w1);
     }
   }
   if (codes_t == nullptr) return;
-  // unpacked codes, column-major in LDS
-#pragma unroll
-  for (int e = 0; e < 8; e++) {
-    lt[16 * tc + e][lr] = (uint8_t)((w0 >> (4 * e)) & 15u);
-    lt[16 * tc + 8 + e][lr] = (uint8_t)((w1 >> (4 * e)) & 15u);
-  }
   __syncthreads();
-  // thread -> (local column, quarter of the rows): 16 rows -> 8 bytes
+  // codes_t: 64 rows (local columns) of up to 128 bytes; 4 threads per row,
+  // 32 bytes each, so each row's line is written by one wave
   const int lc = threadIdx.x >> 2;
   const int q = threadIdx.x & 3;
   const int64_t ct = c0 + lc;
-  const int64_t rq = r0 + 16 * q;
-  if (ct < cols && rq < rows) {
-    uint4 b = *reinterpret_cast<const uint4*>(&lt[lc][16 * q]);
-    uint32_t in[4] = {b.x, b.y, b.z, b.w};
-    uint32_t out[2];
-#pragma unroll
-    for (int h = 0; h < 2; h++) {
-      uint32_t a0 = in[2 * h], a1 = in[2 * h + 1];
-      // bytes (codes) c0..c3 of a0 and c4..c7 of a1 -> nibbles
-      uint32_t o = (a0 & 0xFu) | ((a0 >> 4) & 0xF0u) | ((a0 >> 8) & 0xF00u) | ((a0 >> 12) & 0xF000u);
-      o |= ((a1 & 0xFu) | ((a1 >> 4) & 0xF0u) | ((a1 >> 8) & 0xF00u) | ((a1 >> 12) & 0xF000u)) << 16;
-      out[h] = o;
-    }
-    *reinterpret_cast<uint2*>(codes_t + ct * (rows / 2) + rq / 2) = make_uint2(out[0], out[1]);
+  if (ct >= cols) return;
+  const int64_t row_bytes = rows / 2;
+  const int64_t off = r0 / 2 + 32 * q;  // byte offset in the output row
+  uint8_t* dst = codes_t + ct * row_bytes + off;
+  const uint8_t* src = &lt[lc][32 * q];
+  if (off + 32 <= row_bytes && ((ct * row_bytes + off) & 15) == 0) {
+    reinterpret_cast<uint4*>(dst)[0] = reinterpret_cast<const uint4*>(src)[0];
+    reinterpret_cast<uint4*>(dst)[1] = reinterpret_cast<const uint4*>(src)[1];
+  } else {
+    for (int k = 0; k < 4 && off + 8 * k < row_bytes; k++)
+      reinterpret_cast<uint2*>(dst)[k] = reinterpret_cast<const uint2*>(src)[k];
   }
 }
 
@@ -667,7 +736,7 @@ static hipError_t launch_cast(const void* x, int dt, int64_t rows, int64_t cols,
     }
 #undef COL_LAUNCH
   } else {
-    dim3 grid((unsigned)((cols + 63) / 64), (unsigned)((rows + 63) / 64));
+    dim3 grid((unsigned)((rows + 255) / 256), (unsigned)((cols + 63) / 64));
 #define TILE_LAUNCH(T, R)                                                                  \
   k_cast_tile2d<T, R><<<grid, 256, 0, s>>>(static_cast<const T*>(x), rows, cols, ld, amax, \
                                            codes, scales, codes_t, scales_t, tensor_scale, key)
