@@ -178,7 +178,10 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mxfp4(
   // iteration may refill it without a second barrier.
   auto stage = [&](int kt, const uint8_t* __restrict__ cur, uint8_t* __restrict__ nxt) {
     const bool more = kt + 1 < kt1;
-    if (more) issue_stage(kt + 1, nxt);
+    // issued on the last stage too (clamped, in-row addresses; the data goes
+    // unused): without the branch around it the compiler interleaves the 20
+    // loads with this stage's first MFMAs and waits less before them
+    issue_stage(kt + 1, nxt);
     read_step(cur, 1, qa[1], qb[1]);
     MX_MFMAS(0, 0)
     read_step(cur, 2, qa[0], qb[0]);
