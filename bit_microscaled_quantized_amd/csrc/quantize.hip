@@ -476,33 +476,85 @@ __global__ __launch_bounds__(256) void k_cast_row_rht(
 }
 
 // amax of the RHT output (and, if amax_plain is not null, of the input itself,
-// from the same read): same thread mapping as the column cast.
+// from the same read).  A thread walks patches of 16 tokens x 4 columns (one
+// 8-byte load per row for bf16), grid-stride, loading the next patch while it
+// transforms the current one, so the reads stay in flight through the
+// transform work.  Lane-consecutive patches are column-consecutive, so a wave
+// reads 512 contiguous bytes per row.
+template <typename T>
+struct QuadTile;
+
+template <>
+struct QuadTile<uint16_t> {
+  uint2 w[16];
+  __device__ __forceinline__ void load(const uint16_t* p, int64_t ld) {
+#pragma unroll
+    for (int j = 0; j < 16; j++) w[j] = *reinterpret_cast<const uint2*>(p + j * ld);
+  }
+  __device__ __forceinline__ void column(int k, float* u) const {
+#pragma unroll
+    for (int j = 0; j < 16; j++) {
+      const uint32_t d = k < 2 ? w[j].x : w[j].y;
+      u[j] = (k & 1) ? bf16hi(d) : bf16lo(d);
+    }
+  }
+};
+
+template <>
+struct QuadTile<float> {
+  float4 w[16];
+  __device__ __forceinline__ void load(const float* p, int64_t ld) {
+#pragma unroll
+    for (int j = 0; j < 16; j++) w[j] = *reinterpret_cast<const float4*>(p + j * ld);
+  }
+  __device__ __forceinline__ void column(int k, float* u) const {
+#pragma unroll
+    for (int j = 0; j < 16; j++) u[j] = k == 0 ? w[j].x : k == 1 ? w[j].y : k == 2 ? w[j].z : w[j].w;
+  }
+};
+
+template <typename T>
+__device__ __forceinline__ void rht_amax_patch(const QuadTile<T>& t, uint32_t sign_mask, bool plain,
+                                               float& am, float& ap) {
+#pragma unroll
+  for (int k = 0; k < 4; k++) {
+    float u[16];
+    t.column(k, u);
+    if (plain) {
+#pragma unroll
+      for (int j = 0; j < 16; j++) ap = fmaxf(ap, fabsf(u[j]));
+    }
+    rht16(u, sign_mask);
+#pragma unroll
+    for (int j = 0; j < 16; j++) am = fmaxf(am, fabsf(u[j]));
+  }
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void k_rht_amax(const T* __restrict__ x, int64_t rows,
                                                   int64_t cols, int64_t ld, uint32_t sign_mask,
                                                   float* amax, float* amax_plain) {
-  const int64_t t0 = (int64_t)blockIdx.y * kColTok;
-  const int64_t c0 = (int64_t)blockIdx.x * kColCols;
-  const int co = threadIdx.x & 7;
-  const int g = threadIdx.x >> 3;
-  const int64_t tg = t0 + 16 * g;
-  const int64_t cc = c0 + 8 * co;
+  const uint32_t quads = (uint32_t)(cols / 4);            // column quads per 16-token band
+  const uint32_t units = (uint32_t)(rows / 16) * quads;   // patches (< 2^26: elements < 2^32)
+  const uint32_t stride = gridDim.x * 256u;
+  const bool plain = amax_plain != nullptr;
+  auto patch = [&](uint32_t p) {
+    const uint32_t band = p / quads, q = p - band * quads;
+    return x + (int64_t)band * 16 * ld + (int64_t)q * 4;
+  };
   float am = 0.0f, ap = 0.0f;
-  if (tg < rows && cc < cols) {
-    ColTile<T> tile;
-    tile.load(x + tg * ld + cc, ld);
-#pragma unroll
-    for (int k = 0; k < 8; k++) {
-      float u[16];
-      tile.column(k, u);
-      if (amax_plain != nullptr) {
-#pragma unroll
-        for (int j = 0; j < 16; j++) ap = fmaxf(ap, fabsf(u[j]));
-      }
-      rht16(u, sign_mask);
-#pragma unroll
-      for (int j = 0; j < 16; j++) am = fmaxf(am, fabsf(u[j]));
-    }
+  uint32_t p = blockIdx.x * 256u + threadIdx.x;
+  QuadTile<T> ta, tb;
+  if (p < units) ta.load(patch(p), ld);
+  while (p < units) {
+    const uint32_t pb = p + stride;
+    if (pb < units) tb.load(patch(pb), ld);
+    rht_amax_patch(ta, sign_mask, plain, am, ap);
+    if (pb >= units) break;
+    const uint32_t pa = pb + stride;
+    if (pa < units) ta.load(patch(pa), ld);
+    rht_amax_patch(tb, sign_mask, plain, am, ap);
+    p = pa;
   }
   block_atomic_max(__float_as_uint(am), amax, __float_as_uint(ap), amax_plain);
 }
@@ -754,7 +806,11 @@ static hipError_t launch_cast(const void* x, int dt, int64_t rows, int64_t cols,
 static hipError_t launch_rht_amax(const void* x, int dt, int64_t tokens, int64_t cols, int64_t ld,
                                   uint32_t sign_mask, float* amax, float* amax_plain, hipStream_t s) {
   k_zero_amax<<<1, 64, 0, s>>>(amax, amax_plain);
-  dim3 grid((unsigned)((cols + kColCols - 1) / kColCols), (unsigned)((tokens + kColTok - 1) / kColTok));
+  // patches of 16 tokens x 4 columns; at most 2048 workgroups, rounds balanced
+  const int64_t units = (tokens / 16) * (cols / 4);
+  const int64_t wgs = (units + 255) / 256;
+  const int64_t rounds = (wgs + 2047) / 2048;
+  const unsigned grid = grid_cap((wgs + rounds - 1) / rounds, 2048);
   if (dt == 0)
     k_rht_amax<uint16_t><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(x), tokens, cols, ld,
                                               sign_mask, amax, amax_plain);
