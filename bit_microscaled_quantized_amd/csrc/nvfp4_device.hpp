@@ -15,7 +15,6 @@ namespace nvfp4 {
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
-typedef float float2_t __attribute__((ext_vector_type(2)));
 
 constexpr float kFltMax = 3.402823466e+38f;
 
@@ -153,10 +152,6 @@ __device__ __forceinline__ uint32_t sr_code_c(float v, uint32_t rc) {
   const uint32_t x_lo = (uint32_t)__builtin_ceilf(a * 131072.0f);
   const uint32_t x = __builtin_unpredictable(b >= 0x3F800000u) ? x_hi : x_lo;
   return ((__float_as_uint(v) >> 28) & 8u) | ((x + rc) >> 16);
-}
-
-__device__ __forceinline__ uint32_t sr_code(float v, uint32_t r16) {
-  return sr_code_c(v, r16 ^ 0xFFFFu);
 }
 
 // Random bits of the SR hash: key = pcg(lo32(seed) ^ pcg(hi32(seed))); one

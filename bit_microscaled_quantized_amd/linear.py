@@ -31,9 +31,6 @@ class Quantized:
     codes_t: object = None
     scales_t: object = None
 
-    def transposed(self) -> "Quantized":
-        return Quantized(self.codes_t, self.scales_t, self.ts, self.amax)
-
 
 def _alloc_q(torch, rows_out, bytes_per_row, scale_rows, scale_cols, dev, t_shape=None):
     u8 = dict(dtype=torch.uint8, device=dev)
