@@ -234,6 +234,33 @@ def test_e2m1_conversion_sweep(ora):
         _same(g, o, KEYS)
 
 
+def test_e2m1_conversion_exhaustive(ora):
+    """Every FP32 bit pattern with |x| <= 6 (1.09e9 magnitudes; every third
+    block negated) through the row cast, RNE and SR, against the oracle, in
+    chunks of 4M blocks.  Each block holds a +-6 anchor and 15 test values, so
+    amax_t = 6, S_enc = 448, e_b = 0x7E, r_b = 1 and the cast sees v = x."""
+    top = int(np.float32(6.0).view(np.uint32)) + 1
+    blocks = 1 << 22
+    per = 15 * blocks
+    for rnd in (nv.NVFP4_RNE, nv.NVFP4_SR):
+        checked = 0
+        for start in range(0, top, per):
+            u = np.arange(start, min(start + per, top), dtype=np.uint32)
+            checked += len(u)
+            probe = np.zeros(per, np.float32)
+            probe[: len(u)] = u.view(np.float32)
+            x = np.empty((blocks, 16), np.float32)
+            x[:, 0] = np.where(np.arange(blocks) % 2 == 0, 6.0, -6.0)
+            x[:, 1:] = probe.reshape(blocks, 15)
+            x[1::3, 1:] *= -1
+            x = x.reshape(-1, 4096)
+            seed = 17 + start
+            g = gpuio.gpu_quantize(x, nv.NVFP4_ROW_1D, rnd, seed)
+            o = ora.quantize(x, ora.ROW_1D, rnd, seed)
+            _same(g, o, KEYS)
+        assert checked == top
+
+
 def test_sr_is_unbiased_on_gpu():
     """Mean of SR-dequantized values over many seeds approaches the input:
     each draw is within one grid step of x, so the mean of n draws lies within
