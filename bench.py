@@ -57,8 +57,8 @@ TOKENS, D_IN, D_OUT = 8192, 5120, 20480
 # (FETCH_SIZE 512 MiB, WRITE_SIZE 1024 MiB).  Valid only for the kernel
 # sources (gemm.hip + gemm_tiling.hpp) with this hash; any other source
 # reports null.
-GEMM_TRAFFIC = dict(src_sha256="7f5129de35e8b9ad04365ffe4c4513d0af42b458f3627081da41d50d0cf589c6",
-                    bytes_per_launch=1.1573e+09, fetch_bytes=7.0980e+08, write_bytes=4.4751e+08)
+GEMM_TRAFFIC = dict(src_sha256="d9aa8b7359bb0f9b8f22da021987d3b8164ca536f12b478f6a465e6b86a25ae1",
+                    bytes_per_launch=1.1573e+09, fetch_bytes=7.0982e+08, write_bytes=4.4747e+08)
 GEMM_SOURCES = ("gemm.hip", "gemm_tiling.hpp")
 
 

@@ -41,6 +41,8 @@ nvfp4_status gemm_common(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes
   if (beta != 0.0f && beta != 1.0f) return NVFP4_EINVAL;
   nvfp4_status st = check_gemm_shape(M, N, K);
   if (st != NVFP4_OK) return st;
+  // the kernel addresses each operand's codes with 32-bit offsets
+  if (M * (K / 2) >= (int64_t(1) << 32) || N * (K / 2) >= (int64_t(1) << 32)) return NVFP4_ESHAPE;
   if (ldc < N || workspace_bytes < 0) return NVFP4_ESHAPE;
   if (!aligned16(a_codes) || !aligned16(b_codes) || !aligned4(a_scales) || !aligned4(b_scales) ||
       !aligned4(a_tensor_scale) || !aligned4(b_tensor_scale) || !aligned16(c) ||

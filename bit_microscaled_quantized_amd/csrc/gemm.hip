@@ -144,24 +144,57 @@ __global__ __launch_bounds__(512, 1) void k_gemm_nvfp4(
   const int cchunk_e = (lane & 7) ^ (crow >> 1);        // even j
   const int cchunk_o = (lane & 7) ^ (4 + (crow >> 1));  // odd j
   const int sdw = lane & 3;
+  // Per-lane 32-bit offsets of each fetch from its operand's first byte
+  // (code and scale arrays are below 4 GiB, checked by the host): row start
+  // plus the lane's chunk or dword.  They stay fixed over the K loop; a full
+  // stage adds its wave-uniform start, kt * 128 code bytes (kt * 16 scale
+  // bytes), as a scalar base, so the fetch holds 12 offset registers rather
+  // than 12 64-bit row pointers.
+  uint32_t o_a[4], o_b[4], o_sa[2], o_sb[2];
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    const int r = 8 * (4 * wave + j) + crow;
+    const int c16 = 16 * ((j & 1) ? cchunk_o : cchunk_e);
+    o_a[j] = (uint32_t)min(m0 + r, M - 1) * (uint32_t)kb + c16;
+    o_b[j] = (uint32_t)min(n0 + r, N - 1) * (uint32_t)kb + c16;
+  }
+#pragma unroll
+  for (int i = 0; i < 2; i++) {
+    const int r = 32 * wave + 16 * i + (lane >> 2);
+    o_sa[i] = (uint32_t)min(m0 + r, M - 1) * (uint32_t)ks + 4 * sdw;
+    o_sb[i] = (uint32_t)(min(n0 + r, N - 1) / b_rowdiv) * (uint32_t)ks + 4 * sdw;
+  }
+  const uint32_t c16e = 16 * cchunk_e, c16o = 16 * cchunk_o, s4 = 4 * sdw;
   auto issue_stage = [&](int kt, uint8_t* st) {
-    // in-row byte offsets, clamped to the row's last chunk / dword
-    const int64_t coff_e = min((int64_t)kt * (BKS / 2) + 16 * cchunk_e, kb - 16);
-    const int64_t coff_o = min((int64_t)kt * (BKS / 2) + 16 * cchunk_o, kb - 16);
-    const int64_t soff = min((int64_t)kt * (BKS / 16) + 4 * sdw, ks - 4);
+    const uint8_t* ab = a_codes + kt * (BKS / 2);
+    const uint8_t* bb = b_codes + kt * (BKS / 2);
+    const uint8_t* asb = a_scales + kt * (BKS / 16);
+    const uint8_t* bsb = b_scales + kt * (BKS / 16);
+    // In a stage that ends past K, each in-row offset is clamped to the row's
+    // last chunk (dword), so every address stays inside its row: the lane's
+    // offset moves back by d (mod 2^32; the clamped offset is >= 0).
+    uint32_t de = 0, dod = 0, dsc = 0;
+    if ((kt + 1) * BKS > K) {
+      const uint32_t ck = (uint32_t)kt * (BKS / 2), sk = (uint32_t)kt * (BKS / 16);
+      de = min(ck + c16e, (uint32_t)kb - 16) - (ck + c16e);
+      dod = min(ck + c16o, (uint32_t)kb - 16) - (ck + c16o);
+      dsc = min(sk + s4, (uint32_t)ks - 4) - (sk + s4);
+    }
+    // (the empty asm keeps each offset a 32-bit register at the load, so
+    // the load takes the scalar-base + 32-bit-offset form)
 #pragma unroll
     for (int j = 0; j < 4; j++) {
-      const int r = 8 * (4 * wave + j) + crow;
-      const int64_t coff = (j & 1) ? coff_o : coff_e;
-      load_lds16(a_codes + (int64_t)min(m0 + r, M - 1) * kb + coff, st + (4 * wave + j) * 1024);
-      load_lds16(b_codes + (int64_t)min(n0 + r, N - 1) * kb + coff, st + OFF_B + (4 * wave + j) * 1024);
+      uint32_t oa = o_a[j] + ((j & 1) ? dod : de), ob = o_b[j] + ((j & 1) ? dod : de);
+      asm volatile("" : "+v"(oa), "+v"(ob));
+      load_lds16(ab + oa, st + (4 * wave + j) * 1024);
+      load_lds16(bb + ob, st + OFF_B + (4 * wave + j) * 1024);
     }
 #pragma unroll
     for (int i = 0; i < 2; i++) {
-      const int r = 32 * wave + 16 * i + (lane >> 2);
-      load_lds4(a_scales + (int64_t)min(m0 + r, M - 1) * ks + soff, st + OFF_SA + (2 * wave + i) * 256);
-      load_lds4(b_scales + (int64_t)(min(n0 + r, N - 1) / b_rowdiv) * ks + soff,
-                st + OFF_SB + (2 * wave + i) * 256);
+      uint32_t oa = o_sa[i] + dsc, ob = o_sb[i] + dsc;
+      asm volatile("" : "+v"(oa), "+v"(ob));
+      load_lds4(asb + oa, st + OFF_SA + (2 * wave + i) * 256);
+      load_lds4(bsb + ob, st + OFF_SB + (2 * wave + i) * 256);
     }
   };
   // In a stage that ends past K, zero the scale bytes of blocks >= K/16: their
@@ -205,10 +238,10 @@ __global__ __launch_bounds__(512, 1) void k_gemm_nvfp4(
   uint4 qa[2][4], qb[2][2];
   uint32_t qsa[2][4], qsb[2][2];
 
-  // 4 MFMA steps on the quad in buffer p: per step, convert the 6 fragments
-  // (48 VALU) and issue 8 MFMAs; the other wave on the SIMD overlaps them
-  auto quad = [&](int p) {
-    half2_t sca[4][2], scb[2][2];
+  // MFMA steps s0 .. s1-1 of the quad in buffer p: per step, convert the 6
+  // fragments (48 VALU) and issue 8 MFMAs; the other wave on the SIMD
+  // overlaps them.  sca / scb: the quad's block scales as FP16 pairs.
+  auto quad_scales = [&](int p, half2_t (&sca)[4][2], half2_t (&scb)[2][2]) {
 #pragma unroll
     for (int i = 0; i < 4; i++) {
       half2_t v = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(qsa[p][i], 1.0f, false);
@@ -221,8 +254,10 @@ __global__ __launch_bounds__(512, 1) void k_gemm_nvfp4(
       scb[j][0] = half2_t{v[0], v[0]};
       scb[j][1] = half2_t{v[1], v[1]};
     }
+  };
+  auto quad_steps = [&](int p, int s0, int s1, const half2_t (&sca)[4][2], const half2_t (&scb)[2][2]) {
 #pragma unroll
-    for (int s = 0; s < 4; s++) {
+    for (int s = s0; s < s1; s++) {
       half8_t fa[4], fb[2];
 #pragma unroll
       for (int i = 0; i < 4; i++) fa[i] = dequant8(dw(qa[p][i], s), sca[i][s >> 1]);
@@ -234,6 +269,11 @@ __global__ __launch_bounds__(512, 1) void k_gemm_nvfp4(
         for (int j = 0; j < 2; j++)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[i], fb[j], acc[i][j], 0, 0, 0);
     }
+  };
+  auto quad = [&](int p) {
+    half2_t sca[4][2], scb[2][2];
+    quad_scales(p, sca, scb);
+    quad_steps(p, 0, 4, sca, scb);
   };
 
   // prologue: stage kt0 in buffer 0, its quad 0 read
@@ -252,15 +292,30 @@ __global__ __launch_bounds__(512, 1) void k_gemm_nvfp4(
     const bool more = kt + 1 < kt1;
     if (more) issue_stage(kt + 1, nxt);
     // quads 0..2: read the following quad of this stage while computing
+    // (the reads are placed after the quad's first step, so they have three
+    // steps of MFMAs to land before the next quad waits for them)
 #pragma unroll
     for (int g = 0; g < 3; g++) {
       const int p = g & 1;
+      half2_t sca[4][2], scb[2][2];
+      quad_scales(p, sca, scb);
+      quad_steps(p, 0, 1, sca, scb);
+      __builtin_amdgcn_sched_barrier(8);
       read_quad(cur, g + 1, qa[p ^ 1], qb[p ^ 1], qsa[p ^ 1], qsb[p ^ 1]);
-      quad(p);
+      __builtin_amdgcn_sched_barrier(8);
+      quad_steps(p, 1, 4, sca, scb);
+#pragma unroll
+      for (int k = 0; k < 24; k++) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+      }
+      __builtin_amdgcn_sched_barrier(8);
     }
-    // quad 3 (buffer 1): the next stage becomes visible, its quad 0 is read
-    // into buffer 0 while this stage's last quad is computed, and a final
-    // barrier releases this stage's LDS buffer for the next prefetch.
+    // quad 3 (buffer 1): the next stage becomes visible, and its quad 0 is
+    // read into buffer 0 while this stage's last quad is computed.  Every wave
+    // reaches this barrier with its last reads of cur complete (quad 3 came
+    // in during quad 2, and the wait covers LDS reads too), so the barrier
+    // also releases cur for the prefetch the next stage issues into it.
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (more) {
@@ -272,7 +327,6 @@ __global__ __launch_bounds__(512, 1) void k_gemm_nvfp4(
       read_quad(nxt, 0, qa[0], qb[0], qsa[0], qsb[0]);
     }
     quad(1);
-    __syncthreads();
   };
   for (int kt = kt0; kt < kt1; kt++) {
     uint8_t* cur = lds + ((kt - kt0) & 1) * STAGE_BYTES;

@@ -150,7 +150,8 @@ nvfp4_status nvfp4_quantize_row_rht(const void *x, int dt, int64_t tokens, int64
  *   Wgrad dW = dY^T X: A = RHT(dY) column-1D, B = RHT(X) column-1D (rowdiv 1),
  *                      K = tokens.
  *   M and N must be positive multiples of 16, K a positive multiple of 64 (all
- *   below 2^31); ldc >= N and a multiple of 4; c 16-byte aligned.
+ *   below 2^31), and each operand's code array below 4 GiB (M*K/2 and N*K/2 <
+ *   2^32); ldc >= N and a multiple of 4; c 16-byte aligned.
  *   Products e2m1 * E4M3 are exact in FP16, so the kernel dequantizes the
  *   block-scaled operands exactly and contracts them on FP16 matrix cores with
  *   FP32 accumulation; the two tensor scales are applied in the epilogue.

@@ -150,6 +150,8 @@ def g(**kw):
     (dict(K=96), b.NVFP4_ESHAPE),
     (dict(K=0), b.NVFP4_ESHAPE),
     (dict(ldc=128), b.NVFP4_ESHAPE),
+    (dict(M=1 << 20, K=1 << 13), b.NVFP4_ESHAPE),                  # A codes of 4 GiB
+    (dict(N=1 << 20, K=1 << 13, ldc=1 << 20), b.NVFP4_ESHAPE),     # B codes of 4 GiB
     (dict(a_codes=FAKE + 4), b.NVFP4_EALIGN),
     (dict(c=FAKE + 4), b.NVFP4_EALIGN),
     (dict(ldc=258), b.NVFP4_EALIGN),
