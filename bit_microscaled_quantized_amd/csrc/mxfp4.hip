@@ -35,19 +35,13 @@ __device__ __forceinline__ uint4 mx_encode32(const float* v, uint32_t key, uint3
   if constexpr (RND == 0) {
     return make_uint4(pack8_rne(v), pack8_rne(v + 8), pack8_rne(v + 16), pack8_rne(v + 24));
   } else {
-    uint32_t w[4] = {0u, 0u, 0u, 0u};
+    uint32_t w[4];
 #pragma unroll
     for (int half = 0; half < 2; half++) {
       uint32_t h[8];
       pcg8(key, pair0 + 8 * half, h);
-#pragma unroll
-      for (int p = 0; p < 8; p++) {
-        const uint32_t nh = ~h[p];
-        const int q = 8 * half + p;  // pair index within the block
-        const uint32_t c0 = sr_code_c(v[2 * q], nh & 0xFFFFu);
-        const uint32_t c1 = sr_code_c(v[2 * q + 1], nh >> 16);
-        w[q >> 2] |= (c0 | (c1 << 4)) << (8 * (q & 3));
-      }
+      w[2 * half] = sr_pack8(v + 16 * half, h);
+      w[2 * half + 1] = sr_pack8(v + 16 * half + 8, h + 4);
     }
     return make_uint4(w[0], w[1], w[2], w[3]);
   }

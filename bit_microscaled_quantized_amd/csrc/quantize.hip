@@ -129,8 +129,8 @@ __device__ __forceinline__ void load8<float>(const float* p, float* v) {
   v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
 }
 
-// Encode 16 scaled values (one block): RNE through the hardware conversion,
-// SR in software with pcg bits of output elements 2 pair0 .. 2 pair0 + 15
+// Encode 16 scaled values (one block): RNE and SR through the hardware
+// conversions, SR with pcg bits of output elements 2 pair0 .. 2 pair0 + 15
 // (pair0 a multiple of 8).  Element 0 lands in the low nibble of x.
 template <int RND>
 __device__ __forceinline__ uint2 encode16(const float* v, uint32_t key, uint32_t pair0) {
@@ -139,15 +139,7 @@ __device__ __forceinline__ uint2 encode16(const float* v, uint32_t key, uint32_t
   } else {
     uint32_t h[8];
     pcg8(key, pair0, h);
-    uint32_t w[2] = {0u, 0u};
-#pragma unroll
-    for (int p = 0; p < 8; p++) {
-      const uint32_t nh = ~h[p];  // 65535 - r16 in each half
-      const uint32_t c0 = sr_code_c(v[2 * p], nh & 0xFFFFu);
-      const uint32_t c1 = sr_code_c(v[2 * p + 1], nh >> 16);
-      w[p >> 2] |= (c0 | (c1 << 4)) << (8 * (p & 3));
-    }
-    return make_uint2(w[0], w[1]);
+    return make_uint2(sr_pack8(v, h), sr_pack8(v + 8, h + 4));
   }
 }
 
@@ -161,15 +153,7 @@ __device__ __forceinline__ uint32_t encode8(const float* v, uint32_t key, uint32
   } else {
     uint32_t h[4];
     pcg4(key, pair0, h);
-    uint32_t w = 0u;
-#pragma unroll
-    for (int p = 0; p < 4; p++) {
-      const uint32_t nh = ~h[p];
-      const uint32_t c0 = sr_code_c(v[2 * p], nh & 0xFFFFu);
-      const uint32_t c1 = sr_code_c(v[2 * p + 1], nh >> 16);
-      w |= (c0 | (c1 << 4)) << (8 * p);
-    }
-    return w;
+    return sr_pack8(v, h);
   }
 }
 
