@@ -135,7 +135,7 @@ __host__ __device__ __forceinline__ uint32_t pcg_host(uint32_t v) {
 // Stochastic rounding of scaled values to E2M1 codes: with a = min(|v|, 6),
 // lo the largest E2M1 magnitude <= a and hi the next one, round up iff
 // r16 < (a - lo) / (hi - lo) * 65536, sign kept.  It runs on gfx950's
-// v_cvt_scalef32_sr_pk_fp4_f32 (scale 1.0), whose rule was measured on the
+// v_cvt_scalef32_sr_pk_fp4_f32, whose rule was measured on the
 // device: sign-magnitude; with F the 22 bits of (a - lo) / (hi - lo) below
 // the grid point, truncated, element 0 of the pair rounds up iff
 // F + R[31:10] >= 2^22 and element 1 iff F + R[30:9] >= 2^22 (R the 32-bit
@@ -151,25 +151,29 @@ __host__ __device__ __forceinline__ uint32_t pcg_host(uint32_t v) {
 // The two elements of a pair draw independent bits, so each pair goes through
 // two conversions, one correct in its low nibble (element 0) and one in its
 // high nibble (element 1), merged by one bit select per 8 codes.
+// The conversion divides its input by the scale operand's power of two, so
+// the rounded-up input is passed as ceil(|v| * 2^23) with v's sign and the
+// scale as 2^23: the division is exact and the multiply back is saved.
 __device__ __forceinline__ float sr_hw_input(float v) {
   const float t = __builtin_ceilf(__builtin_fabsf(v) * 8388608.0f);  // exact: |v| < 2^105
-  return __builtin_copysignf(t, v) * 0x1p-23f;                        // exact
+  return __builtin_copysignf(t, v);
 }
 
-// One SR conversion into byte `sel` of d, the other bytes of d kept.  Written
-// as inline asm with d read-write: the compiler's builtin for this instruction
-// does not tie its `old` operand to the destination, so the kept bytes would
-// be whatever the destination register held.
+// One SR conversion (scale 2^23) into byte `sel` of d, the other bytes of d
+// kept.  Written as inline asm with d read-write: the compiler's builtin for
+// this instruction does not tie its `old` operand to the destination, so the
+// kept bytes would be whatever the destination register held.
 template <int sel>
 __device__ __forceinline__ void cvt_sr_pk(uint32_t& d, double x, uint32_t r) {
+  const float s = 8388608.0f;  // 2^23 (no literal operand in this encoding: an SGPR)
   if constexpr (sel == 0)
-    asm volatile("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, 1.0" : "+v"(d) : "v"(x), "v"(r));
+    asm volatile("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, %3" : "+v"(d) : "v"(x), "v"(r), "s"(s));
   else if constexpr (sel == 1)
-    asm volatile("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, 1.0 op_sel:[0,0,1,0]" : "+v"(d) : "v"(x), "v"(r));
+    asm volatile("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, %3 op_sel:[0,0,1,0]" : "+v"(d) : "v"(x), "v"(r), "s"(s));
   else if constexpr (sel == 2)
-    asm volatile("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, 1.0 op_sel:[0,0,0,1]" : "+v"(d) : "v"(x), "v"(r));
+    asm volatile("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, %3 op_sel:[0,0,0,1]" : "+v"(d) : "v"(x), "v"(r), "s"(s));
   else
-    asm volatile("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, 1.0 op_sel:[0,0,1,1]" : "+v"(d) : "v"(x), "v"(r));
+    asm volatile("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, %3 op_sel:[0,0,1,1]" : "+v"(d) : "v"(x), "v"(r), "s"(s));
 }
 
 template <int sel>
