@@ -24,7 +24,9 @@ tensor scale, no Hadamard) row and column quantization of W, X (RNE) and dY
 (SR), then the same three GEMMs on the block-scaled FP4 matrix instruction.
 `components.linear_module` times the autograd layer (NVFP4Linear forward +
 backward with BF16 outputs) against the same layer kept in BF16, and the
-NVFP4 -> BF16 dequantization of W.
+NVFP4 -> BF16 dequantization of W.  `components.hbm_copy_GBps` is the
+achievable HBM rate measured live (an elementwise kernel reading and writing
+1 GiB each), the reference for the quantize rates beside the 8 TB/s peak.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
 """
@@ -194,6 +196,19 @@ def _events_ms(torch, fn, steps, warmup):
     return a.elapsed_time(b) / steps
 
 
+def copy_bench(mib=1024, steps=10, warmup=3):
+    """Achievable HBM rate on this GPU: an elementwise kernel (torch.neg) that
+    reads and writes `mib` MiB each, read + write bytes per second (GB/s)."""
+    import torch
+    n = (mib << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    ms = _events_ms(torch, lambda: torch.neg(src, out=dst), steps, warmup)
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2.0 * (mib << 20) / (ms * 1e-3) / 1e9
+
+
 def module_bench(x, w, dy, st, steps, warmup):
     """The autograd layer on the same tensors: NVFP4Linear forward + backward
     (quantize, Fprop, Dgrad, Wgrad, BF16 outputs) against the same layer kept
@@ -345,6 +360,7 @@ def main():
         sys.exit(2)
     inp = make_inputs()
     ms_step, per, mx, mod = gpu_bench(inp, args.steps, args.warmup)
+    copy_gbs = copy_bench()
     if args.copy_probe_mib:
         import torch
         # an elementwise kernel (not a DMA copy, which no counter sees) that
@@ -404,6 +420,8 @@ def main():
         "components": {
             "quantize_GBps": round(q_gbs, 1),
             "quantize_frac_hbm": round(q_gbs / HBM_PEAK_GBS, 4),
+            "hbm_copy_GBps": round(copy_gbs, 1),
+            "quantize_frac_of_copy": round(q_gbs / copy_gbs, 4),
             "gemm_TFLOPs": round(gemm_tflops, 2),
             "gemm_frac_mfma_f16": round(gemm_tflops / MFMA_F16_PEAK, 4),
             "gemm_frac_mfma_fp4": round(gemm_tflops / MFMA_FP4_PEAK, 4),
