@@ -27,6 +27,10 @@ backward with BF16 outputs) against the same layer kept in BF16, and the
 NVFP4 -> BF16 dequantization of W.  `components.hbm_copy_GBps` is the
 achievable HBM rate measured live (an elementwise kernel reading and writing
 1 GiB each), the reference for the quantize rates beside the 8 TB/s peak.
+`components.quantize_sweep` times the quantize-only workload on its own
+tensors (bf16 8192x5120 and 8192x20480, N(0,1) with 0.1% 100x outliers):
+one row-1D nvfp4_quantize call each (tensor amax pass + cast pass), RNE and
+SR, with the algorithmic bytes of the call (input once, codes, scales).
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
 """
@@ -321,6 +325,42 @@ def mx_bench(x, w, dy, s_row, s_col, steps, warmup):
     }
 
 
+def sweep_bench(steps, warmup):
+    """The quantize-only workload: each bf16 tensor quantized row-1D by one
+    nvfp4_quantize call (zero amax, tensor amax pass, cast pass), RNE and SR,
+    mean HIP-event time per call on the current stream.  GB/s counts the
+    call's algorithmic bytes: the input read once (2 B/elem), codes
+    (0.5 B/elem) and E4M3 scales (1/16 B/elem)."""
+    import torch
+    import bit_microscaled_quantized_amd as nv
+    from bit_microscaled_quantized_amd import synth
+    dev = torch.device("cuda", 0)
+    u8 = dict(dtype=torch.uint8, device=dev)
+    out = {}
+    for which in (0, 1):
+        xb = synth.f32_to_bf16_bits(synth.quantize_sweep(which))
+        R, C = xb.shape
+        x = torch.from_numpy(xb.view(np.int16)).to(dev)
+        codes, scales = torch.empty((R, C // 2), **u8), torch.empty((R, C // 16), **u8)
+        ts = torch.empty(1, dtype=torch.float32, device=dev)
+        am = torch.empty(1, dtype=torch.float32, device=dev)
+        nbytes = R * C * 2 + R * C // 2 + R * C // 16
+        for rname, rnd, seed in (("rne", nv.NVFP4_RNE, 0), ("sr", nv.NVFP4_SR, 3)):
+            ms = _events_ms(torch, lambda: nv.nvfp4_quantize(
+                x, nv.NVFP4_BF16, R, C, C, nv.NVFP4_ROW_1D, rnd, seed, codes, scales, None, None,
+                ts, am), steps, warmup)
+            gbs = nbytes / (ms * 1e-3) / 1e9
+            out[f"{R}x{C}_{rname}"] = dict(ms=round(ms, 4), GBps=round(gbs, 1),
+                                          frac_hbm=round(gbs / HBM_PEAK_GBS, 4), bytes=nbytes)
+        del x, codes, scales
+        torch.cuda.empty_cache()
+    tot_b = sum(v["bytes"] for v in out.values())
+    tot_ms = sum(v["ms"] for v in out.values())
+    out["all"] = dict(GBps=round(tot_b / (tot_ms * 1e-3) / 1e9, 1),
+                      frac_hbm=round(tot_b / (tot_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4))
+    return out
+
+
 def cpu_baseline(inp, tokens):
     """The oracle, as it stands, on the same step restricted to the first
     `tokens` tokens (full weight): five quantizations plus the three FP64
@@ -361,6 +401,7 @@ def main():
     inp = make_inputs()
     ms_step, per, mx, mod = gpu_bench(inp, args.steps, args.warmup)
     copy_gbs = copy_bench()
+    sweep = sweep_bench(args.steps, args.warmup)
     if args.copy_probe_mib:
         import torch
         # an elementwise kernel (not a DMA copy, which no counter sees) that
@@ -422,6 +463,7 @@ def main():
             "quantize_frac_hbm": round(q_gbs / HBM_PEAK_GBS, 4),
             "hbm_copy_GBps": round(copy_gbs, 1),
             "quantize_frac_of_copy": round(q_gbs / copy_gbs, 4),
+            "quantize_sweep": sweep,
             "gemm_TFLOPs": round(gemm_tflops, 2),
             "gemm_frac_mfma_f16": round(gemm_tflops / MFMA_F16_PEAK, 4),
             "gemm_frac_mfma_fp4": round(gemm_tflops / MFMA_FP4_PEAK, 4),

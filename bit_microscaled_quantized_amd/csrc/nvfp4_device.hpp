@@ -133,63 +133,57 @@ __host__ __device__ __forceinline__ uint32_t pcg_host(uint32_t v) {
 }
 
 // Stochastic rounding of scaled values to E2M1 codes: with a = min(|v|, 6),
-// lo the largest E2M1 magnitude <= a and hi the next one, round up iff
-// r16 < (a - lo) / (hi - lo) * 65536, sign kept.  It runs on gfx950's
-// v_cvt_scalef32_sr_pk_fp4_f32, whose rule was measured on the
-// device: sign-magnitude; with F the 22 bits of (a - lo) / (hi - lo) below
-// the grid point, truncated, element 0 of the pair rounds up iff
-// F + R[31:10] >= 2^22 and element 1 iff F + R[30:9] >= 2^22 (R the 32-bit
-// random operand); a >= 6 gives magnitude code 7.  Two adjustments turn that
-// into the rule above exactly:
-//   * the fraction must count as ceil(frac * 2^22).  For a >= 1 it is an exact
-//     22-bit integer; for a < 1 the input is first rounded up in magnitude to
-//     a multiple of 2^-23 (sr_hw_input), which leaves every a >= 1 unchanged;
-//   * r16 < frac * 65536 is 64 r16 < ceil(frac * 2^22), i.e.
-//     F + (2^22 - 1 - 64 r16) >= 2^22, so the element's field must hold
-//     2^22 - 1 - 64 r16: R = ~(r16 << 16) for element 0 (low 10 bits free) and
-//     (~r16 << 15) | 0x7FFF for element 1 (low 9 bits free).
+// lo the largest E2M1 magnitude <= a, hi the next one and F = floor(frac *
+// 2^22) the fraction frac = (a - lo) / (hi - lo) truncated to 22 bits, round
+// up iff F > 64 r16 (r16 the element's 16 random bits), sign kept.  It runs
+// on gfx950's v_cvt_scalef32_sr_pk_fp4_f32, whose rule was measured on the
+// device: sign-magnitude; with F as above, element 0 of the pair rounds up
+// iff F + R[31:10] >= 2^22 and element 1 iff F + R[30:9] >= 2^22 (R the
+// 32-bit random operand); a >= 6 gives magnitude code 7.  F > 64 r16 is
+// F + (2^22 - 1 - 64 r16) >= 2^22, so the element's field must hold
+// 2^22 - 1 - 64 r16: R = ~(r16 << 16) for element 0 (low 10 bits free) and
+// (~r16 << 15) | 0x7FFF for element 1 (low 9 bits free).  The scaled values
+// go in as they are, with scale operand 1.0.
 // The two elements of a pair draw independent bits, so each pair goes through
 // two conversions, one correct in its low nibble (element 0) and one in its
 // high nibble (element 1), merged by one bit select per 8 codes.
-// The conversion divides its input by the scale operand's power of two, so
-// the rounded-up input is passed as ceil(|v| * 2^23) with v's sign and the
-// scale as 2^23: the division is exact and the multiply back is saved.
-__device__ __forceinline__ float sr_hw_input(float v) {
-  const float t = __builtin_ceilf(__builtin_fabsf(v) * 8388608.0f);  // exact: |v| < 2^105
-  return __builtin_copysignf(t, v);
-}
 
-// One SR conversion (scale 2^23) into byte `sel` of d, the other bytes of d
+// One SR conversion (scale 1.0) into byte `sel` of d, the other bytes of d
 // kept.  Written as inline asm with d read-write: the compiler's builtin for
 // this instruction does not tie its `old` operand to the destination, so the
-// kept bytes would be whatever the destination register held.
-template <int sel>
+// kept bytes would be whatever the destination register held.  The first
+// conversion into a word (FIRST) writes byte 0 and leaves bytes that later
+// conversions overwrite, so its destination needs no initial value.
+template <int sel, bool FIRST = false>
 __device__ __forceinline__ void cvt_sr_pk(uint32_t& d, double x, uint32_t r) {
-  const float s = 8388608.0f;  // 2^23 (no literal operand in this encoding: an SGPR)
-  if constexpr (sel == 0)
-    asm volatile("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, %3" : "+v"(d) : "v"(x), "v"(r), "s"(s));
-  else if constexpr (sel == 1)
-    asm volatile("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, %3 op_sel:[0,0,1,0]" : "+v"(d) : "v"(x), "v"(r), "s"(s));
-  else if constexpr (sel == 2)
-    asm volatile("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, %3 op_sel:[0,0,0,1]" : "+v"(d) : "v"(x), "v"(r), "s"(s));
-  else
-    asm volatile("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, %3 op_sel:[0,0,1,1]" : "+v"(d) : "v"(x), "v"(r), "s"(s));
+  if constexpr (FIRST) {
+    static_assert(sel == 0, "only the byte-0 conversion starts a word");
+    asm volatile("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, 1.0" : "=v"(d) : "v"(x), "v"(r));
+  } else if constexpr (sel == 0) {
+    asm volatile("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, 1.0" : "+v"(d) : "v"(x), "v"(r));
+  } else if constexpr (sel == 1) {
+    asm volatile("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, 1.0 op_sel:[0,0,1,0]" : "+v"(d) : "v"(x), "v"(r));
+  } else if constexpr (sel == 2) {
+    asm volatile("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, 1.0 op_sel:[0,0,0,1]" : "+v"(d) : "v"(x), "v"(r));
+  } else {
+    asm volatile("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, 1.0 op_sel:[0,0,1,1]" : "+v"(d) : "v"(x), "v"(r));
+  }
 }
 
 template <int sel>
 __device__ __forceinline__ void sr_pk(uint32_t& lo, uint32_t& hi, float v0, float v1, uint32_t h) {
   typedef float float2v __attribute__((ext_vector_type(2)));
-  const float2v xv = {sr_hw_input(v0), sr_hw_input(v1)};
+  const float2v xv = {v0, v1};
   const double x = __builtin_bit_cast(double, xv);  // the pair as one 64-bit register pair
   const uint32_t nh = ~h;  // 65535 - r16 in each half: r16(v0) = h & 0xFFFF, r16(v1) = h >> 16
-  cvt_sr_pk<sel>(lo, x, (nh << 16) | 0xFFFFu);
-  cvt_sr_pk<sel>(hi, x, (nh >> 1) | 0x7FFFu);
+  cvt_sr_pk<sel, sel == 0>(lo, x, (nh << 16) | 0xFFFFu);
+  cvt_sr_pk<sel, sel == 0>(hi, x, (nh >> 1) | 0x7FFFu);
 }
 
 // Eight scaled values to eight SR codes, element 0 in the low nibble; h[p] is
 // the hash of pair p (r16 of element 2p in its low half, 2p + 1 in its high).
 __device__ __forceinline__ uint32_t sr_pack8(const float* v, const uint32_t* h) {
-  uint32_t lo = 0u, hi = 0u;
+  uint32_t lo, hi;
   sr_pk<0>(lo, hi, v[0], v[1], h[0]);
   sr_pk<1>(lo, hi, v[2], v[3], h[1]);
   sr_pk<2>(lo, hi, v[4], v[5], h[2]);
@@ -237,12 +231,29 @@ struct OutElem<uint16_t> {
   }
 };
 
-// Radix-2 Walsh-Hadamard butterflies over 16 values with sign flips first and
-// the 1/4 normalization last: y = (1/4) H16 diag(d) x, Sylvester ordering.
-__device__ __forceinline__ void rht16(float* u, uint32_t sign_mask) {
-#pragma unroll
-  for (int j = 0; j < 16; j++)
-    if ((sign_mask >> j) & 1u) u[j] = -u[j];
+// The random Hadamard transform y = (1/4) H16 diag(d) x (Sylvester H16,
+// d_j = -1 where bit j of the sign mask is set) runs in three parts: the
+// sign flips, applied by the loaders as they convert each element (sign_bit
+// below), the radix-2 butterflies (fwht16), and the 1/4 normalization.
+
+// 0x80000000 where bit j of the sign mask is set, else 0 (wave-uniform).
+__device__ __forceinline__ uint32_t sign_bit(uint32_t sign_mask, int j) {
+  return ((sign_mask >> j) & 1u) << 31;
+}
+
+// bf16 halves of a word as FP32 with the sign bit flipped by s (0 or
+// 0x80000000): adding s to the top bit flips it (the carry drops out), so
+// the low half costs one shift-add and the high half one and-xor.
+__device__ __forceinline__ float bf16lo_signed(uint32_t w, uint32_t s) { return __uint_as_float((w << 16) + s); }
+__device__ __forceinline__ float bf16hi_signed(uint32_t w, uint32_t s) {
+  return __uint_as_float((w & 0xFFFF0000u) ^ s);
+}
+__device__ __forceinline__ float f32_signed(float x, uint32_t s) { return __uint_as_float(__float_as_uint(x) ^ s); }
+
+// Radix-2 Walsh-Hadamard butterflies over 16 values, stages h = 1, 2, 4, 8,
+// each pair (p, p + h) with (p & h) == 0 becoming (u_p + u_{p+h},
+// u_p - u_{p+h}): u <- H16 u.
+__device__ __forceinline__ void fwht16(float* u) {
 #pragma unroll
   for (int h = 1; h < 16; h <<= 1) {
 #pragma unroll
@@ -254,6 +265,11 @@ __device__ __forceinline__ void rht16(float* u, uint32_t sign_mask) {
       }
     }
   }
+}
+
+// Butterflies and the 1/4 normalization of already sign-flipped values.
+__device__ __forceinline__ void rht16_signed(float* u) {
+  fwht16(u);
 #pragma unroll
   for (int j = 0; j < 16; j++) u[j] = 0.25f * u[j];
 }

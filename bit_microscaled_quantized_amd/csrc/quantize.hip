@@ -240,13 +240,20 @@ struct ColTile<uint16_t> {
 #pragma unroll
     for (int j = 0; j < 16; j++) w[j] = *reinterpret_cast<const uint4*>(p + j * ld);
   }
-  // column k (0..7) of the 16 rows
-  __device__ __forceinline__ void column(int k, float* u) const {
+  // column k (0..7) of the 16 rows; with SIGN, row j's value negated where
+  // bit j of sign_mask is set (the transform's sign flips)
+  template <bool SIGN>
+  __device__ __forceinline__ void column(int k, float* u, uint32_t sign_mask) const {
 #pragma unroll
     for (int j = 0; j < 16; j++) {
       const uint32_t d = k < 2 ? w[j].x : k < 4 ? w[j].y : k < 6 ? w[j].z : w[j].w;
-      u[j] = (k & 1) ? bf16hi(d) : bf16lo(d);
+      const uint32_t sb = SIGN ? sign_bit(sign_mask, j) : 0u;
+      u[j] = (k & 1) ? bf16hi_signed(d, sb) : bf16lo_signed(d, sb);
     }
+  }
+  __device__ __forceinline__ void opaque() {
+#pragma unroll
+    for (int j = 0; j < 16; j++) asm volatile("" : "+v"(w[j].x), "+v"(w[j].y), "+v"(w[j].z), "+v"(w[j].w));
   }
   // the 8 values of row j
   __device__ __forceinline__ void row(int j, float* v) const {
@@ -265,13 +272,21 @@ struct ColTile<float> {
       w[j][1] = *reinterpret_cast<const float4*>(p + j * ld + 4);
     }
   }
-  __device__ __forceinline__ void column(int k, float* u) const {
+  template <bool SIGN>
+  __device__ __forceinline__ void column(int k, float* u, uint32_t sign_mask) const {
 #pragma unroll
     for (int j = 0; j < 16; j++) {
       const float4 q = w[j][k >> 2];
       const int e = k & 3;
-      u[j] = e == 0 ? q.x : e == 1 ? q.y : e == 2 ? q.z : q.w;
+      const float x = e == 0 ? q.x : e == 1 ? q.y : e == 2 ? q.z : q.w;
+      u[j] = SIGN ? f32_signed(x, sign_bit(sign_mask, j)) : x;
     }
+  }
+  __device__ __forceinline__ void opaque() {
+#pragma unroll
+    for (int j = 0; j < 16; j++)
+      for (int h = 0; h < 2; h++)
+        asm volatile("" : "+v"(w[j][h].x), "+v"(w[j][h].y), "+v"(w[j][h].z), "+v"(w[j][h].w));
   }
   __device__ __forceinline__ void row(int j, float* v) const {
     v[0] = w[j][0].x; v[1] = w[j][0].y; v[2] = w[j][0].z; v[3] = w[j][0].w;
@@ -281,35 +296,69 @@ struct ColTile<float> {
 
 // The column encoding of a tile (transform, block scale, encode) into the LDS
 // staging arrays, and the contiguous stores of the staged codes and scales.
-template <typename T, int RND, bool RHT>
-__device__ __forceinline__ void col_encode(const ColTile<T>& tile, bool valid, int64_t rows, int64_t tg,
+//
+// FOLD (bf16 input, RHT only) leaves the 1/4 of the transform out of the 16
+// values and puts it into the block's multiplier instead: the block maximum
+// is 0.25 * max |u| (exact: rounding is monotone) and the scaled value is
+// u * (0.25 * r_b).  That equals y * r_b with y = 0.25 u whenever both
+// quarters are exact: 0.25 u always is for bf16 input (u is a multiple of
+// 2^-133, so y is a multiple of 2^-135, never below the FP32 subnormal step),
+// and 0.25 r_b is whenever r_b >= 2^-124 or r_b = 0, which S_enc >= 2^-100
+// guarantees (r_b >= S_enc / 448).  The caller checks S_enc.
+template <typename T, int RND, bool RHT, bool FOLD>
+__device__ __forceinline__ void col_encode(const ColTile<T>& tile, int64_t rows, int64_t tg,
                                            int64_t cc, int g, int co, uint32_t sign_mask, float s_enc,
                                            const float* rtab, uint32_t key,
                                            uint8_t (*lcodes)[kColTok / 2],
                                            uint8_t (*lscales)[kColTok / 16]) {
+  static_assert(!FOLD || (RHT && sizeof(T) == 2), "the 1/4 fold is exact for bf16 RHT input only");
 #pragma unroll
   for (int k = 0; k < 8; k++) {
-    uint32_t e_b = 0u;
-    uint32_t w0 = 0u, w1 = 0u;
-    if (valid) {
-      float u[16];
-      tile.column(k, u);
-      if constexpr (RHT) rht16(u, sign_mask);
-      float am = 0.0f;
+    float u[16];
+    tile.template column<RHT>(k, u, sign_mask);
+    if constexpr (FOLD)
+      fwht16(u);
+    else if constexpr (RHT)
+      rht16_signed(u);
+    float am = 0.0f;
 #pragma unroll
-      for (int j = 0; j < 16; j++) am = fmaxf(am, fabsf(u[j]));
-      float r_b;
-      block_scale(am, s_enc, rtab, e_b, r_b);
-      float s[16];
+    for (int j = 0; j < 16; j++) am = fmaxf(am, fabsf(u[j]));
+    if constexpr (FOLD) am = 0.25f * am;
+    uint32_t e_b;
+    float r_b;
+    block_scale(am, s_enc, rtab, e_b, r_b);
+    if constexpr (FOLD) r_b = 0.25f * r_b;
+    float s[16];
 #pragma unroll
-      for (int j = 0; j < 16; j++) s[j] = u[j] * r_b;
-      const uint2 w = encode16<RND>(s, key, (uint32_t)((cc + k) * rows + tg) >> 1);
-      w0 = w.x;
-      w1 = w.y;
-    }
-    *reinterpret_cast<uint2*>(&lcodes[8 * co + k][8 * g]) = make_uint2(w0, w1);
+    for (int j = 0; j < 16; j++) s[j] = u[j] * r_b;
+    const uint2 w = encode16<RND>(s, key, (uint32_t)((cc + k) * rows + tg) >> 1);
+    *reinterpret_cast<uint2*>(&lcodes[8 * co + k][8 * g]) = w;
     lscales[8 * co + k][g] = (uint8_t)e_b;
   }
+}
+
+// Whether the 1/4 of the transform may be folded into the block multipliers
+// (see col_encode): bf16 input and S_enc >= 2^-100.
+template <typename T>
+__device__ __forceinline__ bool rht_fold_ok(float s_enc) {
+  return sizeof(T) == 2 && s_enc >= 0x1p-100f;
+}
+
+template <typename T, int RND, bool RHT>
+__device__ __forceinline__ void col_encode_any(const ColTile<T>& tile, int64_t rows, int64_t tg,
+                                               int64_t cc, int g, int co, uint32_t sign_mask,
+                                               float s_enc, const float* rtab, uint32_t key,
+                                               uint8_t (*lcodes)[kColTok / 2],
+                                               uint8_t (*lscales)[kColTok / 16]) {
+  if constexpr (RHT && sizeof(T) == 2) {
+    if (rht_fold_ok<T>(s_enc)) {  // uniform: one tensor scale
+      col_encode<T, RND, true, true>(tile, rows, tg, cc, g, co, sign_mask, s_enc, rtab, key, lcodes,
+                                     lscales);
+      return;
+    }
+  }
+  col_encode<T, RND, RHT, false>(tile, rows, tg, cc, g, co, sign_mask, s_enc, rtab, key, lcodes,
+                                 lscales);
 }
 
 __device__ __forceinline__ void col_store(int64_t rows, int64_t cols, int64_t t0, int64_t c0,
@@ -375,11 +424,14 @@ __global__ __launch_bounds__(256) void k_cast_col1d(const T* __restrict__ x, int
   const int g = threadIdx.x >> 3;   // 16-token group within the tile
   const int64_t tg = t0 + 16 * g;   // first token of the group
   const int64_t cc = c0 + 8 * co;   // first column of the octet
+  // A thread whose 16 x 8 patch lies past the tensor loads the first patch
+  // instead (in bounds: rows and cols are positive multiples of 16) and
+  // encodes it into LDS slots that col_store never writes out.
   const bool valid = tg < rows && cc < cols;
 
   ColTile<T> tile;
-  if (valid) tile.load(x + tg * ld + cc, ld);
-  col_encode<T, RND, RHT>(tile, valid, rows, tg, cc, g, co, sign_mask, s_enc, rtab, key, lcodes, lscales);
+  tile.load(valid ? x + tg * ld + cc : x, ld);
+  col_encode_any<T, RND, RHT>(tile, rows, tg, cc, g, co, sign_mask, s_enc, rtab, key, lcodes, lscales);
   __syncthreads();
   col_store(rows, cols, t0, c0, lcodes, lscales, codes, scales);
 }
@@ -418,22 +470,24 @@ __global__ __launch_bounds__(256) void k_cast_row_rht(
   const int g = threadIdx.x >> 3;
   const int64_t tg = t0 + 16 * g;
   const int64_t cc = c0 + 8 * co;
-  const bool valid = tg < rows && cc < cols;  // the lane pair (co, co^1) agrees (cols % 16 == 0)
+  // the lane pair (co, co^1) agrees on validity (cols % 16 == 0); an invalid
+  // thread loads the first patch instead (in bounds) and stores nothing
+  const bool valid = tg < rows && cc < cols;
 
   ColTile<T> tile;
-  if (valid) tile.load(x + tg * ld + cc, ld);
+  tile.load(valid ? x + tg * ld + cc : x, ld);
 
-  // row copy: rows tg .. tg + 15, columns cc .. cc + 7 of this lane
+  // row copy: rows tg .. tg + 15, columns cc .. cc + 7 of this lane; the
+  // output addresses and the hash index step by one row per iteration
   const int64_t rbytes = cols / 2, rscales = cols / 16;
+  uint8_t* crow = row_codes + tg * rbytes + cc / 2;
+  uint8_t* srow = row_scales + tg * rscales + cc / 16;
+  uint32_t pair = (uint32_t)(tg * cols + cc) >> 1;  // elements < 2^32 (host check)
+  const uint32_t pair_step = (uint32_t)cols >> 1;
 #pragma unroll
   for (int j = 0; j < 16; j++) {
     float v[8];
-    if (valid) {
-      tile.row(j, v);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; e++) v[e] = 0.0f;
-    }
+    tile.row(j, v);
     float am = 0.0f;
 #pragma unroll
     for (int e = 0; e < 8; e++) am = fmaxf(am, fabsf(v[e]));
@@ -444,17 +498,22 @@ __global__ __launch_bounds__(256) void k_cast_row_rht(
     float sv[8];
 #pragma unroll
     for (int e = 0; e < 8; e++) sv[e] = v[e] * r_b;
-    const int64_t r = tg + j;
-    const uint32_t w = encode8<RR>(sv, row_key, (uint32_t)(r * cols + cc) >> 1);
+    const uint32_t w = encode8<RR>(sv, row_key, pair);
     if (valid) {
-      *reinterpret_cast<uint32_t*>(row_codes + r * rbytes + cc / 2) = w;
-      if ((co & 1) == 0) row_scales[r * rscales + cc / 16] = (uint8_t)e_b;
+      *reinterpret_cast<uint32_t*>(crow) = w;
+      if ((co & 1) == 0) *srow = (uint8_t)e_b;
     }
+    crow += rbytes;
+    srow += rscales;
+    pair += pair_step;
   }
 
-  // RHT column copy
-  col_encode<T, RH, true>(tile, valid, rows, tg, cc, g, co, sign_mask, s_rht, rtab_rht, rht_key, lcodes,
-                          lscales);
+  // RHT column copy.  The raw words pass through an empty asm first, so the
+  // compiler converts them again one column at a time instead of keeping
+  // the row copy's 128 converted values live (which costs ~50 VGPRs).
+  tile.opaque();
+  col_encode_any<T, RH, true>(tile, rows, tg, cc, g, co, sign_mask, s_rht, rtab_rht, rht_key, lcodes,
+                              lscales);
   __syncthreads();
   col_store(rows, cols, t0, c0, lcodes, lscales, rht_codes, rht_scales);
 }
@@ -475,11 +534,13 @@ struct QuadTile<uint16_t> {
 #pragma unroll
     for (int j = 0; j < 16; j++) w[j] = *reinterpret_cast<const uint2*>(p + j * ld);
   }
-  __device__ __forceinline__ void column(int k, float* u) const {
+  // column k (0..3), row j negated where bit j of sign_mask is set
+  __device__ __forceinline__ void column(int k, float* u, uint32_t sign_mask) const {
 #pragma unroll
     for (int j = 0; j < 16; j++) {
       const uint32_t d = k < 2 ? w[j].x : w[j].y;
-      u[j] = (k & 1) ? bf16hi(d) : bf16lo(d);
+      const uint32_t sb = sign_bit(sign_mask, j);
+      u[j] = (k & 1) ? bf16hi_signed(d, sb) : bf16lo_signed(d, sb);
     }
   }
 };
@@ -491,9 +552,11 @@ struct QuadTile<float> {
 #pragma unroll
     for (int j = 0; j < 16; j++) w[j] = *reinterpret_cast<const float4*>(p + j * ld);
   }
-  __device__ __forceinline__ void column(int k, float* u) const {
+  __device__ __forceinline__ void column(int k, float* u, uint32_t sign_mask) const {
 #pragma unroll
-    for (int j = 0; j < 16; j++) u[j] = k == 0 ? w[j].x : k == 1 ? w[j].y : k == 2 ? w[j].z : w[j].w;
+    for (int j = 0; j < 16; j++)
+      u[j] = f32_signed(k == 0 ? w[j].x : k == 1 ? w[j].y : k == 2 ? w[j].z : w[j].w,
+                        sign_bit(sign_mask, j));
   }
 };
 
@@ -503,12 +566,12 @@ __device__ __forceinline__ void rht_amax_patch(const QuadTile<T>& t, uint32_t si
 #pragma unroll
   for (int k = 0; k < 4; k++) {
     float u[16];
-    t.column(k, u);
+    t.column(k, u, sign_mask);  // sign flips do not change |u|
     if (plain) {
 #pragma unroll
       for (int j = 0; j < 16; j++) ap = fmaxf(ap, fabsf(u[j]));
     }
-    rht16(u, sign_mask);
+    fwht16(u);  // the 1/4 is applied once, to the maximum
 #pragma unroll
     for (int j = 0; j < 16; j++) am = fmaxf(am, fabsf(u[j]));
   }
@@ -540,6 +603,8 @@ __global__ __launch_bounds__(256) void k_rht_amax(const T* __restrict__ x, int64
     rht_amax_patch(tb, sign_mask, plain, am, ap);
     p = pa;
   }
+  // max |RN(u / 4)| = RN(max |u| / 4): rounding is monotone
+  am = 0.25f * am;
   block_atomic_max(__float_as_uint(am), amax, __float_as_uint(ap), amax_plain);
 }
 

@@ -37,7 +37,8 @@
  *   element scale  r_b = 0 if e_b == 0 else min(S_enc / dec(e_b), FLT_MAX)
  *   scaled value   v = y * r_b, E2M1 code = sign(y) | magnitude index
  *   RNE            nearest E2M1 magnitude, ties to the even index, clamp at 6
- *   SR             up iff r16 < frac * 65536, frac = (a - lo) / (hi - lo)
+ *   SR             up iff 64 * r16 < floor(frac * 2^22), frac = (a - lo) / (hi - lo):
+ *                  the fraction truncated to 22 bits against 16 random bits
  *   random bits    r16 from the pcg hash keyed by (seed, output index)
  *   RHT            per 16 tokens of one column: sign flips, FWHT stages
  *                  h = 1, 2, 4, 8 as (a + b, a - b), then * 0.25
@@ -142,12 +143,16 @@ int ora_e2m1_rne(float v)
 
 /* E2M1 stochastic rounding of v with 16 random bits r16 in [0, 65535].
  * a = min(|v|, 6); lo = largest magnitude <= a, hi = the next one;
- * rounds up iff r16 < frac * 65536 with frac = (a - lo) / (hi - lo), so the
- * probability of rounding up is ceil(frac * 65536) / 65536. */
+ * frac = (a - lo) / (hi - lo), truncated to 22 bits: f22 = floor(frac * 2^22).
+ * Rounds up iff 64 * r16 < f22, i.e. iff r16 < f22 / 64, so the probability
+ * of rounding up is ceil(f22 / 64) / 65536, within 2^-16 of frac.  For
+ * a >= 1, frac * 2^22 is already an integer (the low 22 mantissa bits of a),
+ * and the truncation only matters below 1.  Everything here is exact in
+ * double precision. */
 int ora_e2m1_sr(float v, uint32_t r16)
 {
     int sign = signbit(v) ? 8 : 0, k = 0, i;
-    double a = fabs((double)v), frac;
+    double a = fabs((double)v), frac, f22;
     if (a > 6.0)
         a = 6.0;
     for (i = 0; i < 8; i++)
@@ -156,7 +161,8 @@ int ora_e2m1_sr(float v, uint32_t r16)
     if (k == 7)
         return sign | 7;
     frac = (a - E2M1_MAG[k]) / (E2M1_MAG[k + 1] - E2M1_MAG[k]);
-    if ((double)r16 < frac * 65536.0)
+    f22 = floor(frac * 4194304.0);
+    if (64.0 * (double)r16 < f22)
         k += 1;
     return sign | k;
 }

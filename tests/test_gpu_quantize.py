@@ -187,25 +187,54 @@ def test_edge_cases(ora, name, layout, rnd):
     _same(g, o, keys)
 
 
-@pytest.mark.parametrize("name", sorted(EDGE))
-@pytest.mark.parametrize("rnd", [nv.NVFP4_RNE, nv.NVFP4_SR])
-def test_edge_cases_rht(ora, name, rnd):
+def _edge_rht_input(name, dtype):
     x = EDGE[name]
     if name == "huge":
         x = x * np.float32(0.01)  # keep the 16-term butterflies finite
+    return synth.f32_to_bf16_bits(x) if dtype == "bf16" else x
+
+
+# bf16 input takes the kernels' folded transform (the 1/4 inside the block
+# multiplier) unless S_enc < 2^-100, as for "huge" (amax ~1e35): both paths
+# are covered here.
+@pytest.mark.parametrize("name", sorted(EDGE))
+@pytest.mark.parametrize("rnd", [nv.NVFP4_RNE, nv.NVFP4_SR])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_edge_cases_rht(ora, name, rnd, dtype):
+    x = _edge_rht_input(name, dtype)
     g = gpuio.gpu_rht_quantize(x, 0x5A5A, rnd, 17)
     o = ora.rht_quantize(x, 0x5A5A, rnd, 17)
     _same(g, o, KEYS)
 
 
 @pytest.mark.parametrize("name", sorted(EDGE))
-def test_edge_cases_row_rht(ora, name):
-    x = EDGE[name]
-    if name == "huge":
-        x = x * np.float32(0.01)
-    g_row, g_rht = gpuio.gpu_quantize_row_rht(x, 0x5A5A, nv.NVFP4_SR, 31, nv.NVFP4_SR, 32)
-    _same(g_row, ora.quantize(x, ora.ROW_1D, ora.SR, 31), KEYS)
-    _same(g_rht, ora.rht_quantize(x, 0x5A5A, ora.SR, 32), KEYS)
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_edge_cases_row_rht(ora, name, dtype):
+    x = _edge_rht_input(name, dtype)
+    for rnd in (nv.NVFP4_SR, nv.NVFP4_RNE):
+        g_row, g_rht = gpuio.gpu_quantize_row_rht(x, 0x5A5A, rnd, 31, rnd, 32)
+        _same(g_row, ora.quantize(x, ora.ROW_1D, rnd, 31), KEYS)
+        _same(g_rht, ora.rht_quantize(x, 0x5A5A, rnd, 32), KEYS)
+
+
+@pytest.mark.parametrize("s_exp", [-110, -101, -100.5, -99.5, -99, 6, 86])
+def test_rht_fold_boundary_bf16(ora, s_exp):
+    """bf16 input whose RHT amax puts S_enc = 2688 / amax near 2^s_exp, on
+    either side of 2^-100 where the kernels switch between the folded and the
+    unfolded transform, with small entries that make subnormal products; the
+    result must not depend on the path."""
+    rng = np.random.default_rng(int(s_exp * 2) + 300)
+    x = rng.standard_normal((64, 96)).astype(np.float32)
+    x[:, ::7] *= np.float32(2.0 ** -120)
+    # the RHT amax of these 64 x 96 normals is about 4.4
+    x = (x * np.float32(2688.0 * 2.0 ** -s_exp / 4.4)).astype(np.float32)
+    xb = synth.f32_to_bf16_bits(x)
+    for rnd in (nv.NVFP4_RNE, nv.NVFP4_SR):
+        g = gpuio.gpu_rht_quantize(xb, 0x3C5A, rnd, 41)
+        _same(g, ora.rht_quantize(xb, 0x3C5A, rnd, 41), KEYS)
+        g_row, g_rht = gpuio.gpu_quantize_row_rht(xb, 0x3C5A, rnd, 42, rnd, 43)
+        _same(g_row, ora.quantize(xb, ora.ROW_1D, rnd, 42), KEYS)
+        _same(g_rht, ora.rht_quantize(xb, 0x3C5A, rnd, 43), KEYS)
 
 
 def test_e2m1_conversion_sweep(ora):

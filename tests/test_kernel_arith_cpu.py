@@ -14,9 +14,8 @@ oracle's E4M3 and stochastic-rounding rules).
   (v_cvt_scalef32_sr_pk_fp4_f32), whose rule was measured on the device:
   sign-magnitude, F = the 22 bits of (a - lo) / (hi - lo) below the E2M1 grid
   point (truncated), element e of the pair rounds up iff F + bits[31:10] of
-  (R << e) >= 2^22, magnitudes >= 6 give code 7.  They feed it
-  ceil(|v| * 2^23) with v's sign and the scale operand 2^23 (the device divides
-  by it exactly), and R = ~(r16 << 16) for element 0
+  (R << e) >= 2^22, magnitudes >= 6 give code 7.  They feed it the scaled
+  value itself (scale operand 1.0) and R = ~(r16 << 16) for element 0
   or (~r16 << 15) | 0x7FFF for element 1.  Restated with that rule, this gives
   the oracle's code for every FP32 v with |v| <= 6.5 (and a sweep beyond), for
   both elements, at r16 values on both sides of each input's rounding
@@ -61,13 +60,11 @@ static uint32_t device_sr(float x, uint32_t R, int el) {
   return sign | (uint32_t)(k + (F + field >= 4194304u));
 }
 
-/* what the kernels feed it: input rounded up in magnitude to a multiple of
-   2^-23, R from the pair's hash h (r16 of element 0 in the low half, of
-   element 1 in the high half; the other half is another element's) */
+/* what the kernels feed it: the scaled value with scale 1.0, R from the
+   pair's hash h (r16 of element 0 in the low half, of element 1 in the high
+   half; the other half is another element's) */
 static uint32_t sr_kernel(float v, uint32_t r16, int el, uint32_t other) {
-  const float t = ceilf(fabsf(v) * 8388608.0f);
-  const float x = copysignf(t, v) * 0x1p-23f;  /* passed as copysign(t, v) with scale 2^23,
-                                                   which the device divides by exactly */
+  const float x = v;
   const uint32_t h = el ? ((r16 << 16) | (other & 0xFFFFu)) : (r16 | (other << 16));
   const uint32_t nh = ~h;
   const uint32_t R = el ? ((nh >> 1) | 0x7FFFu) : ((nh << 16) | 0xFFFFu);
@@ -119,10 +116,16 @@ int main(int argc, char** argv) {
     double a = fmin(fabs((double)v), 6.0);
     int k = 0;
     for (int j = 0; j < 8; j++) if (MAG[j] <= a) k = j;
-    uint32_t rs[4];
+    uint32_t rs[6];
     int n = 0;
     if (k < 7) {
-      double thr = ceil((a - MAG[k]) / (MAG[k + 1] - MAG[k]) * 65536.0);  /* up iff r16 < thr */
+      /* the exact fraction's threshold and the 22-bit one: r16 values on both
+         sides of each */
+      double frac = (a - MAG[k]) / (MAG[k + 1] - MAG[k]);
+      double thr = ceil(frac * 65536.0);
+      double thr22 = ceil(floor(frac * 4194304.0) / 64.0);
+      if (thr22 >= 1.0) rs[n++] = (uint32_t)thr22 - 1u;
+      if (thr22 <= 65535.0) rs[n++] = (uint32_t)thr22;
       if (thr >= 1.0) rs[n++] = (uint32_t)thr - 1u;
       if (thr <= 65535.0) rs[n++] = (uint32_t)thr;
     }

@@ -215,7 +215,8 @@ def test_rht_spreads_an_outlier(ora):
 
 
 # ---------------------------------------------------------------- P6: SR
-@pytest.mark.parametrize("v", [0.1, 0.3, 0.6, 0.75, 1.3, 1.7, 2.2, 2.5, 3.7, 4.4, 5.9, -1.1, -0.01])
+@pytest.mark.parametrize("v", [0.1, 0.3, 0.6, 0.75, 1.3, 1.7, 2.2, 2.5, 3.7, 4.4, 5.9, -1.1, -0.01,
+                               0.5 + 2.0 ** -24, 0.25 + 2.0 ** -25, 2.0 ** -30, 0.9999999])
 def test_sr_exact_expectation_over_all_random_values(ora, v):
     v = f32(v)
     a = abs(v)
@@ -229,10 +230,34 @@ def test_sr_exact_expectation_over_all_random_values(ora, v):
         assert (c & 8) == (8 if v < 0 else 0)
         assert c & 7 in (k, k + 1)  # only the two neighbours
         ups += (c & 7) == k + 1
-    # P(up) = ceil(frac * 2^16) / 2^16: unbiased up to one part in 2^16 of a step
-    assert ups == math.ceil(frac * 65536)
+    # unbiased up to one part in 2^16 of a step, either way: E[q] - a is
+    # (ups / 2^16 - frac) * step, and |ups / 2^16 - frac| < 2^-16
     mean = Fraction(lo) + Fraction(ups, 65536) * (Fraction(hi) - Fraction(lo))
-    assert 0 <= mean - Fraction(a) < Fraction(hi - lo) / 65536
+    assert abs(mean - Fraction(a)) < Fraction(hi - lo) / 65536
+    # for a >= 1 the fraction is a multiple of 2^-22, so P(up) is exactly
+    # ceil(frac * 2^16) / 2^16 (the 16 random bits resolve it completely)
+    if a >= 1:
+        assert ups == math.ceil(frac * 65536)
+    # below 1 the fraction is resolved to 22 bits: values within 2^-22 of a
+    # step of each other round alike, so P(up) never exceeds the exact
+    # ceiling and falls short of it only when frac * 2^16 lies within 2^-6
+    # above an integer
+    else:
+        assert ups <= math.ceil(frac * 65536)
+        if ups < math.ceil(frac * 65536):
+            assert frac * 65536 - math.floor(frac * 65536) <= Fraction(1, 64)
+
+
+def test_sr_rounds_values_within_one_22_bit_step_alike(ora):
+    # a < 1: a fraction below 2^-22 of a step never rounds up, one at 2^-22
+    # rounds up only for r16 = 0
+    for lo, step in ((0.0, 0.5), (0.5, 0.5)):
+        tiny = f32(lo + step * 2.0 ** -23)
+        assert tiny != f32(lo)
+        assert all(ora.e2m1_sr(tiny, r) & 7 == ora.e2m1_sr(f32(lo), 0) & 7 for r in (0, 1, 65535))
+        one = f32(lo + step * 2.0 ** -22)
+        k = ora.e2m1_sr(f32(lo), 0)
+        assert ora.e2m1_sr(one, 0) == k + 1 and ora.e2m1_sr(one, 1) == k
 
 
 def test_sr_saturates_and_mean_over_seeds(ora):
