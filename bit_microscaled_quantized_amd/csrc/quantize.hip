@@ -780,6 +780,16 @@ static inline unsigned grid_cap(int64_t want, int64_t cap) {
   return (unsigned)(want < cap ? want : cap);
 }
 
+// Compute units of the current device (256, the MI355X count, if the query
+// fails).
+static int cu_count() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+    return 256;
+  return n;
+}
+
 template <typename T>
 static hipError_t launch_amax(const void* x, int64_t rows, int64_t cols, int64_t ld, float* amax,
                               hipStream_t s) {
@@ -791,11 +801,17 @@ static hipError_t launch_amax(const void* x, int64_t rows, int64_t cols, int64_t
     rows = 1;
   }
   int64_t cpr = cols / EPC;
-  // at most 2048 workgroups (each one reads the running maximum once), with
-  // the rounds balanced so that no workgroup idles in a partial last round
+  // one long row: four workgroups per compute unit walking the tensor in
+  // rounds (measured: 1.3x the rate of twice as many on an 84 MB tensor);
+  // strided rows: at most 2048 workgroups per row, rounds balanced
   const int64_t units = (cpr + 256 * UNROLL - 1) / (256 * UNROLL);
-  const int64_t rounds = (units + 2047) / 2048;
-  dim3 grid(grid_cap((units + rounds - 1) / rounds, 2048), grid_cap(rows, 65535));
+  dim3 grid;
+  if (rows == 1) {
+    grid = dim3(grid_cap(units, 4 * (int64_t)cu_count()), 1);
+  } else {
+    const int64_t rounds = (units + 2047) / 2048;
+    grid = dim3(grid_cap((units + rounds - 1) / rounds, 2048), grid_cap(rows, 65535));
+  }
   k_amax<T, UNROLL><<<grid, 256, 0, s>>>(static_cast<const T*>(x), rows, cols, ld, amax);
   return hipGetLastError();
 }
@@ -855,7 +871,8 @@ static hipError_t launch_cast(const void* x, int dt, int64_t rows, int64_t cols,
 static hipError_t launch_rht_amax(const void* x, int dt, int64_t tokens, int64_t cols, int64_t ld,
                                   uint32_t sign_mask, float* amax, float* amax_plain, hipStream_t s) {
   k_zero_amax<<<1, 64, 0, s>>>(amax, amax_plain);
-  // patches of 16 tokens x 4 columns; at most 2048 workgroups, rounds balanced
+  // patches of 16 tokens x 4 columns; at most 2048 workgroups, rounds
+  // balanced (capping the grid at the resident count was 1-5 % slower here)
   const int64_t units = (tokens / 16) * (cols / 4);
   const int64_t wgs = (units + 255) / 256;
   const int64_t rounds = (wgs + 2047) / 2048;
