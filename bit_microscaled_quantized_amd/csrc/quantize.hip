@@ -608,6 +608,44 @@ __global__ __launch_bounds__(256) void k_rht_amax(const T* __restrict__ x, int64
   block_atomic_max(__float_as_uint(am), amax, __float_as_uint(ap), amax_plain);
 }
 
+// 16 consecutive elements as loaded (bf16: two 16-byte words; fp32: four),
+// converted to FP32 on use.
+template <typename T>
+struct Raw16;
+
+template <>
+struct Raw16<uint16_t> {
+  uint4 w[2];
+  __device__ __forceinline__ void load(const uint16_t* p) {
+    w[0] = reinterpret_cast<const uint4*>(p)[0];
+    w[1] = reinterpret_cast<const uint4*>(p)[1];
+  }
+  __device__ __forceinline__ void get(float* v) const {
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+      v[8 * h + 0] = bf16lo(w[h].x); v[8 * h + 1] = bf16hi(w[h].x);
+      v[8 * h + 2] = bf16lo(w[h].y); v[8 * h + 3] = bf16hi(w[h].y);
+      v[8 * h + 4] = bf16lo(w[h].z); v[8 * h + 5] = bf16hi(w[h].z);
+      v[8 * h + 6] = bf16lo(w[h].w); v[8 * h + 7] = bf16hi(w[h].w);
+    }
+  }
+};
+
+template <>
+struct Raw16<float> {
+  float4 w[4];
+  __device__ __forceinline__ void load(const float* p) {
+#pragma unroll
+    for (int q = 0; q < 4; q++) w[q] = reinterpret_cast<const float4*>(p)[q];
+  }
+  __device__ __forceinline__ void get(float* v) const {
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+      v[4 * q + 0] = w[q].x; v[4 * q + 1] = w[q].y; v[4 * q + 2] = w[q].z; v[4 * q + 3] = w[q].w;
+    }
+  }
+};
+
 // ---------------------------------------------------------------------------
 // 2D tile cast: one scale per 16x16 tile.  A workgroup covers 256 rows x 64
 // columns in four passes; in pass j wave w takes tile row 4j + w, lane l holds
@@ -709,20 +747,23 @@ __global__ __launch_bounds__(256) void k_cast_tile2d(const T* __restrict__ x, in
   const int rr = lane & 15;  // row within the tile
   const int64_t c = c0 + 16 * tc;
 
-  // tile rows 4j + wave of the region (16 rows each), one per iteration
-#pragma unroll 2
+  // The four tile rows 4j + wave of the region (16 rows each): all their
+  // loads are issued first (a tile outside the tensor reads the tensor's
+  // first 16 elements instead and stores nothing), then each is encoded.
+  Raw16<T> raw[4];
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    const int64_t r = r0 + 16 * (4 * j + wave) + rr;
+    const bool tile_valid = (r0 + 16 * (4 * j + wave)) < rows && c < cols;
+    raw[j].load(tile_valid ? x + r * ld + c : x);
+  }
+#pragma unroll
   for (int j = 0; j < 4; j++) {
     const int tr = 4 * j + wave;
     const int64_t r = r0 + 16 * tr + rr;
     const bool tile_valid = (r0 + 16 * tr) < rows && c < cols;  // whole tile in or out
     float v[16];
-    if (tile_valid) {
-      load8<T>(x + r * ld + c, v);
-      load8<T>(x + r * ld + c + 8, v + 8);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 16; e++) v[e] = 0.0f;
-    }
+    raw[j].get(v);
     float am = 0.0f;
 #pragma unroll
     for (int e = 0; e < 16; e++) am = fmaxf(am, fabsf(v[e]));
@@ -744,7 +785,8 @@ __global__ __launch_bounds__(256) void k_cast_tile2d(const T* __restrict__ x, in
       }
     }
     if (codes_t != nullptr) {
-      // every lane of the wave takes part in the exchange (invalid tiles carry zeros)
+      // every lane of the wave takes part in the exchange (an invalid tile's
+      // codes land in staging slots that are never stored)
       transpose16x16_nibbles(w0, w1, rr);
       // lane (tc, rr) now holds column c + rr of the tile's 16 rows
       *reinterpret_cast<uint2*>(&lt[16 * tc + rr][8 * tr]) = make_uint2(w0, w1);
