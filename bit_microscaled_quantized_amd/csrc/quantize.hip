@@ -217,15 +217,20 @@ __global__ __launch_bounds__(256) void k_cast_row1d(const T* __restrict__ x, int
 
 // ---------------------------------------------------------------------------
 // 1D column cast (COL_1D, and the Wgrad RHT path): blocks of 16 consecutive
-// rows (tokens) in one column, written transposed.  A workgroup covers 512
-// tokens x 64 columns: thread (g, co) loads 16 rows x 8 columns (16-byte
-// row segments, 8 threads per 128-byte line), transforms and encodes its 8
-// column blocks, and stages codes and scales in LDS so each output row
-// (one input column) is written as contiguous 16-byte pieces.
+// rows (tokens) in one column, written transposed.  A workgroup covers 256
+// tokens x 128 columns: thread (g, co) loads 16 rows x 8 columns (16-byte
+// row segments, 16 threads per 256-byte row piece), transforms and encodes
+// its 8 column blocks, and stages codes and scales in LDS so each output row
+// (one input column) gets one whole 128-byte line per workgroup.  The fused
+// row + RHT kernel below writes its row copy straight from registers, 64
+// bytes of codes per row per workgroup (a 512 x 64 tile gave 32-byte pieces).
 // codes [cols][rows/2], scales [cols][rows/16].
 // ---------------------------------------------------------------------------
-constexpr int kColTok = 512;  // tokens per workgroup tile
-constexpr int kColCols = 64;  // columns per workgroup tile
+constexpr int kColTok = 256;   // tokens per workgroup tile
+constexpr int kColCols = 128;  // columns per workgroup tile
+constexpr int kColOct = kColCols / 8;  // column octets (threads per 16-token group)
+static_assert(kColOct * (kColTok / 16) == 256, "one thread per 16 tokens x 8 columns");
+static_assert(kColTok >= 256, "col_store writes the scales as whole 16-byte pieces");
 
 // A thread's 16 rows x 8 columns, kept as loaded (bf16: one 16-byte word per
 // row, 64 VGPRs; fp32: two) and converted one column at a time, which keeps
@@ -365,11 +370,13 @@ __device__ __forceinline__ void col_store(int64_t rows, int64_t cols, int64_t t0
                                           const uint8_t (*lcodes)[kColTok / 2],
                                           const uint8_t (*lscales)[kColTok / 16], uint8_t* codes,
                                           uint8_t* scales) {
-  // codes: 64 rows of 256 bytes; 16 threads per row, 16 bytes each
+  // codes: kColCols rows of kColTok / 2 bytes, 16 bytes per thread
+  constexpr int kPieces = kColTok / 32;           // 16-byte pieces per row
+  constexpr int kRowsPerPass = 256 / kPieces;
   const int64_t row_bytes = rows / 2;
-  for (int pass = 0; pass < 4; pass++) {
-    int lc = pass * 16 + (threadIdx.x >> 4);  // local column
-    int piece = threadIdx.x & 15;
+  for (int pass = 0; pass < kColCols / kRowsPerPass; pass++) {
+    int lc = pass * kRowsPerPass + (int)threadIdx.x / kPieces;  // local column
+    int piece = (int)threadIdx.x % kPieces;
     int64_t c = c0 + lc;
     int64_t off = t0 / 2 + 16 * piece;  // byte offset within the output row
     if (c < cols && off < row_bytes) {
@@ -384,10 +391,11 @@ __device__ __forceinline__ void col_store(int64_t rows, int64_t cols, int64_t t0
       }
     }
   }
-  // scales: 64 rows of 32 bytes; 2 threads per row, 16 bytes each
-  if (threadIdx.x < 128) {
-    int lc = threadIdx.x >> 1;
-    int piece = threadIdx.x & 1;
+  // scales: kColCols rows of kColTok / 16 bytes, 16 bytes per thread
+  constexpr int kSPieces = kColTok / 256;
+  if ((int)threadIdx.x < kColCols * kSPieces) {
+    int lc = (int)threadIdx.x / kSPieces;
+    int piece = (int)threadIdx.x % kSPieces;
     int64_t c = c0 + lc;
     const int64_t srow = rows / 16;
     int64_t off = t0 / 16 + 16 * piece;
@@ -420,8 +428,8 @@ __global__ __launch_bounds__(256) void k_cast_col1d(const T* __restrict__ x, int
 
   const int64_t t0 = (int64_t)blockIdx.y * kColTok;
   const int64_t c0 = (int64_t)blockIdx.x * kColCols;
-  const int co = threadIdx.x & 7;   // column octet
-  const int g = threadIdx.x >> 3;   // 16-token group within the tile
+  const int co = (int)threadIdx.x % kColOct;  // column octet
+  const int g = (int)threadIdx.x / kColOct;   // 16-token group within the tile
   const int64_t tg = t0 + 16 * g;   // first token of the group
   const int64_t cc = c0 + 8 * co;   // first column of the octet
   // A thread whose 16 x 8 patch lies past the tensor loads the first patch
@@ -466,8 +474,8 @@ __global__ __launch_bounds__(256) void k_cast_row_rht(
 
   const int64_t t0 = (int64_t)blockIdx.y * kColTok;
   const int64_t c0 = (int64_t)blockIdx.x * kColCols;
-  const int co = threadIdx.x & 7;
-  const int g = threadIdx.x >> 3;
+  const int co = (int)threadIdx.x % kColOct;
+  const int g = (int)threadIdx.x / kColOct;
   const int64_t tg = t0 + 16 * g;
   const int64_t cc = c0 + 8 * co;
   // the lane pair (co, co^1) agrees on validity (cols % 16 == 0); an invalid
