@@ -19,6 +19,26 @@
 
 namespace nvfp4 {
 
+// Non-temporal output stores, for the casts whose workgroups write whole
+// contiguous lines (the row cast and the staged column stores): their codes
+// and scales are read next by another kernel (a GEMM), and dirty lines left
+// in the caches would be written back while the next quantize call's amax
+// pass streams its input.  Casts that write partial lines per workgroup (the
+// fused row copy, the 2D tile cast's row-major codes) keep ordinary stores:
+// non-temporal partial lines made them 3-40 % slower.
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void st_nt(void* p, uint4 v) {
+  __builtin_nontemporal_store(u32x4_t{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4_t*>(p));
+}
+__device__ __forceinline__ void st_nt(void* p, uint2 v) {
+  __builtin_nontemporal_store(u32x2_t{v.x, v.y}, reinterpret_cast<u32x2_t*>(p));
+}
+__device__ __forceinline__ void st_nt(void* p, uint32_t v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<uint32_t*>(p));
+}
+__device__ __forceinline__ void st_nt8(uint8_t* p, uint8_t v) { __builtin_nontemporal_store(v, p); }
+
 // ---------------------------------------------------------------------------
 // Tensor amax
 // ---------------------------------------------------------------------------
@@ -207,8 +227,8 @@ __global__ __launch_bounds__(256) void k_cast_row1d(const T* __restrict__ x, int
 #pragma unroll
         for (int e = 0; e < 16; e++) sv[e] = v[j][e] * r_b;
         if (it < items) {
-          crow[it] = encode16<RND>(sv, key, (row_index + (uint32_t)(it * 16)) >> 1);
-          srow[it] = (uint8_t)e_b;
+          st_nt(&crow[it], encode16<RND>(sv, key, (row_index + (uint32_t)(it * 16)) >> 1));
+          st_nt8(&srow[it], (uint8_t)e_b);
         }
       }
     }
@@ -384,10 +404,10 @@ __device__ __forceinline__ void col_store(int64_t rows, int64_t cols, int64_t t0
       const uint2* src = reinterpret_cast<const uint2*>(&lcodes[lc][16 * piece]);
       // row_bytes is a multiple of 8; 16-byte stores only where aligned
       if (off + 16 <= row_bytes && ((c * row_bytes + off) & 15) == 0) {
-        *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+        st_nt(dst, *reinterpret_cast<const uint4*>(src));
       } else {
-        reinterpret_cast<uint2*>(dst)[0] = src[0];
-        if (off + 16 <= row_bytes) reinterpret_cast<uint2*>(dst)[1] = src[1];
+        st_nt(dst, src[0]);
+        if (off + 16 <= row_bytes) st_nt(dst + 8, src[1]);
       }
     }
   }
@@ -403,9 +423,9 @@ __device__ __forceinline__ void col_store(int64_t rows, int64_t cols, int64_t t0
       uint8_t* dst = scales + c * srow + off;
       const uint8_t* src = &lscales[lc][16 * piece];
       if (off + 16 <= srow && ((c * srow + off) & 15) == 0) {
-        *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+        st_nt(dst, *reinterpret_cast<const uint4*>(src));
       } else {
-        for (int b = 0; b < 16 && off + b < srow; b++) dst[b] = src[b];
+        for (int b = 0; b < 16 && off + b < srow; b++) st_nt8(dst + b, src[b]);
       }
     }
   }
