@@ -96,9 +96,9 @@ __global__ __launch_bounds__(256) void k_mx_cast_row(const T* __restrict__ x, in
     mx_scale(am, code, mul);
 #pragma unroll
     for (int e = 0; e < 32; e++) v[e] *= mul;
-    reinterpret_cast<uint4*>(codes + r * (cols / 2))[it] =
-        mx_encode32<RND>(v, key, (uint32_t)(r * cols + it * 32) >> 1);
-    scales[r * blocks + it] = (uint8_t)code;
+    // whole lines per workgroup: non-temporal, like the NVFP4 row cast
+    st_nt(codes + r * (cols / 2) + 16 * it, mx_encode32<RND>(v, key, (uint32_t)(r * cols + it * 32) >> 1));
+    st_nt8(scales + r * blocks + it, (uint8_t)code);
   }
 }
 
@@ -168,8 +168,7 @@ __global__ __launch_bounds__(256) void k_mx_cast_col(const T* __restrict__ x, in
     const int64_t c = c0 + lc;
     const int64_t off = t0 / 2 + 16 * piece;
     if (c < cols && off < row_bytes)
-      *reinterpret_cast<uint4*>(codes + c * row_bytes + off) =
-          *reinterpret_cast<const uint4*>(&lcodes[lc][16 * piece]);
+      st_nt(codes + c * row_bytes + off, *reinterpret_cast<const uint4*>(&lcodes[lc][16 * piece]));
   }
   // scales: 64 output rows of 16 bytes
   if (threadIdx.x < kMxCols) {
@@ -181,9 +180,9 @@ __global__ __launch_bounds__(256) void k_mx_cast_col(const T* __restrict__ x, in
       uint8_t* dst = scales + c * srow + off;
       const int n = (int)min((int64_t)16, srow - off);
       if (n == 16 && ((c * srow + off) & 15) == 0)
-        *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(&lscales[lc][0]);
+        st_nt(dst, *reinterpret_cast<const uint4*>(&lscales[lc][0]));
       else
-        for (int b = 0; b < n; b++) dst[b] = lscales[lc][b];
+        for (int b = 0; b < n; b++) st_nt8(dst + b, lscales[lc][b]);
     }
   }
 }

@@ -214,6 +214,20 @@ __device__ __forceinline__ uint32_t bf16_rne(float v) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
+// Non-temporal stores of 16, 8, 4 and 1 bytes.
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void st_nt(void* p, uint4 v) {
+  __builtin_nontemporal_store(u32x4_t{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4_t*>(p));
+}
+__device__ __forceinline__ void st_nt(void* p, uint2 v) {
+  __builtin_nontemporal_store(u32x2_t{v.x, v.y}, reinterpret_cast<u32x2_t*>(p));
+}
+__device__ __forceinline__ void st_nt(void* p, uint32_t v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<uint32_t*>(p));
+}
+__device__ __forceinline__ void st_nt8(uint8_t* p, uint8_t v) { __builtin_nontemporal_store(v, p); }
+
 // One output element of a GEMM or a dequantization: FP32 as is, BF16 rounded
 // to nearest even; load() reads one back as FP32.
 template <typename OutT>

@@ -19,26 +19,6 @@
 
 namespace nvfp4 {
 
-// Non-temporal output stores, for the casts whose workgroups write whole
-// contiguous lines (the row cast and the staged column stores): their codes
-// and scales are read next by another kernel (a GEMM), and dirty lines left
-// in the caches would be written back while the next quantize call's amax
-// pass streams its input.  Casts that write partial lines per workgroup (the
-// fused row copy, the 2D tile cast's row-major codes) keep ordinary stores:
-// non-temporal partial lines made them 3-40 % slower.
-typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ void st_nt(void* p, uint4 v) {
-  __builtin_nontemporal_store(u32x4_t{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4_t*>(p));
-}
-__device__ __forceinline__ void st_nt(void* p, uint2 v) {
-  __builtin_nontemporal_store(u32x2_t{v.x, v.y}, reinterpret_cast<u32x2_t*>(p));
-}
-__device__ __forceinline__ void st_nt(void* p, uint32_t v) {
-  __builtin_nontemporal_store(v, reinterpret_cast<uint32_t*>(p));
-}
-__device__ __forceinline__ void st_nt8(uint8_t* p, uint8_t v) { __builtin_nontemporal_store(v, p); }
-
 // ---------------------------------------------------------------------------
 // Tensor amax
 // ---------------------------------------------------------------------------
@@ -176,6 +156,14 @@ __device__ __forceinline__ uint32_t encode8(const float* v, uint32_t key, uint32
     return sr_pack8(v, h);
   }
 }
+
+// Non-temporal output stores, for the casts whose workgroups write whole
+// contiguous lines (the row cast and the staged column stores): their codes
+// and scales are read next by another kernel (a GEMM), and dirty lines left
+// in the caches would be written back while the next quantize call's amax
+// pass streams its input.  Casts that write partial lines per workgroup (the
+// fused row copy, the 2D tile cast's row-major codes) keep ordinary stores:
+// non-temporal partial lines made them 3-40 % slower.
 
 // ---------------------------------------------------------------------------
 // 1D row cast: blocks of 16 along a row; each lane owns whole blocks (two
