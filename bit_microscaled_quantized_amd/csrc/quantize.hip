@@ -157,13 +157,14 @@ __device__ __forceinline__ uint32_t encode8(const float* v, uint32_t key, uint32
   }
 }
 
-// Non-temporal output stores, for the casts whose workgroups write whole
-// contiguous lines (the row cast and the staged column stores): their codes
-// and scales are read next by another kernel (a GEMM), and dirty lines left
-// in the caches would be written back while the next quantize call's amax
-// pass streams its input.  Casts that write partial lines per workgroup (the
-// fused row copy, the 2D tile cast's row-major codes) keep ordinary stores:
-// non-temporal partial lines made them 3-40 % slower.
+// Non-temporal output stores, where a workgroup writes whole contiguous lines
+// (the row cast, the staged column stores, the 2D tile cast's transposed
+// codes): the codes and scales are read next by another kernel (a GEMM), and
+// dirty lines left in the caches would be written back while the next
+// quantize call's amax pass streams its input.  Partial lines per workgroup
+// (the fused row copy, the 2D tile cast's row-major codes and its scales)
+// keep ordinary stores: non-temporal partial lines made those casts 8-41 %
+// slower.
 
 // ---------------------------------------------------------------------------
 // 1D row cast: blocks of 16 along a row; each lane owns whole blocks (two
@@ -821,11 +822,11 @@ __global__ __launch_bounds__(256) void k_cast_tile2d(const T* __restrict__ x, in
   uint8_t* dst = codes_t + ct * row_bytes + off;
   const uint8_t* src = &lt[lc][32 * q];
   if (off + 32 <= row_bytes && ((ct * row_bytes + off) & 15) == 0) {
-    reinterpret_cast<uint4*>(dst)[0] = reinterpret_cast<const uint4*>(src)[0];
-    reinterpret_cast<uint4*>(dst)[1] = reinterpret_cast<const uint4*>(src)[1];
+    st_nt(dst, reinterpret_cast<const uint4*>(src)[0]);
+    st_nt(dst + 16, reinterpret_cast<const uint4*>(src)[1]);
   } else {
     for (int k = 0; k < 4 && off + 8 * k < row_bytes; k++)
-      reinterpret_cast<uint2*>(dst)[k] = reinterpret_cast<const uint2*>(src)[k];
+      st_nt(dst + 8 * k, reinterpret_cast<const uint2*>(src)[k]);
   }
 }
 
