@@ -481,8 +481,16 @@ __global__ __launch_bounds__(256) void k_cast_row_rht(
     rtab_rht[threadIdx.x - 128] = element_scale(threadIdx.x - 128, s_rht);
   __syncthreads();
 
-  const int64_t t0 = (int64_t)blockIdx.y * kColTok;
-  const int64_t c0 = (int64_t)blockIdx.x * kColCols;
+  // XCD-aware tile order: the hardware deals workgroups round-robin over the
+  // 8 XCDs, so each XCD takes a contiguous range of tiles instead.  The two
+  // tiles that write the two halves of each row-copy line then run on the
+  // same XCD one after the other, and their halves meet in its L2.
+  const uint32_t G = gridDim.x * gridDim.y;
+  const uint32_t bid = blockIdx.y * gridDim.x + blockIdx.x;
+  const uint32_t xcd = bid & 7u, per = G >> 3, rem = G & 7u;
+  const uint32_t id = xcd < rem ? xcd * (per + 1) + (bid >> 3) : rem * (per + 1) + (xcd - rem) * per + (bid >> 3);
+  const int64_t t0 = (int64_t)(id / gridDim.x) * kColTok;
+  const int64_t c0 = (int64_t)(id % gridDim.x) * kColCols;
   const int co = (int)threadIdx.x % kColOct;
   const int g = (int)threadIdx.x / kColOct;
   const int64_t tg = t0 + 16 * g;
