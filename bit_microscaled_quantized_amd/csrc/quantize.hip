@@ -159,12 +159,13 @@ __device__ __forceinline__ uint32_t encode8(const float* v, uint32_t key, uint32
 
 // Non-temporal output stores, where a workgroup writes whole contiguous lines
 // (the row cast, the staged column stores, the 2D tile cast's transposed
-// codes): the codes and scales are read next by another kernel (a GEMM), and
-// dirty lines left in the caches would be written back while the next
-// quantize call's amax pass streams its input.  Partial lines per workgroup
-// (the fused row copy, the 2D tile cast's row-major codes and its scales)
-// keep ordinary stores: non-temporal partial lines made those casts 8-41 %
-// slower.
+// codes) or the rest of each line is written by a neighbour on the same XCD
+// right after (the fused cast's row codes): the codes and scales are read
+// next by another kernel (a GEMM), and dirty lines left in the caches would
+// be written back while the next quantize call's amax pass streams its input.
+// Partial lines from workgroups on different XCDs (the 2D tile cast's
+// row-major codes, scale bytes) keep ordinary stores: non-temporal partial
+// lines made those casts 8-41 % slower.
 
 // ---------------------------------------------------------------------------
 // 1D row cast: blocks of 16 along a row; each lane owns whole blocks (two
@@ -525,7 +526,7 @@ __global__ __launch_bounds__(256) void k_cast_row_rht(
     for (int e = 0; e < 8; e++) sv[e] = v[e] * r_b;
     const uint32_t w = encode8<RR>(sv, row_key, pair);
     if (valid) {
-      *reinterpret_cast<uint32_t*>(crow) = w;
+      st_nt(crow, w);
       if ((co & 1) == 0) *srow = (uint8_t)e_b;
     }
     crow += rbytes;
