@@ -4,9 +4,9 @@ one MI355X.
 
 A step is the whole hot path over one batch of the FFN up-projection layer
 (X bf16 8192x5120, W bf16 20480x5120 ~N(0, 0.02^2), dY bf16 8192x20480
-~N(0, 1e-3^2)): W 16x16 2D quantize (RNE, with the transposed copy); X row-1D
-RNE together with its random Hadamard + column-1D quantization (RNE, the Wgrad
-operand) in one call; Fprop GEMM; dY row-1D SR together with its random
+~N(0, 1e-3^2)): X row-1D RNE together with its random Hadamard + column-1D
+quantization (RNE, the Wgrad operand) in one call; W 16x16 2D quantize (RNE,
+with the transposed copy); Fprop GEMM; dY row-1D SR together with its random
 Hadamard + column-1D SR quantization in one call; Dgrad GEMM with the same
 quantized W; Wgrad GEMM.  Inputs are resident in HBM before the timed region.
 
@@ -141,14 +141,16 @@ def gpu_bench(inp, steps, warmup):
             fn()
             b.record()
             rec.append((name, a, b))
-        q = st.qw
-        timed("quant_w_2d", lambda: nv.nvfp4_quantize(
-            w, bf, O, I, I, nv.NVFP4_TILE_2D, nv.NVFP4_RNE, 0, q.codes, q.scales, q.codes_t,
-            q.scales_t, q.ts, q.amax))
+        # X first: its amax pass then follows the previous step's Wgrad GEMM
+        # (non-temporal output) rather than the 2D cast's row-major stores
         qx, b_ = st.qx, st.qx_t
         timed("quant_x_row_rht", lambda: nv.nvfp4_quantize_row_rht(
             x, bf, T, I, I, nv.NVFP4_RNE, 0, qx.codes, qx.scales, qx.ts, qx.amax, mask,
             nv.NVFP4_RNE, 0, b_.codes, b_.scales, b_.ts, b_.amax))
+        q = st.qw
+        timed("quant_w_2d", lambda: nv.nvfp4_quantize(
+            w, bf, O, I, I, nv.NVFP4_TILE_2D, nv.NVFP4_RNE, 0, q.codes, q.scales, q.codes_t,
+            q.scales_t, q.ts, q.amax))
         timed("gemm_fprop", lambda: nv.nvfp4_gemm(
             T, O, I, qx.codes, qx.scales, qx.ts, q.codes, q.scales, 16, q.ts, st.y, O, 0.0, workspace=st.ws))
         qd, a_ = st.qdy, st.qdy_t
