@@ -7,6 +7,7 @@ bit_microscaled_quantized_amd/libnvfp4.so (in-tree, next to the binding).
 """
 from __future__ import annotations
 
+import concurrent.futures
 import glob
 import os
 import shutil
@@ -36,20 +37,25 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libnvfp4)")
 
 
+def _compile(src: str, tmp: str, verbose: bool) -> str:
+    obj = os.path.join(tmp, os.path.basename(src) + ".o")
+    cmd = [hipcc(), *HIPCC_FLAGS, "-I", CSRC, "-c", src, "-o", obj]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError(f"hipcc failed on {src}")
+    return obj
+
+
 def build(verbose: bool = False) -> str:
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-    objs = []
     with tempfile.TemporaryDirectory() as tmp:
-        for src in srcs:
-            obj = os.path.join(tmp, os.path.basename(src) + ".o")
-            cmd = [hipcc(), *HIPCC_FLAGS, "-I", CSRC, "-c", src, "-o", obj]
-            if verbose:
-                print(" ".join(cmd), flush=True)
-            r = subprocess.run(cmd, capture_output=True, text=True)
-            if r.returncode != 0:
-                sys.stderr.write(r.stdout + r.stderr)
-                raise RuntimeError(f"hipcc failed on {src}")
-            objs.append(obj)
+        # one hipcc per translation unit, in parallel
+        workers = max(1, min(len(srcs), os.cpu_count() or 1, 8))
+        with concurrent.futures.ThreadPoolExecutor(workers) as pool:
+            objs = list(pool.map(lambda s: _compile(s, tmp, verbose), srcs))
         tmp_lib = LIB + ".tmp"
         cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp_lib, *objs]
         r = subprocess.run(cmd, capture_output=True, text=True)

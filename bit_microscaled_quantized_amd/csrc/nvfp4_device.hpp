@@ -133,47 +133,68 @@ __host__ __device__ __forceinline__ uint32_t pcg_host(uint32_t v) {
 }
 
 // Stochastic rounding of scaled values to E2M1 codes: with a = min(|v|, 6),
-// lo the largest E2M1 magnitude <= a, hi the next one and F = floor(frac *
-// 2^22) the fraction frac = (a - lo) / (hi - lo) truncated to 22 bits, round
-// up iff F > 64 r16 (r16 the element's 16 random bits), sign kept.  It runs
-// on gfx950's v_cvt_scalef32_sr_pk_fp4_f32, whose rule was measured on the
-// device: sign-magnitude; with F as above, element 0 of the pair rounds up
-// iff F + R[31:10] >= 2^22 and element 1 iff F + R[30:9] >= 2^22 (R the
-// 32-bit random operand); a >= 6 gives magnitude code 7.  F > 64 r16 is
-// F + (2^22 - 1 - 64 r16) >= 2^22, so the element's field must hold
-// 2^22 - 1 - 64 r16: R = ~(r16 << 16) for element 0 (low 10 bits free) and
-// (~r16 << 15) | 0x7FFF for element 1 (low 9 bits free).  The scaled values
-// go in as they are, with scale operand 1.0.
+// lo the largest E2M1 magnitude <= a and hi the next one, round up iff
+// r16 < frac * 2^16, frac = (a - lo) / (hi - lo) exact (r16 the element's 16
+// random bits), sign kept.  It runs on gfx950's v_cvt_scalef32_sr_pk_fp4_f32,
+// whose rule was measured on the device: sign-magnitude; the input is divided
+// by the scale operand's power of two; with F the fraction of the quotient's
+// magnitude truncated to 22 bits, floor(frac * 2^22), element 0 of the pair
+// rounds up iff F + R[31:10] >= 2^22 and element 1 iff F + R[30:9] >= 2^22 (R
+// the 32-bit random operand); magnitudes >= 6 give code 7.  Two adjustments
+// turn that into the rule above exactly:
+//   * F must count as ceil(frac * 2^22).  For a >= 1, a is a multiple of
+//     2^-23 and frac * 2^22 = (a - lo) * 2^22 / step an integer (steps 1/2,
+//     1, 2), so F is exact.  Below 1 the step is 1/2 and frac * 2^22 =
+//     (a - lo) * 2^23: rounding |v| up to a multiple of 2^-23 first
+//     (sr_hw_input; lo is on that grid) turns the truncation into the
+//     ceiling, and leaves every |v| >= 1 unchanged;
+//   * r16 < frac * 2^16 is 64 r16 < ceil(frac * 2^22), i.e.
+//     F + (2^22 - 1 - 64 r16) >= 2^22, so the element's field must hold
+//     2^22 - 1 - 64 r16: R = ~(r16 << 16) for element 0 (low 10 bits free) and
+//     (~r16 << 15) | 0x7FFF for element 1 (low 9 bits free).
+// The rounded-up input goes in as ceil(|v| * 2^23) with v's sign and the
+// scale operand 2^23, which the conversion divides out exactly.
 // The two elements of a pair draw independent bits, so each pair goes through
 // two conversions, one correct in its low nibble (element 0) and one in its
 // high nibble (element 1), merged by one bit select per 8 codes.
 
-// One SR conversion (scale 1.0) into byte `sel` of d, the other bytes of d
+// ceil(|v| * 2^23) with v's sign, exact: every scaled value has |v| < 10 (a
+// block's maximum maps to at most 6 * (1 + 2^-4) through a normal E4M3 scale
+// and to at most 9 through a subnormal one; the FLT_MAX clamps only shrink
+// it).
+__device__ __forceinline__ float sr_hw_input(float v) {
+  const float t = __builtin_ceilf(__builtin_fabsf(v) * 8388608.0f);
+  return __builtin_copysignf(t, v);
+}
+
+// One SR conversion (scale 2^23) into byte `sel` of d, the other bytes of d
 // kept.  Written as inline asm with d read-write: the compiler's builtin for
 // this instruction does not tie its `old` operand to the destination, so the
 // kept bytes would be whatever the destination register held.  The first
 // conversion into a word (FIRST) writes byte 0 and leaves bytes that later
-// conversions overwrite, so its destination needs no initial value.
+// conversions overwrite, so its destination needs no initial value.  The
+// scale is an SGPR operand (this encoding takes no 32-bit literal).
 template <int sel, bool FIRST = false>
 __device__ __forceinline__ void cvt_sr_pk(uint32_t& d, double x, uint32_t r) {
+  const float s = 8388608.0f;  // 2^23
   if constexpr (FIRST) {
     static_assert(sel == 0, "only the byte-0 conversion starts a word");
-    asm volatile("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, 1.0" : "=v"(d) : "v"(x), "v"(r));
+    asm volatile("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, %3" : "=v"(d) : "v"(x), "v"(r), "s"(s));
   } else if constexpr (sel == 0) {
-    asm volatile("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, 1.0" : "+v"(d) : "v"(x), "v"(r));
+    asm volatile("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, %3" : "+v"(d) : "v"(x), "v"(r), "s"(s));
   } else if constexpr (sel == 1) {
-    asm volatile("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, 1.0 op_sel:[0,0,1,0]" : "+v"(d) : "v"(x), "v"(r));
+    asm volatile("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, %3 op_sel:[0,0,1,0]" : "+v"(d) : "v"(x), "v"(r), "s"(s));
   } else if constexpr (sel == 2) {
-    asm volatile("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, 1.0 op_sel:[0,0,0,1]" : "+v"(d) : "v"(x), "v"(r));
+    asm volatile("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, %3 op_sel:[0,0,0,1]" : "+v"(d) : "v"(x), "v"(r), "s"(s));
   } else {
-    asm volatile("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, 1.0 op_sel:[0,0,1,1]" : "+v"(d) : "v"(x), "v"(r));
+    asm volatile("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, %3 op_sel:[0,0,1,1]" : "+v"(d) : "v"(x), "v"(r), "s"(s));
   }
 }
 
 template <int sel>
 __device__ __forceinline__ void sr_pk(uint32_t& lo, uint32_t& hi, float v0, float v1, uint32_t h) {
   typedef float float2v __attribute__((ext_vector_type(2)));
-  const float2v xv = {v0, v1};
+  const float2v xv = {sr_hw_input(v0), sr_hw_input(v1)};
   const double x = __builtin_bit_cast(double, xv);  // the pair as one 64-bit register pair
   const uint32_t nh = ~h;  // 65535 - r16 in each half: r16(v0) = h & 0xFFFF, r16(v1) = h >> 16
   cvt_sr_pk<sel, sel == 0>(lo, x, (nh << 16) | 0xFFFFu);

@@ -20,9 +20,16 @@
  *   e_b    = E4M3 nearest-even, saturating at 448, of (amax_b / 6) * S_enc
  *   r_b    = e_b == 0 ? 0 : min(S_enc / dec(e_b), FLT_MAX);   v = y * r_b
  *   code   = sign(y) << 3 | E2M1 index of |v|: RNE (ties to even index,
- *            saturating at 6) or SR (round up iff r16 < frac * 65536, r16 =
- *            16 bits of the pcg hash of Jarzynski & Olano, JCGT 2020, keyed by
- *            the seed and the element's index in the output code array).
+ *            saturating at 6) or SR: with a = min(|v|, 6) between the E2M1
+ *            magnitudes lo <= a < hi and frac = (a - lo) / (hi - lo) taken
+ *            exactly, round up iff r16 < frac * 65536, so P(up) =
+ *            ceil(frac * 65536) / 65536 (technique 4, "Arredondamento
+ *            Estocastico": rounding up with probability given by the distance
+ *            keeps the expected value).  r16 = 16 bits of the pcg hash of
+ *            Jarzynski & Olano, JCGT 2020: key = pcg(lo32(seed) ^
+ *            pcg(hi32(seed))), w = pcg(key ^ (i >> 1)), r16 = the low half of w
+ *            for even i and the high half for odd i, i the element's index in
+ *            the output code array.
  *   Dequantized value = e2m1(code) * dec(e_b) * tensor_scale.
  *
  * Packing: two codes per byte, the even element in the low nibble.

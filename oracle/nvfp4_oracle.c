@@ -37,16 +37,22 @@
  *   element scale  r_b = 0 if e_b == 0 else min(S_enc / dec(e_b), FLT_MAX)
  *   scaled value   v = y * r_b, E2M1 code = sign(y) | magnitude index
  *   RNE            nearest E2M1 magnitude, ties to the even index, clamp at 6
- *   SR             up iff 64 * r16 < floor(frac * 2^22), frac = (a - lo) / (hi - lo):
- *                  the fraction truncated to 22 bits against 16 random bits
+ *   SR             up iff r16 < frac * 2^16, frac = (a - lo) / (hi - lo) exact,
+ *                  r16 the element's 16 random bits
  *   random bits    r16 from the pcg hash keyed by (seed, output index)
  *   RHT            per 16 tokens of one column: sign flips, FWHT stages
  *                  h = 1, 2, 4, 8 as (a + b, a - b), then * 0.25
  *
- * Parity pins: see tests/test_oracle_pins.py.  The FP32 operation order of
- * the scale rule and of the FWHT is a reading, pinned only on inputs where it
- * is exact and by the invariants the pages state ("parity unpinned" for the
- * general rounding order).
+ * Parity pins: see tests/test_oracle_pins.py.  Parity unpinned (readings no
+ * source fixes, so no test can tell a plausible alternative from them):
+ *   - the bits of the random source: the pcg steps and constants follow the
+ *     publication, but the key derivation from the seed, the pair index
+ *     i >> 1 and the even-low / odd-high half-word split are this oracle's
+ *     choice, checked only for uniformity, distinctness and invertibility;
+ *   - the FP32 rounding order of the scale rule and of the FWHT where it is
+ *     inexact (pinned only on inputs where it is exact, and by invariants);
+ *   - the FLT_MAX clamps of S_enc and r_b, checked only through the
+ *     quantization error bound and a hand-derived example at the clamp.
  */
 #include <float.h>
 #include <math.h>
@@ -143,16 +149,16 @@ int ora_e2m1_rne(float v)
 
 /* E2M1 stochastic rounding of v with 16 random bits r16 in [0, 65535].
  * a = min(|v|, 6); lo = largest magnitude <= a, hi = the next one;
- * frac = (a - lo) / (hi - lo), truncated to 22 bits: f22 = floor(frac * 2^22).
- * Rounds up iff 64 * r16 < f22, i.e. iff r16 < f22 / 64, so the probability
- * of rounding up is ceil(f22 / 64) / 65536, within 2^-16 of frac.  For
- * a >= 1, frac * 2^22 is already an integer (the low 22 mantissa bits of a),
- * and the truncation only matters below 1.  Everything here is exact in
- * double precision. */
+ * frac = (a - lo) / (hi - lo), exact.  Rounds up iff r16 < frac * 2^16, so
+ * exactly ceil(frac * 2^16) of the 2^16 values of r16 round up: the expected
+ * result is within 2^-16 of a step above a, and representable values never
+ * move.  Everything here is exact in double precision ([NV-SUM] technique 4:
+ * gradients are rounded up with a probability given by their distance to the
+ * two neighbours, which keeps the expected value). */
 int ora_e2m1_sr(float v, uint32_t r16)
 {
     int sign = signbit(v) ? 8 : 0, k = 0, i;
-    double a = fabs((double)v), frac, f22;
+    double a = fabs((double)v), frac;
     if (a > 6.0)
         a = 6.0;
     for (i = 0; i < 8; i++)
@@ -161,8 +167,7 @@ int ora_e2m1_sr(float v, uint32_t r16)
     if (k == 7)
         return sign | 7;
     frac = (a - E2M1_MAG[k]) / (E2M1_MAG[k + 1] - E2M1_MAG[k]);
-    f22 = floor(frac * 4194304.0);
-    if (64.0 * (double)r16 < f22)
+    if ((double)r16 < frac * 65536.0)
         k += 1;
     return sign | k;
 }

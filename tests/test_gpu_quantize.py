@@ -151,8 +151,37 @@ def test_golden_worked_example_on_gpu(ora):
     assert not g["codes"][1:].any() and not g["scales"][1:].any()
 
 
+def test_golden_flt_max_clamps_on_gpu(ora):
+    """The hand-derived example where both FLT_MAX clamps of the scale rule
+    act (S_enc, and r_b in the second block)."""
+    g_ = json.load(open(os.path.join(GOLDEN, "row1d_flt_max_clamps.json")))
+    rows, cols = g_["shape"]
+    x = np.zeros((rows, cols), np.float32)
+    x[0] = [float.fromhex(v) for v in g_["input_row0_fp32_hex"]]
+    g = gpuio.gpu_quantize(x, nv.NVFP4_ROW_1D, nv.NVFP4_RNE)
+    assert [f"{b:02X}" for b in g["codes"][0]] == g_["expected_codes_row0_hex"]
+    assert [f"{b:02X}" for b in g["scales"][0]] == g_["expected_scales_row0_hex"]
+    assert np.float32(g["tensor_scale"]).view(np.uint32) == int(g_["expected_tensor_scale_bits"], 16)
+    assert np.float32(g["amax"]).view(np.uint32) == int(g_["expected_amax_bits"], 16)
+    assert not g["codes"][1:].any() and not g["scales"][1:].any()
+
+
+def _clamp_tensor():
+    """The clamp example's row repeated over a 32 x 64 tensor (transposed in
+    alternate 16-row bands, so column blocks see the clamps too)."""
+    g_ = json.load(open(os.path.join(GOLDEN, "row1d_flt_max_clamps.json")))
+    row = np.array([float.fromhex(v) for v in g_["input_row0_fp32_hex"]], np.float32)
+    x = np.zeros((32, 64), np.float32)
+    x[0, :32] = row
+    x[5, 32:] = -row
+    x[16:, 7] = row[:16]
+    x[16:, 40] = row[16:]
+    return x
+
+
 def _edge_tensors():
     out = {}
+    out["flt_max_clamps"] = _clamp_tensor()
     out["zeros"] = np.zeros((32, 64), np.float32)
     z = np.zeros((32, 64), np.float32)
     z[::3, ::5] = -0.0

@@ -148,6 +148,27 @@ def test_golden_row1d_worked_example(ora):
     assert not q["codes"][1:].any() and not q["scales"][1:].any()
 
 
+def golden_clamp_input():
+    g = json.load(open(os.path.join(GOLDEN, "row1d_flt_max_clamps.json")))
+    rows, cols = g["shape"]
+    x = np.zeros((rows, cols), np.float32)
+    x[0] = [float.fromhex(v) for v in g["input_row0_fp32_hex"]]
+    return g, x
+
+
+def test_golden_row1d_flt_max_clamps(ora):
+    """Both FLT_MAX clamps of the scale reading on a hand-derived example."""
+    g, x = golden_clamp_input()
+    q = ora.quantize(x, ora.ROW_1D, ora.RNE)
+    assert f32_bits(q["tensor_scale"]) == int(g["expected_tensor_scale_bits"], 16)
+    assert f32_bits(q["amax"]) == int(g["expected_amax_bits"], 16)
+    assert [f"{b:02X}" for b in q["codes"][0]] == g["expected_codes_row0_hex"]
+    assert [f"{b:02X}" for b in q["scales"][0]] == g["expected_scales_row0_hex"]
+    assert not q["codes"][1:].any() and not q["scales"][1:].any()
+    assert ora.encode_scale(float(np.float32(1.5 * 2.0 ** -118))) == float(np.finfo(np.float32).max)
+    assert ora.element_scale(0x28, float(np.finfo(np.float32).max)) == float(np.finfo(np.float32).max)
+
+
 # ---------------------------------------------------------------- P4: tensor scale
 def test_tensor_scale_puts_amax_on_the_largest_product(ora):
     rng = np.random.default_rng(2)
@@ -216,8 +237,14 @@ def test_rht_spreads_an_outlier(ora):
 
 # ---------------------------------------------------------------- P6: SR
 @pytest.mark.parametrize("v", [0.1, 0.3, 0.6, 0.75, 1.3, 1.7, 2.2, 2.5, 3.7, 4.4, 5.9, -1.1, -0.01,
-                               0.5 + 2.0 ** -24, 0.25 + 2.0 ** -25, 2.0 ** -30, 0.9999999])
+                               0.5 + 2.0 ** -24, 0.25 + 2.0 ** -25, 2.0 ** -30, 0.9999999,
+                               2.0 ** -149, -(2.0 ** -126), 1.0 - 2.0 ** -24, 0.5 - 2.0 ** -25,
+                               5.0 + 2.0 ** -21, 3.0 - 2.0 ** -22])
 def test_sr_exact_expectation_over_all_random_values(ora, v):
+    """Rounding up with probability equal to the fractional distance
+    (unbiased) and 16 random bits: exactly ceil(frac * 2^16) of the 2^16
+    values of r16 round up, for every input, with frac computed here in
+    rational arithmetic."""
     v = f32(v)
     a = abs(v)
     k = max(i for i in range(8) if E2M1[i] <= a)
@@ -227,37 +254,29 @@ def test_sr_exact_expectation_over_all_random_values(ora, v):
     ups = 0
     for r16 in range(65536):
         c = ora.e2m1_sr(v, r16)
-        assert (c & 8) == (8 if v < 0 else 0)
+        assert (c & 8) == (8 if math.copysign(1.0, v) < 0 else 0)
         assert c & 7 in (k, k + 1)  # only the two neighbours
         ups += (c & 7) == k + 1
-    # unbiased up to one part in 2^16 of a step, either way: E[q] - a is
-    # (ups / 2^16 - frac) * step, and |ups / 2^16 - frac| < 2^-16
+    assert ups == math.ceil(frac * 65536)
+    # so the expectation is within one part in 2^16 of a step above a
     mean = Fraction(lo) + Fraction(ups, 65536) * (Fraction(hi) - Fraction(lo))
-    assert abs(mean - Fraction(a)) < Fraction(hi - lo) / 65536
-    # for a >= 1 the fraction is a multiple of 2^-22, so P(up) is exactly
-    # ceil(frac * 2^16) / 2^16 (the 16 random bits resolve it completely)
-    if a >= 1:
-        assert ups == math.ceil(frac * 65536)
-    # below 1 the fraction is resolved to 22 bits: values within 2^-22 of a
-    # step of each other round alike, so P(up) never exceeds the exact
-    # ceiling and falls short of it only when frac * 2^16 lies within 2^-6
-    # above an integer
-    else:
-        assert ups <= math.ceil(frac * 65536)
-        if ups < math.ceil(frac * 65536):
-            assert frac * 65536 - math.floor(frac * 65536) <= Fraction(1, 64)
+    assert Fraction(0) <= mean - Fraction(a) < Fraction(hi - lo) / 65536
 
 
-def test_sr_rounds_values_within_one_22_bit_step_alike(ora):
-    # a < 1: a fraction below 2^-22 of a step never rounds up, one at 2^-22
-    # rounds up only for r16 = 0
-    for lo, step in ((0.0, 0.5), (0.5, 0.5)):
-        tiny = f32(lo + step * 2.0 ** -23)
-        assert tiny != f32(lo)
-        assert all(ora.e2m1_sr(tiny, r) & 7 == ora.e2m1_sr(f32(lo), 0) & 7 for r in (0, 1, 65535))
-        one = f32(lo + step * 2.0 ** -22)
+def test_sr_resolves_the_smallest_fractions(ora):
+    # a value one FP32 ulp above a grid point, however small its fraction of
+    # the step, rounds up for r16 = 0 and only then (r16 < frac * 2^16 with
+    # 0 < frac * 2^16 <= 1); the grid points themselves never move
+    for lo in (0.0, 0.5, 1.0, 2.0, 4.0):
         k = ora.e2m1_sr(f32(lo), 0)
-        assert ora.e2m1_sr(one, 0) == k + 1 and ora.e2m1_sr(one, 1) == k
+        up = nextup(lo)
+        assert ora.e2m1_sr(up, 0) == k + 1
+        assert all(ora.e2m1_sr(up, r) == k for r in (1, 2, 65535))
+        assert all(ora.e2m1_sr(f32(lo), r) == k for r in (0, 1, 65535))
+    # just below a grid point: up for every r16 below ceil(frac * 2^16) = 2^16
+    for hi_code, hi in ((1, 0.5), (2, 1.0), (5, 3.0), (7, 6.0)):
+        below = nextdown(hi)
+        assert all(ora.e2m1_sr(below, r) == hi_code for r in (0, 65534, 65535))
 
 
 def test_sr_saturates_and_mean_over_seeds(ora):
@@ -325,11 +344,17 @@ def test_block_max_keeps_near_fp8_precision(ora):
     assert worst <= 2.0 ** -4 * (1 + 1e-6)
 
 
-def test_quantization_error_bound(ora):
+@pytest.mark.parametrize("scale", [1.0, 2.0 ** -120])
+def test_quantization_error_bound(ora, scale):
     """RNE lands on the nearest grid value: |deq - x| <= half the local E2M1
-    gap times the block's decode scale (plus FP32 scale rounding)."""
-    x = synth.normal(7, (32, 128))
+    gap times the block's decode scale (plus FP32 scale rounding).  At 2^-120
+    the tensor scale 2688 / amax_t overflows FP32 and is clamped to FLT_MAX;
+    encode and decode still agree, so the bound holds there too."""
+    x = (synth.normal(7, (32, 128)) * np.float32(scale)).astype(np.float32)
     q = ora.quantize(x, ora.ROW_1D, ora.RNE)
+    if scale != 1.0:
+        assert 2688.0 / q["amax"] > float(np.finfo(np.float32).max)  # the clamp is active
+        assert q["tensor_scale"] == f32(1.0 / float(np.finfo(np.float32).max))
     deq = ora.dequant(q["codes"], q["scales"], q["tensor_scale"])
     dec = np.array([ora.e4m3_value(int(e)) for e in q["scales"].reshape(-1)]).reshape(32, 8)
     unit = np.repeat(dec, 16, axis=1) * q["tensor_scale"]  # value of 1.0 on the grid
