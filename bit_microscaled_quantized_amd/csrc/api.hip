@@ -140,6 +140,30 @@ nvfp4_status nvfp4_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
                      b_tensor_scale, c, 0, ldc, beta, workspace, workspace_bytes, stream);
 }
 
+nvfp4_status nvfp4_gemm_noalloc(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
+                                const uint8_t* a_scales, const float* a_tensor_scale,
+                                const uint8_t* b_codes, const uint8_t* b_scales,
+                                int32_t b_scale_rowdiv, const float* b_tensor_scale, float* c,
+                                int64_t ldc, float beta, void* stream) {
+  if (a_codes == nullptr || a_scales == nullptr || a_tensor_scale == nullptr ||
+      b_codes == nullptr || b_scales == nullptr || b_tensor_scale == nullptr || c == nullptr)
+    return NVFP4_EINVAL;
+  if (b_scale_rowdiv != 1 && b_scale_rowdiv != 16) return NVFP4_EINVAL;
+  if (beta != 0.0f && beta != 1.0f) return NVFP4_EINVAL;
+  nvfp4_status st = check_gemm_shape(M, N, K);
+  if (st != NVFP4_OK) return st;
+  if (M * (K / 2) >= (int64_t(1) << 32) || N * (K / 2) >= (int64_t(1) << 32) || ldc < N)
+    return NVFP4_ESHAPE;
+  if (!aligned16(a_codes) || !aligned16(b_codes) || !aligned4(a_scales) || !aligned4(b_scales) ||
+      !aligned4(a_tensor_scale) || !aligned4(b_tensor_scale) || !aligned16(c) || ldc % 4 != 0)
+    return NVFP4_EALIGN;
+  if (nvfp4::gemm_workspace_size(M, N, K) > nvfp4::static_workspace_bytes()) return NVFP4_ESCRATCH;
+  hipError_t e = nvfp4::launch_gemm_static_ws(M, N, K, a_codes, a_scales, a_tensor_scale, b_codes,
+                                              b_scales, b_scale_rowdiv, b_tensor_scale, c, ldc,
+                                              beta == 1.0f ? 1 : 0, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? NVFP4_OK : NVFP4_EHIP;
+}
+
 nvfp4_status nvfp4_gemm_bf16(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
                              const uint8_t* a_scales, const float* a_tensor_scale,
                              const uint8_t* b_codes, const uint8_t* b_scales,
@@ -214,6 +238,8 @@ const char* nvfp4_status_str(int status) {
     case NVFP4_ESHAPE: return "NVFP4_ESHAPE: unsupported shape";
     case NVFP4_EALIGN: return "NVFP4_EALIGN: misaligned pointer or leading dimension";
     case NVFP4_EHIP: return "NVFP4_EHIP: HIP launch failed";
+    case NVFP4_ESCRATCH:
+      return "NVFP4_ESCRATCH: the problem needs more split workspace than the static scratch holds";
     default: return "unknown nvfp4 status";
   }
 }

@@ -56,7 +56,6 @@
 // order 0 .. S-1, scales by the tensor scales and applies beta, so the result
 // does not depend on scheduling.
 #include <mutex>
-#include <vector>
 
 #include "gemm_tiling.hpp"
 #include "nvfp4_device.hpp"
@@ -418,20 +417,50 @@ __global__ __launch_bounds__(256) void k_gemm_split_reduce(int M, int N, int ful
 
 namespace {
 
-// Compute units of the current device (cached per device).
+constexpr int kMaxDevices = 64;
+
+// Compute units of the current device (cached per device, no allocation).
 int device_cus() {
   static std::mutex mu;
-  static std::vector<int> cache;
+  static int cache[kMaxDevices] = {};
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
   std::lock_guard<std::mutex> lock(mu);
-  if ((int)cache.size() <= dev) cache.resize(dev + 1, 0);
   if (cache[dev] == 0) {
     int n = 0;
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
     cache[dev] = n;
   }
   return cache[dev];
+}
+
+// Split-tail workspace of the allocation-free entry point, one copy per
+// device for the life of the process.  The split plan fills at most one round
+// of 256 x 256 FP32 partial tiles, 256 KiB per compute unit: 64 MiB holds the
+// plan of any shape on a 256-CU MI355X.  Every call on a device shares its
+// copy; the GEMM writes each partial tile whole before the reduction reads
+// it, so nothing needs clearing, but calls that overlap on one device race.
+constexpr int64_t kStaticWorkspaceBytes = int64_t(64) << 20;
+__device__ __align__(256) float scratch[kStaticWorkspaceBytes / 4];
+
+// Device address of the current device's `scratch`, looked up once per
+// device (the host-side name is not a device address).
+hipError_t static_workspace(void** ptr) {
+  static std::mutex mu;
+  static void* cache[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (cache[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    cache[dev] = p;
+  }
+  *ptr = cache[dev];
+  return hipSuccess;
 }
 
 }  // namespace
@@ -515,6 +544,20 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
                          static_cast<uint16_t*>(c), ldc, accumulate, workspace, workspace_bytes, s);
   return launch_gemm_t(M, N, K, a_codes, a_scales, a_ts, b_codes, b_scales, b_rowdiv, b_ts,
                        static_cast<float*>(c), ldc, accumulate, workspace, workspace_bytes, s);
+}
+
+int64_t static_workspace_bytes() { return kStaticWorkspaceBytes; }
+
+hipError_t launch_gemm_static_ws(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
+                                 const uint8_t* a_scales, const float* a_ts,
+                                 const uint8_t* b_codes, const uint8_t* b_scales, int b_rowdiv,
+                                 const float* b_ts, float* c, int64_t ldc, int accumulate,
+                                 hipStream_t s) {
+  void* ws = nullptr;
+  hipError_t e = static_workspace(&ws);
+  if (e != hipSuccess) return e;
+  return launch_gemm_t(M, N, K, a_codes, a_scales, a_ts, b_codes, b_scales, b_rowdiv, b_ts, c, ldc,
+                       accumulate, ws, kStaticWorkspaceBytes, s);
 }
 
 }  // namespace nvfp4

@@ -44,6 +44,16 @@ hipError_t launch_mx_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_code
                           float* c, int64_t ldc, int accumulate, void* workspace,
                           int64_t workspace_bytes, hipStream_t s);
 
+// launch_gemm (FP32 output) with the split-tail partials in the library's
+// per-device static workspace instead of a caller's buffer; it never
+// allocates.  static_workspace_bytes() is that workspace's size.
+hipError_t launch_gemm_static_ws(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
+                                 const uint8_t* a_scales, const float* a_ts,
+                                 const uint8_t* b_codes, const uint8_t* b_scales, int b_rowdiv,
+                                 const float* b_ts, float* c, int64_t ldc, int accumulate,
+                                 hipStream_t s);
+int64_t static_workspace_bytes();
+
 // Workspace bytes launch_gemm (and launch_mx_gemm) uses for this shape on the current device
 // (0: no split).
 int64_t gemm_workspace_size(int64_t M, int64_t N, int64_t K);

@@ -14,13 +14,13 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libnvfp4.so")
 
-NVFP4_OK, NVFP4_EINVAL, NVFP4_ESHAPE, NVFP4_EALIGN, NVFP4_EHIP = range(5)
+NVFP4_OK, NVFP4_EINVAL, NVFP4_ESHAPE, NVFP4_EALIGN, NVFP4_EHIP, NVFP4_ESCRATCH = range(6)
 NVFP4_BF16, NVFP4_F32 = 0, 1
 NVFP4_RNE, NVFP4_SR = 0, 1
 NVFP4_ROW_1D, NVFP4_COL_1D, NVFP4_TILE_2D = 0, 1, 2
 
 EXPORTED = ("nvfp4_quantize", "nvfp4_rht_quantize", "nvfp4_quantize_row_rht", "nvfp4_gemm",
-            "nvfp4_gemm_bf16", "nvfp4_dequantize", "nvfp4_gemm_workspace_size", "nvfp4_status_str",
+            "nvfp4_gemm_noalloc", "nvfp4_gemm_bf16", "nvfp4_dequantize", "nvfp4_gemm_workspace_size", "nvfp4_status_str",
             "mxfp4_quantize", "mxfp4_gemm")
 
 _lib = None
@@ -60,6 +60,8 @@ def load_library():
     L.mxfp4_gemm.restype = i32
     L.nvfp4_gemm.argtypes = [i64, i64, i64, vp, vp, vp, vp, vp, i32, vp, vp, i64, f32, vp, i64, vp]
     L.nvfp4_gemm.restype = i32
+    L.nvfp4_gemm_noalloc.argtypes = [i64, i64, i64, vp, vp, vp, vp, vp, i32, vp, vp, i64, f32, vp]
+    L.nvfp4_gemm_noalloc.restype = i32
     L.nvfp4_gemm_bf16.argtypes = [i64, i64, i64, vp, vp, vp, vp, vp, i32, vp, vp, i64, f32, vp, i64,
                                   vp]
     L.nvfp4_gemm_bf16.restype = i32
@@ -142,6 +144,17 @@ def nvfp4_gemm(M, N, K, a_codes, a_scales, a_tensor_scale, b_codes, b_scales, b_
         _addr(b_scales), b_scale_rowdiv, _addr(b_tensor_scale), _addr(c), ldc, float(beta),
         _addr(workspace), int(workspace_bytes), _stream(stream))
     return _check("nvfp4_gemm", st, raise_on_error)
+
+
+def nvfp4_gemm_noalloc(M, N, K, a_codes, a_scales, a_tensor_scale, b_codes, b_scales,
+                       b_scale_rowdiv, b_tensor_scale, c, ldc, beta, stream=None,
+                       raise_on_error=True) -> int:
+    """nvfp4_gemm with the split workspace in the library's static scratch."""
+    st = load_library().nvfp4_gemm_noalloc(
+        M, N, K, _addr(a_codes), _addr(a_scales), _addr(a_tensor_scale), _addr(b_codes),
+        _addr(b_scales), b_scale_rowdiv, _addr(b_tensor_scale), _addr(c), ldc, float(beta),
+        _stream(stream))
+    return _check("nvfp4_gemm_noalloc", st, raise_on_error)
 
 
 def nvfp4_gemm_bf16(M, N, K, a_codes, a_scales, a_tensor_scale, b_codes, b_scales, b_scale_rowdiv,

@@ -63,7 +63,8 @@ typedef enum {
     NVFP4_EINVAL = 1, /* null pointer, unknown enum value, bad rowdiv/beta */
     NVFP4_ESHAPE = 2, /* dimension not a multiple of 16 (quantize) or of the GEMM tile */
     NVFP4_EALIGN = 3, /* pointer or leading dimension not 16-byte aligned */
-    NVFP4_EHIP = 4    /* a HIP launch failed */
+    NVFP4_EHIP = 4,   /* a HIP launch failed */
+    NVFP4_ESCRATCH = 5 /* nvfp4_gemm_noalloc: more split workspace than its static scratch */
 } nvfp4_status;
 
 typedef enum { NVFP4_BF16 = 0, NVFP4_F32 = 1 } nvfp4_dtype;
@@ -176,6 +177,28 @@ nvfp4_status nvfp4_gemm(int64_t M, int64_t N, int64_t K, const uint8_t *a_codes,
                         const uint8_t *b_codes, const uint8_t *b_scales, int32_t b_scale_rowdiv,
                         const float *b_tensor_scale, float *c, int64_t ldc, float beta,
                         void *workspace, int64_t workspace_bytes, void *stream);
+
+/*
+ * nvfp4_gemm_noalloc -- nvfp4_gemm for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same arguments without the workspace pair, the same
+ * FP32 result as nvfp4_gemm given a workspace of nvfp4_gemm_workspace_size()
+ * bytes (bit for bit: same kernels, same split of the last round of tiles).
+ * The split partials live in a file-scope static device array of 64 MiB, one
+ * per device, held until the process ends (256 KiB per compute unit of a
+ * 256-CU MI355X, the most the split plan uses there).  It allocates nothing:
+ * no hipMalloc, hipFree or allocating library call.  Every call on a device
+ * shares that device's array, so calls that overlap on one device (different
+ * streams, or graph replays in flight together) race; calls on one stream are
+ * safe.  A shape whose split would need more than the static array (possible
+ * only on a device with more than 256 compute units) returns NVFP4_ESCRATCH
+ * before anything is enqueued.  Other errors as for nvfp4_gemm.
+ */
+nvfp4_status nvfp4_gemm_noalloc(int64_t M, int64_t N, int64_t K, const uint8_t *a_codes,
+                                const uint8_t *a_scales, const float *a_tensor_scale,
+                                const uint8_t *b_codes, const uint8_t *b_scales,
+                                int32_t b_scale_rowdiv, const float *b_tensor_scale, float *c,
+                                int64_t ldc, float beta, void *stream);
 
 /*
  * nvfp4_gemm_bf16 -- nvfp4_gemm with a BF16 output: every argument as for

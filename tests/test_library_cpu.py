@@ -215,3 +215,22 @@ def test_gemm_bf16_argument_errors():
     assert g16(K=96) == b.NVFP4_ESHAPE
     assert g16(ldc=260) == b.NVFP4_EALIGN                 # BF16 rows must be 16-byte multiples
     assert g16(c=FAKE + 8) == b.NVFP4_EALIGN
+
+
+def test_gemm_noalloc_argument_errors():
+    def gn(**kw):
+        args = dict(M=256, N=256, K=256, a_codes=FAKE, a_scales=FAKE, a_tensor_scale=FAKE,
+                    b_codes=FAKE, b_scales=FAKE, b_scale_rowdiv=1, b_tensor_scale=FAKE, c=FAKE,
+                    ldc=256, beta=0.0)
+        args.update(kw)
+        return nv.nvfp4_gemm_noalloc(**args, stream=0, raise_on_error=False)
+    assert gn(a_codes=None) == b.NVFP4_EINVAL
+    assert gn(b_tensor_scale=None) == b.NVFP4_EINVAL
+    assert gn(b_scale_rowdiv=8) == b.NVFP4_EINVAL
+    assert gn(beta=2.0) == b.NVFP4_EINVAL
+    assert gn(K=96) == b.NVFP4_ESHAPE
+    assert gn(ldc=128) == b.NVFP4_ESHAPE
+    assert gn(M=1 << 20, K=1 << 13) == b.NVFP4_ESHAPE
+    assert gn(c=FAKE + 4) == b.NVFP4_EALIGN
+    assert gn(ldc=258) == b.NVFP4_EALIGN
+    assert "static" in nv.nvfp4_status_str(b.NVFP4_ESCRATCH)
