@@ -1,42 +1,37 @@
 #!/usr/bin/env python3
-"""Benchmark of the NVFP4 quantize-and-contract step of one linear layer on
-one MI355X.
+"""Benchmark of the NVFP4 quantize-and-contract step on one MI355X.
 
-A step is the whole hot path over one batch of the FFN up-projection layer
-(X bf16 8192x5120, W bf16 20480x5120 ~N(0, 0.02^2), dY bf16 8192x20480
-~N(0, 1e-3^2)): X row-1D RNE together with its random Hadamard + column-1D
-quantization (RNE, the Wgrad operand) in one call; W 16x16 2D quantize (RNE,
-with the transposed copy); Fprop GEMM; dY row-1D SR together with its random
-Hadamard + column-1D SR quantization in one call; Dgrad GEMM with the same
-quantized W; Wgrad GEMM.  Inputs are resident in HBM before the timed region.
+Headline workload: the FFN down-projection stress layer of a 12B-class model,
+X_in bf16 32768x20480, W bf16 5120x20480 ([out x in]), dY bf16 32768x5120, all
+with log-normal magnitudes exp(2z) and random signs.  A step quantizes W once
+(16x16 2D, RNE, with its transposed copy) and then streams four chunks of 8192
+tokens on one HIP stream; per chunk: X row-1D RNE together with its random
+Hadamard + column-1D RNE quantization (one call), Fprop GEMM, dY row-1D SR
+together with its random Hadamard + column-1D SR quantization (one call),
+Dgrad GEMM with the same quantized W, Wgrad GEMM accumulated into one dW
+(beta = 1 after the first chunk).  Inputs are resident in HBM before the
+timed region.
 
-Output: one JSON line.  `value` is the step's GEMM work (3 x 2MNK flops)
+Output: one JSON line.  `value` is the step's GEMM work (12 x 2MNK flops)
 divided by the whole step's wall time, so quantization time counts against
-it; the per-component figures (quantize GB/s, GEMM TFLOP/s and their
-fractions of the MI355X peaks) sit beside it.  `roofline` describes the
-dominant kernel (the GEMM) from HIP events around every GEMM launch in the
-timed steps.  `cpu_baseline` times the CPU oracle on the same step (all 8192
-tokens by default; --cpu-sample-tokens bounds it).
-
-`components.mxfp4` times the comparison format on the same tensors after the
-NVFP4 step (not part of `value`): MXFP4 (32-element blocks, E8M0 scales, no
-tensor scale, no Hadamard) row and column quantization of W, X (RNE) and dY
-(SR), then the same three GEMMs on the block-scaled FP4 matrix instruction.
-`components.linear_module` times the autograd layer (NVFP4Linear forward +
-backward with BF16 outputs) against the same layer kept in BF16, and the
-NVFP4 -> BF16 dequantization of W.  `components.hbm_copy_GBps` is the
-achievable HBM rate measured live (an elementwise kernel reading and writing
-1 GiB each), the reference for the quantize rates beside the 8 TB/s peak.
-`components.quantize_sweep` times the quantize-only workload on its own
-tensors (bf16 8192x5120 and 8192x20480, N(0,1) with 0.1% 100x outliers):
-one row-1D nvfp4_quantize call each (tensor amax pass + cast pass), RNE and
-SR, with the algorithmic bytes of the call (input once, codes, scales).
+it.  `roofline` describes the dominant kernel (the NVFP4 GEMM) from HIP events
+around every GEMM call of the timed steps; its peak is the dense FP16 MFMA
+rate, the matrix-core class the exact NVFP4 GEMM issues (the FP4 fraction is
+in `components`).  `components` holds the quantize rates (HBM GB/s of the
+calls' algorithmic bytes), the GEMM rates against the FP16 and FP4 peaks, the
+FFN up-projection step, the quantize-only sweep timed cold (Infinity Cache
+flushed by a 1 GiB read before each call), the live HBM copy rate, the MXFP4
+comparison step and the autograd layer.  `cpu_baseline` times the CPU oracle
+on the first chunk of the headline step, plus its quantizer single-threaded
+and on all cores and its FP64 contraction.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
+    python bench.py --summarize-trace <rocprofv3 kernel_trace.csv> [--steps K --warmup W]
 """
 from __future__ import annotations
 
 import argparse
+import csv
 import hashlib
 import json
 import os
@@ -51,21 +46,25 @@ sys.path.insert(0, ROOT)
 METRIC = "NVFP4 quantize GB/s (% HBM peak) + NVFP4 GEMM TFLOPS (% MFMA peak), 1 GPU"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_F16_PEAK = 2500.0         # dense FP16 MFMA, TFLOP/s (the class the exact GEMM issues)
-MFMA_FP4_PEAK = 10100.0        # dense FP4 MFMA, TFLOP/s (context)
+MFMA_FP4_PEAK = 10100.0        # dense FP4 MFMA, TFLOP/s
 
-TOKENS, D_IN, D_OUT = 8192, 5120, 20480
+# headline: FFN down-projection stress layer, four chunks of 8192 tokens
+S_TOKENS, S_CHUNK, S_IN, S_OUT = 32768, 8192, 20480, 5120
+S_CHUNKS = S_TOKENS // S_CHUNK
+# FFN up-projection layer (one 8192-token batch)
+U_TOKENS, U_IN, U_OUT = 8192, 5120, 20480
 
-# HBM bytes per k_gemm_nvfp4 launch (mean over the Fprop, Dgrad and Wgrad
-# launches of this workload) from two rocprofv3 --pmc runs of
-#   bench.py --steps 3 --warmup 1 --no-cpu-baseline --copy-probe-mib 1024
-# FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0 (KiB -> bytes): the factors are what the
-# same counters read for the 1 GiB read + 1 GiB write elementwise probe
-# (FETCH_SIZE 512 MiB, WRITE_SIZE 1024 MiB).  Valid only for the kernel
-# sources (gemm.hip + gemm_tiling.hpp) with this hash; any other source
-# reports null.
-GEMM_TRAFFIC = dict(src_sha256="d9aa8b7359bb0f9b8f22da021987d3b8164ca536f12b478f6a465e6b86a25ae1",
-                    bytes_per_launch=1.1573e+09, fetch_bytes=7.0982e+08, write_bytes=4.4747e+08)
+# HBM bytes per k_gemm_nvfp4 launch of the headline step (mean over its
+# Fprop, Dgrad and Wgrad launches), from two rocprofv3 --pmc runs (FETCH_SIZE,
+# then WRITE_SIZE) of `bench.py --headline-only --copy-probe-mib 1024`, each
+# scaled by what the same counter reads for the 1 GiB read + 1 GiB write
+# elementwise probe.  Valid only for the kernel sources with this hash; any
+# other source reports null.
+GEMM_TRAFFIC = None
 GEMM_SOURCES = ("gemm.hip", "gemm_tiling.hpp")
+
+GEMM_KERNEL = "k_gemm_nvfp4<float>"
+REDUCE_KERNEL = "k_gemm_split_reduce<float>"
 
 
 def gemm_src_sha() -> str:
@@ -81,113 +80,53 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--cpu-sample-tokens", type=int, default=8192)
+    p.add_argument("--cpu-sample-tokens", type=int, default=S_CHUNK)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--headline-only", action="store_true",
+                   help="run only the headline step (for profiler runs)")
     p.add_argument("--copy-probe-mib", type=int, default=0,
                    help="also run one plain device copy of this many MiB (calibrates "
                         "the FETCH_SIZE / WRITE_SIZE counters against known bytes)")
+    p.add_argument("--summarize-trace", default=None,
+                   help="summarize a rocprofv3 kernel-trace CSV of a bench run instead of running")
     return p.parse_args()
 
 
-def make_inputs():
+# ----------------------------------------------------------------- inputs
+def stress_inputs():
     from bit_microscaled_quantized_amd import synth
-    d = synth.ffn_up(TOKENS, D_IN, D_OUT)
+    d = synth.ffn_down(S_TOKENS, S_OUT, S_IN)
+    return dict(x=synth.f32_to_bf16_bits(d["x_in"]), w=synth.f32_to_bf16_bits(d["w"]),
+                dy=synth.f32_to_bf16_bits(d["dy"]), sign_mask=d["sign_mask"],
+                seed_base=d["sr_seed_base"])
+
+
+def up_inputs():
+    from bit_microscaled_quantized_amd import synth
+    d = synth.ffn_up(U_TOKENS, U_IN, U_OUT)
     return dict(x=synth.f32_to_bf16_bits(d["x"]), w=synth.f32_to_bf16_bits(d["w"]),
                 dy=synth.f32_to_bf16_bits(d["dy"]), sign_mask=d["sign_mask"],
                 seed_row=d["sr_seed_row"], seed_col=d["sr_seed_col"])
 
 
-def quantize_bytes():
-    """Algorithmic bytes of the three quantize calls of a step: input read once,
-    codes (0.5 B/elem) and scales (1/16 B/elem, 1/256 B/elem for 2D tiles)
-    written; the 2D call also writes its transposed copy, the row + RHT calls
-    write both a row-1D and an RHT column quantization."""
-    T, I, O = TOKENS, D_IN, D_OUT
-    w = O * I * 2 + 2 * (O * I // 2 + O * I // 256)
-    x = T * I * 2 + 2 * (T * I // 2 + T * I // 16)
-    dy = T * O * 2 + 2 * (T * O // 2 + T * O // 16)
-    return dict(w=w, x=x, dy=dy)
+def q2d_bytes(rows, cols):
+    """2D quantize: input read once (bf16), codes + tile scales in both orientations."""
+    n = rows * cols
+    return 2 * n + 2 * (n // 2 + n // 256)
 
 
-def gpu_bench(inp, steps, warmup):
-    import torch
-    import bit_microscaled_quantized_amd as nv
-    from bit_microscaled_quantized_amd.linear import LinearStep
-
-    nv.load_library()  # fails loudly if the HIP library is missing
-    dev = torch.device("cuda", 0)
-    torch.cuda.set_device(dev)
-
-    def up(a):
-        return torch.from_numpy(a.view(np.int16)).to(dev)
-
-    x, w, dy = up(inp["x"]), up(inp["w"]), up(inp["dy"])
-    st = LinearStep(TOKENS, D_IN, D_OUT, device=dev)
-    bf = nv.NVFP4_BF16
-    T, I, O = TOKENS, D_IN, D_OUT
-    mask, s_row, s_col = inp["sign_mask"], inp["seed_row"], inp["seed_col"]
-
-    def ev():
-        return torch.cuda.Event(enable_timing=True)
-
-    def one_step(rec):
-        """One whole step; rec collects (name, start, end) events."""
-        def timed(name, fn):
-            if rec is None:
-                fn()
-                return
-            a, b = ev(), ev()
-            a.record()
-            fn()
-            b.record()
-            rec.append((name, a, b))
-        # X first: its amax pass then follows the previous step's Wgrad GEMM
-        # (non-temporal output) rather than the 2D cast's row-major stores
-        qx, b_ = st.qx, st.qx_t
-        timed("quant_x_row_rht", lambda: nv.nvfp4_quantize_row_rht(
-            x, bf, T, I, I, nv.NVFP4_RNE, 0, qx.codes, qx.scales, qx.ts, qx.amax, mask,
-            nv.NVFP4_RNE, 0, b_.codes, b_.scales, b_.ts, b_.amax))
-        q = st.qw
-        timed("quant_w_2d", lambda: nv.nvfp4_quantize(
-            w, bf, O, I, I, nv.NVFP4_TILE_2D, nv.NVFP4_RNE, 0, q.codes, q.scales, q.codes_t,
-            q.scales_t, q.ts, q.amax))
-        timed("gemm_fprop", lambda: nv.nvfp4_gemm(
-            T, O, I, qx.codes, qx.scales, qx.ts, q.codes, q.scales, 16, q.ts, st.y, O, 0.0, workspace=st.ws))
-        qd, a_ = st.qdy, st.qdy_t
-        timed("quant_dy_row_rht_sr", lambda: nv.nvfp4_quantize_row_rht(
-            dy, bf, T, O, O, nv.NVFP4_SR, s_row, qd.codes, qd.scales, qd.ts, qd.amax, mask,
-            nv.NVFP4_SR, s_col, a_.codes, a_.scales, a_.ts, a_.amax))
-        timed("gemm_dgrad", lambda: nv.nvfp4_gemm(
-            T, I, O, qd.codes, qd.scales, qd.ts, q.codes_t, q.scales_t, 16, q.ts, st.dx, I, 0.0, workspace=st.ws))
-        timed("gemm_wgrad", lambda: nv.nvfp4_gemm(
-            O, I, T, a_.codes, a_.scales, a_.ts, b_.codes, b_.scales, 1, b_.ts, st.dw, I, 0.0, workspace=st.ws))
-
-    for _ in range(warmup):
-        one_step(None)
-    torch.cuda.synchronize()
-
-    # whole-step wall time: K steps between two synchronizations, no events
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        one_step(None)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-
-    # per-call HIP-event durations over another K steps on the same stream
-    rec = []
-    for _ in range(steps):
-        one_step(rec)
-    torch.cuda.synchronize()
-    per = {}
-    for name, a, b in rec:
-        per.setdefault(name, []).append(a.elapsed_time(b))
-    per = {k: float(np.mean(v)) for k, v in per.items()}
-    mx = mx_bench(x, w, dy, s_row, s_col, steps, warmup)
-    mod = module_bench(x, w, dy, st, steps, warmup)
-    return wall / steps, per, mx, mod
+def q_row_rht_bytes(tokens, cols):
+    """Fused row + RHT column quantize: input once, two sets of codes + block scales."""
+    n = tokens * cols
+    return 2 * n + 2 * (n // 2 + n // 16)
 
 
+def q_row_bytes(rows, cols):
+    n = rows * cols
+    return 2 * n + n // 2 + n // 16
+
+
+# ----------------------------------------------------------------- helpers
 def _events_ms(torch, fn, steps, warmup):
     """Mean HIP-event time of fn() on the current stream."""
     for _ in range(warmup):
@@ -202,10 +141,178 @@ def _events_ms(torch, fn, steps, warmup):
     return a.elapsed_time(b) / steps
 
 
-def copy_bench(mib=1024, steps=10, warmup=3):
+class Timer:
+    """Collects (name, start, end) HIP events around calls on the current stream."""
+
+    def __init__(self, torch, on: bool):
+        self.torch, self.on, self.rec = torch, on, []
+
+    def __call__(self, name, fn):
+        if not self.on:
+            fn()
+            return
+        a = self.torch.cuda.Event(enable_timing=True)
+        b = self.torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        self.rec.append((name, a, b))
+
+    def means(self):
+        per = {}
+        for name, a, b in self.rec:
+            per.setdefault(name, []).append(a.elapsed_time(b))
+        return {k: float(np.mean(v)) for k, v in per.items()}, per
+
+
+def run_steps(torch, step, steps, warmup):
+    """Warmup, then K steps between two synchronizations (wall time), then K
+    more with HIP events around every call.  Returns (ms per step, per-call
+    mean ms, per-call lists)."""
+    off = Timer(torch, False)
+    for _ in range(warmup):
+        step(off)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step(off)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    tm = Timer(torch, True)
+    for _ in range(steps):
+        step(tm)
+    torch.cuda.synchronize()
+    per, lists = tm.means()
+    return wall * 1e3, per, lists
+
+
+# ----------------------------------------------------------------- headline
+def stress_bench(torch, nv, inp, steps, warmup):
+    """The headline step; returns its figures and the device tensors."""
+    from bit_microscaled_quantized_amd.linear import LinearStep
+    dev = torch.device("cuda", 0)
+
+    def up(a):
+        return torch.from_numpy(a.view(np.int16)).to(dev)
+
+    x, w, dy = up(inp["x"]), up(inp["w"]), up(inp["dy"])
+    T, I, O = S_CHUNK, S_IN, S_OUT
+    st = LinearStep(T, I, O, device=dev)
+    bf, RNE, SR = nv.NVFP4_BF16, nv.NVFP4_RNE, nv.NVFP4_SR
+    mask, base = inp["sign_mask"], inp["seed_base"]
+    qw, qx, qxt, qd, qdt = st.qw, st.qx, st.qx_t, st.qdy, st.qdy_t
+    xs = [x[c * T:(c + 1) * T] for c in range(S_CHUNKS)]
+    dys = [dy[c * T:(c + 1) * T] for c in range(S_CHUNKS)]
+
+    def step(tm):
+        tm("quant_w_2d", lambda: nv.nvfp4_quantize(
+            w, bf, O, I, I, nv.NVFP4_TILE_2D, RNE, 0, qw.codes, qw.scales, qw.codes_t, qw.scales_t,
+            qw.ts, qw.amax))
+        for c in range(S_CHUNKS):
+            xc, dc = xs[c], dys[c]
+            tm("quant_x_row_rht", lambda: nv.nvfp4_quantize_row_rht(
+                xc, bf, T, I, I, RNE, 0, qx.codes, qx.scales, qx.ts, qx.amax, mask,
+                RNE, 0, qxt.codes, qxt.scales, qxt.ts, qxt.amax))
+            tm("gemm_fprop", lambda: nv.nvfp4_gemm(
+                T, O, I, qx.codes, qx.scales, qx.ts, qw.codes, qw.scales, 16, qw.ts, st.y, O, 0.0,
+                workspace=st.ws))
+            s_row, s_col = base + 2 * c, base + 2 * c + 1
+            tm("quant_dy_row_rht_sr", lambda: nv.nvfp4_quantize_row_rht(
+                dc, bf, T, O, O, SR, s_row, qd.codes, qd.scales, qd.ts, qd.amax, mask,
+                SR, s_col, qdt.codes, qdt.scales, qdt.ts, qdt.amax))
+            tm("gemm_dgrad", lambda: nv.nvfp4_gemm(
+                T, I, O, qd.codes, qd.scales, qd.ts, qw.codes_t, qw.scales_t, 16, qw.ts, st.dx, I,
+                0.0, workspace=st.ws))
+            beta = 1.0 if c > 0 else 0.0
+            tm("gemm_wgrad", lambda: nv.nvfp4_gemm(
+                O, I, T, qdt.codes, qdt.scales, qdt.ts, qxt.codes, qxt.scales, 1, qxt.ts, st.dw, I,
+                beta, workspace=st.ws))
+
+    ms_step, per, lists = run_steps(torch, step, steps, warmup)
+    gemm_calls = lists["gemm_fprop"] + lists["gemm_dgrad"] + lists["gemm_wgrad"]
+    flops = 2.0 * T * I * O
+    q_ms = per["quant_w_2d"] + S_CHUNKS * (per["quant_x_row_rht"] + per["quant_dy_row_rht_sr"])
+    q_bytes = q2d_bytes(O, I) + S_CHUNKS * (q_row_rht_bytes(T, I) + q_row_rht_bytes(T, O))
+    out = dict(ms_step=ms_step, per=per, gemm_ms=float(np.mean(gemm_calls)), gemm_flops=flops,
+               gemm_launches=len(gemm_calls), q_ms=q_ms, q_bytes=q_bytes,
+               q_bytes_by_call={"quant_w_2d": q2d_bytes(O, I),
+                                "quant_x_row_rht": q_row_rht_bytes(T, I),
+                                "quant_dy_row_rht_sr": q_row_rht_bytes(T, O)})
+    del x, w, dy, st, xs, dys
+    torch.cuda.empty_cache()
+    return out
+
+
+# ----------------------------------------------------------------- FFN up
+def up_bench(torch, nv, inp, steps, warmup):
+    """The FFN up-projection layer's step (one 8192-token batch, W quantized
+    every step), as in the headline but with one chunk."""
+    from bit_microscaled_quantized_amd.linear import LinearStep
+    dev = torch.device("cuda", 0)
+
+    def up(a):
+        return torch.from_numpy(a.view(np.int16)).to(dev)
+
+    x, w, dy = up(inp["x"]), up(inp["w"]), up(inp["dy"])
+    T, I, O = U_TOKENS, U_IN, U_OUT
+    st = LinearStep(T, I, O, device=dev)
+    bf, RNE, SR = nv.NVFP4_BF16, nv.NVFP4_RNE, nv.NVFP4_SR
+    mask, s_row, s_col = inp["sign_mask"], inp["seed_row"], inp["seed_col"]
+    qw, qx, qxt, qd, qdt = st.qw, st.qx, st.qx_t, st.qdy, st.qdy_t
+
+    def step(tm):
+        tm("quant_x_row_rht", lambda: nv.nvfp4_quantize_row_rht(
+            x, bf, T, I, I, RNE, 0, qx.codes, qx.scales, qx.ts, qx.amax, mask,
+            RNE, 0, qxt.codes, qxt.scales, qxt.ts, qxt.amax))
+        tm("quant_w_2d", lambda: nv.nvfp4_quantize(
+            w, bf, O, I, I, nv.NVFP4_TILE_2D, RNE, 0, qw.codes, qw.scales, qw.codes_t, qw.scales_t,
+            qw.ts, qw.amax))
+        tm("gemm_fprop", lambda: nv.nvfp4_gemm(
+            T, O, I, qx.codes, qx.scales, qx.ts, qw.codes, qw.scales, 16, qw.ts, st.y, O, 0.0,
+            workspace=st.ws))
+        tm("quant_dy_row_rht_sr", lambda: nv.nvfp4_quantize_row_rht(
+            dy, bf, T, O, O, SR, s_row, qd.codes, qd.scales, qd.ts, qd.amax, mask,
+            SR, s_col, qdt.codes, qdt.scales, qdt.ts, qdt.amax))
+        tm("gemm_dgrad", lambda: nv.nvfp4_gemm(
+            T, I, O, qd.codes, qd.scales, qd.ts, qw.codes_t, qw.scales_t, 16, qw.ts, st.dx, I, 0.0,
+            workspace=st.ws))
+        tm("gemm_wgrad", lambda: nv.nvfp4_gemm(
+            O, I, T, qdt.codes, qdt.scales, qdt.ts, qxt.codes, qxt.scales, 1, qxt.ts, st.dw, I, 0.0,
+            workspace=st.ws))
+
+    ms_step, per, _ = run_steps(torch, step, steps, warmup)
+    flops = 2.0 * T * I * O
+    gemm_ms = float(np.mean([per["gemm_fprop"], per["gemm_dgrad"], per["gemm_wgrad"]]))
+    qb = {"quant_x_row_rht": q_row_rht_bytes(T, I), "quant_w_2d": q2d_bytes(O, I),
+          "quant_dy_row_rht_sr": q_row_rht_bytes(T, O)}
+    q_ms = sum(per[k] for k in qb)
+    q_gbs = sum(qb.values()) / (q_ms * 1e-3) / 1e9
+    gt = flops / (gemm_ms * 1e-3) / 1e12
+    mx = mx_bench(torch, nv, x, w, dy, s_row, s_col, steps, warmup)
+    mod = module_bench(torch, nv, x, w, dy, st, steps, warmup)
+    out = {
+        "workload": "ffn_up_fwd_bwd: X bf16 8192x5120 N(0,1), W bf16 20480x5120 N(0,0.02^2), "
+                    "dY bf16 8192x20480 N(0,1e-3^2); same calls as the headline, one chunk, "
+                    "W quantized every step",
+        "ms_per_step": round(ms_step, 4),
+        "TFLOPs": round(3 * flops / (ms_step * 1e-3) / 1e12, 2),
+        "quantize_GBps": round(q_gbs, 1),
+        "quantize_frac_hbm": round(q_gbs / HBM_PEAK_GBS, 4),
+        "gemm_TFLOPs": round(gt, 2),
+        "gemm_frac_mfma_f16": round(gt / MFMA_F16_PEAK, 4),
+        "per_call_ms": {k: round(v, 4) for k, v in per.items()},
+        "quantize_bytes": qb,
+        "mxfp4": mx,
+        "linear_module": mod,
+    }
+    del x, w, dy, st
+    torch.cuda.empty_cache()
+    return out
+
+
+def copy_bench(torch, mib=1024, steps=10, warmup=3):
     """Achievable HBM rate on this GPU: an elementwise kernel (torch.neg) that
     reads and writes `mib` MiB each, read + write bytes per second (GB/s)."""
-    import torch
     n = (mib << 20) // 4
     src = torch.ones(n, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
@@ -215,14 +322,13 @@ def copy_bench(mib=1024, steps=10, warmup=3):
     return 2.0 * (mib << 20) / (ms * 1e-3) / 1e9
 
 
-def module_bench(x, w, dy, st, steps, warmup):
-    """The autograd layer on the same tensors: NVFP4Linear forward + backward
-    (quantize, Fprop, Dgrad, Wgrad, BF16 outputs) against the same layer kept
-    in BF16 (torch's BF16 matmul); and NVFP4 -> BF16 dequantization of W."""
-    import torch
-    import bit_microscaled_quantized_amd as nv
+def module_bench(torch, nv, x, w, dy, st, steps, warmup):
+    """The autograd layer on the FFN up-projection tensors: NVFP4Linear forward
+    + backward (quantize, Fprop, Dgrad, Wgrad, BF16 outputs) against the same
+    layer kept in BF16 (torch's BF16 matmul); and NVFP4 -> BF16 dequantization
+    of W."""
     from bit_microscaled_quantized_amd.module import NVFP4Linear
-    T, I, O = TOKENS, D_IN, D_OUT
+    T, I, O = U_TOKENS, U_IN, U_OUT
     xb = x.view(torch.bfloat16)
     dyb = dy.view(torch.bfloat16)
     out = {}
@@ -239,7 +345,7 @@ def module_bench(x, w, dy, st, steps, warmup):
         ms = _events_ms(torch, fwd_bwd, steps, warmup)
         out[f"{name}_fwd_bwd_ms"] = round(ms, 4)
         out[f"{name}_TFLOPs"] = round(3 * 2.0 * T * I * O / (ms * 1e-3) / 1e12, 2)
-    q = st.qw  # W quantized by the NVFP4 step above
+    q = st.qw  # W quantized by the step above
     wd = torch.empty((O, I), dtype=torch.bfloat16, device=x.device)
     ms = _events_ms(torch, lambda: nv.nvfp4_dequantize(q.codes, q.scales, 16, q.ts, O, I, nv.NVFP4_BF16,
                                                        wd, I), steps, warmup)
@@ -250,25 +356,12 @@ def module_bench(x, w, dy, st, steps, warmup):
     return out
 
 
-def mx_quantize_bytes():
-    """Algorithmic bytes of each MXFP4 quantize call of the comparison step:
-    bf16 input read once, codes (0.5 B/elem) and E8M0 scales (1/32 B/elem)
-    written."""
-    def one(n):
-        return n * 2 + n // 2 + n // 32
-    T, I, O = TOKENS, D_IN, D_OUT
-    return dict(w_row=one(O * I), w_col=one(O * I), x_row=one(T * I), x_col=one(T * I),
-                dy_row_sr=one(T * O), dy_col_sr=one(T * O))
-
-
-def mx_bench(x, w, dy, s_row, s_col, steps, warmup):
-    """The MXFP4 comparison step on the same device tensors: each of the six
-    quantize calls and three GEMMs timed with HIP events on the current
-    stream, averaged over `steps` steps after `warmup` untimed ones."""
-    import torch
-    import bit_microscaled_quantized_amd as nv
+def mx_bench(torch, nv, x, w, dy, s_row, s_col, steps, warmup):
+    """The MXFP4 comparison step on the FFN up-projection tensors: each of the
+    six quantize calls (bf16 in, codes + E8M0 scales out) and three GEMMs timed
+    with HIP events on the current stream."""
     dev = x.device
-    T, I, O = TOKENS, D_IN, D_OUT
+    T, I, O = U_TOKENS, U_IN, U_OUT
     bf = nv.NVFP4_BF16
     u8 = dict(dtype=torch.uint8, device=dev)
 
@@ -294,24 +387,16 @@ def mx_bench(x, w, dy, s_row, s_col, steps, warmup):
         ("gemm_dgrad", lambda: nv.mxfp4_gemm(T, I, O, *d_r, *w_c, dx, I, 0.0, workspace=ws)),
         ("gemm_wgrad", lambda: nv.mxfp4_gemm(O, I, T, *d_c, *x_c, dw, I, 0.0, workspace=ws)),
     ]
-    for _ in range(warmup):
-        for _, fn in calls:
-            fn()
-    torch.cuda.synchronize()
-    rec = []
-    for _ in range(steps):
+
+    def step(tm):
         for name, fn in calls:
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
-            fn()
-            b.record()
-            rec.append((name, a, b))
-    torch.cuda.synchronize()
-    per = {}
-    for name, a, b in rec:
-        per.setdefault(name, []).append(a.elapsed_time(b))
-    per = {k: float(np.mean(v)) for k, v in per.items()}
-    qb = mx_quantize_bytes()
+            tm(name, fn)
+    _, per, _ = run_steps(torch, step, steps, warmup)
+
+    def one(n):
+        return n * 2 + n // 2 + n // 32
+    qb = dict(w_row=one(O * I), w_col=one(O * I), x_row=one(T * I), x_col=one(T * I),
+              dy_row_sr=one(T * O), dy_col_sr=one(T * O))
     q_ms = sum(per[k] for k in qb)
     g_ms = float(np.mean([per["gemm_fprop"], per["gemm_dgrad"], per["gemm_wgrad"]]))
     g_tf = 2.0 * T * I * O / (g_ms * 1e-3) / 1e12
@@ -327,17 +412,20 @@ def mx_bench(x, w, dy, s_row, s_col, steps, warmup):
     }
 
 
-def sweep_bench(steps, warmup):
-    """The quantize-only workload: each bf16 tensor quantized row-1D by one
-    nvfp4_quantize call (zero amax, tensor amax pass, cast pass), RNE and SR,
-    mean HIP-event time per call on the current stream.  GB/s counts the
-    call's algorithmic bytes: the input read once (2 B/elem), codes
-    (0.5 B/elem) and E4M3 scales (1/16 B/elem)."""
-    import torch
-    import bit_microscaled_quantized_amd as nv
+# ----------------------------------------------------------------- quantize-only sweep
+def sweep_bench(torch, nv, steps):
+    """The quantize-only workload, each call timed cold: bf16 tensors 8192x5120
+    and 8192x20480 (N(0,1) with 0.1% 100x outliers), row-1D, RNE and SR, one
+    nvfp4_quantize call each.  Before every timed call a 1 GiB read (outside
+    the events) evicts the tensor from the 256 MB Infinity Cache.  GB/s counts
+    the call's algorithmic bytes: input read once (2 B/elem), codes
+    (0.5 B/elem) and E4M3 scales (1/16 B/elem); the median over the calls is
+    reported."""
     from bit_microscaled_quantized_amd import synth
     dev = torch.device("cuda", 0)
     u8 = dict(dtype=torch.uint8, device=dev)
+    flush = torch.ones((1 << 30) // 4, dtype=torch.float32, device=dev)
+    sink = torch.empty((), dtype=torch.float32, device=dev)
     out = {}
     for which in (0, 1):
         xb = synth.f32_to_bf16_bits(synth.quantize_sweep(which))
@@ -346,11 +434,23 @@ def sweep_bench(steps, warmup):
         codes, scales = torch.empty((R, C // 2), **u8), torch.empty((R, C // 16), **u8)
         ts = torch.empty(1, dtype=torch.float32, device=dev)
         am = torch.empty(1, dtype=torch.float32, device=dev)
-        nbytes = R * C * 2 + R * C // 2 + R * C // 16
+        nbytes = q_row_bytes(R, C)
         for rname, rnd, seed in (("rne", nv.NVFP4_RNE, 0), ("sr", nv.NVFP4_SR, 3)):
-            ms = _events_ms(torch, lambda: nv.nvfp4_quantize(
-                x, nv.NVFP4_BF16, R, C, C, nv.NVFP4_ROW_1D, rnd, seed, codes, scales, None, None,
-                ts, am), steps, warmup)
+            def call():
+                nv.nvfp4_quantize(x, nv.NVFP4_BF16, R, C, C, nv.NVFP4_ROW_1D, rnd, seed, codes,
+                                  scales, None, None, ts, am)
+            for _ in range(3):
+                call()
+            times = []
+            for _ in range(max(steps, 5)):
+                torch.amax(flush, dim=0, out=sink)  # a 1 GiB read evicts the Infinity Cache
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                call()
+                b.record()
+                torch.cuda.synchronize()
+                times.append(a.elapsed_time(b))
+            ms = float(np.median(times))
             gbs = nbytes / (ms * 1e-3) / 1e9
             out[f"{R}x{C}_{rname}"] = dict(ms=round(ms, 4), GBps=round(gbs, 1),
                                           frac_hbm=round(gbs / HBM_PEAK_GBS, 4), bytes=nbytes)
@@ -360,52 +460,147 @@ def sweep_bench(steps, warmup):
     tot_ms = sum(v["ms"] for v in out.values())
     out["all"] = dict(GBps=round(tot_b / (tot_ms * 1e-3) / 1e9, 1),
                       frac_hbm=round(tot_b / (tot_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4))
+    out["timing"] = "cold: a 1 GiB read before each call, median of the calls"
+    del flush
+    torch.cuda.empty_cache()
     return out
 
 
+# ----------------------------------------------------------------- CPU baseline
 def cpu_baseline(inp, tokens):
-    """The oracle, as it stands, on the same step restricted to the first
-    `tokens` tokens (full weight): five quantizations plus the three FP64
-    contractions of its dequantized operands."""
+    """The oracle, as it stands, on the first `tokens` tokens of the headline
+    step (its first chunk) with the full weight: W 2D, X row + RHT, dY row SR +
+    RHT SR quantization in C (OpenMP over blocks, all host threads) and the
+    three FP64 contractions of the dequantized operands (numpy BLAS).  Also the
+    oracle's row-1D quantizer alone on one thread and on all threads, and one
+    FP64 contraction, each with its thread count."""
     import oracle as ora
     from threadpoolctl import threadpool_info
     x, w, dy = inp["x"][:tokens], inp["w"], inp["dy"][:tokens]
-    mask, s_row, s_col = inp["sign_mask"], inp["seed_row"], inp["seed_col"]
+    mask, base = inp["sign_mask"], inp["seed_base"]
+    threads = ora.num_threads()
     t0 = time.perf_counter()
     qw = ora.quantize(w, ora.TILE_2D, ora.RNE)
     qx = ora.quantize(x, ora.ROW_1D, ora.RNE)
-    y = ora.gemm_f64(ora.dequant(qx["codes"], qx["scales"], qx["tensor_scale"]),
-                     ora.dequant(qw["codes"], qw["scales"], qw["tensor_scale"], 16))
-    qd = ora.quantize(dy, ora.ROW_1D, ora.SR, s_row)
+    qxt = ora.rht_quantize(x, mask, ora.RNE)
+    dqx = ora.dequant(qx["codes"], qx["scales"], qx["tensor_scale"])
+    dqw = ora.dequant(qw["codes"], qw["scales"], qw["tensor_scale"], 16)
+    tq = time.perf_counter()
+    y = ora.gemm_f64(dqx, dqw)
+    tg = time.perf_counter() - tq
+    del dqx, dqw
+    qd = ora.quantize(dy, ora.ROW_1D, ora.SR, base)
+    qdt = ora.rht_quantize(dy, mask, ora.SR, base + 1)
     dx = ora.gemm_f64(ora.dequant(qd["codes"], qd["scales"], qd["tensor_scale"]),
                       ora.dequant(qw["codes_t"], qw["scales_t"], qw["tensor_scale"], 16))
-    qdt = ora.rht_quantize(dy, mask, ora.SR, s_col)
-    qxt = ora.rht_quantize(x, mask, ora.RNE)
     dw = ora.gemm_f64(ora.dequant(qdt["codes"], qdt["scales"], qdt["tensor_scale"]),
                       ora.dequant(qxt["codes"], qxt["scales"], qxt["tensor_scale"]))
     dt = time.perf_counter() - t0
     del y, dx, dw
-    flops = 3 * 2.0 * tokens * D_IN * D_OUT
+    flops = 3 * 2.0 * tokens * S_IN * S_OUT
     blas = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
-    return dict(value=flops / dt / 1e12, unit="TFLOP/s", cores=max(ora.num_threads(), blas),
-                kind="oracle", seconds=dt,
-                sample=f"same step on the first {tokens} of {TOKENS} tokens with the full "
-                       f"{D_OUT}x{D_IN} weight: W 2D, X row, dY row SR, RHT(dY) SR, RHT(X) "
-                       f"quantization in the C oracle (OpenMP) + 3 FP64 BLAS contractions")
+
+    # the row-1D quantizer alone (RNE, bf16), all threads, then one thread on a
+    # sixteenth of the rows
+    xs = inp["x"][:tokens]
+    nb = q_row_bytes(*xs.shape)
+    t1 = time.perf_counter()
+    ora.quantize(xs, ora.ROW_1D, ora.RNE)
+    q_all = nb / (time.perf_counter() - t1) / 1e9
+    ora.set_num_threads(1)
+    xs1 = xs[: tokens // 16]
+    t1 = time.perf_counter()
+    ora.quantize(xs1, ora.ROW_1D, ora.RNE)
+    q_one = q_row_bytes(*xs1.shape) / (time.perf_counter() - t1) / 1e9
+    ora.set_num_threads(threads)
+    return dict(value=flops / dt / 1e12, unit="TFLOP/s", cores=max(threads, blas), kind="oracle",
+                seconds=round(dt, 3),
+                sample=f"the headline step's first chunk ({tokens} of {S_TOKENS} tokens) with the full "
+                       f"{S_OUT}x{S_IN} weight: W 2D, X row + RHT, dY row SR + RHT SR quantization in "
+                       f"the C oracle (OpenMP, {threads} threads) + 3 FP64 BLAS contractions "
+                       f"({blas} threads); value = that chunk's 3 x 2MNK flops / its wall time",
+                quantize_row_GBps_all_threads=round(q_all, 3), quantize_threads=threads,
+                quantize_row_GBps_one_thread=round(q_one, 3),
+                gemm_f64_GFLOPs=round(2.0 * tokens * S_IN * S_OUT / tg / 1e9, 1), gemm_threads=blas)
 
 
+# ----------------------------------------------------------------- trace summary
+def _kernel_short(name: str) -> str:
+    s = name.replace("(anonymous namespace)::", "").split("(")[0]
+    return s.replace("void ", "").replace("nvfp4::", "").strip()
+
+
+def summarize_trace(path, steps, warmup):
+    """Markdown summary of a rocprofv3 kernel-trace CSV of `bench.py` with the
+    same --steps / --warmup: per-kernel statistics over the whole run, and the
+    NVFP4 GEMM launches of the headline's timed steps (the first `warmup`
+    steps' launches skipped, the next 2 x `steps` steps' taken: wall-timed
+    and event-timed), each with the split-tail reduction that follows it."""
+    rows = []
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            rows.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]),
+                         _kernel_short(r["Kernel_Name"])))
+    rows.sort()
+    stats = {}
+    for s, e, k in rows:
+        stats.setdefault(k, []).append((e - s) / 1e3)
+    print("| kernel | calls | mean µs | median µs | total ms |")
+    print("|---|---:|---:|---:|---:|")
+    for k, v in sorted(stats.items(), key=lambda kv: -sum(kv[1])):
+        print(f"| `{k}` | {len(v)} | {np.mean(v):.1f} | {np.median(v):.1f} | {sum(v) / 1e3:.3f} |")
+    per_step = 3 * S_CHUNKS
+    gem = [(i, s, e) for i, (s, e, k) in enumerate(rows) if k == GEMM_KERNEL]
+    first, n = warmup * per_step, 2 * steps * per_step
+    timed = gem[first:first + n]
+    if len(timed) < n:
+        print(f"\nonly {len(timed)} of {n} headline GEMM launches found")
+        return
+    dur, call = [], []
+    for i, s, e in timed:
+        d = (e - s) / 1e3
+        extra = 0.0
+        j = i + 1
+        if j < len(rows) and rows[j][2] == REDUCE_KERNEL:
+            extra = (rows[j][1] - rows[j][0]) / 1e3
+        dur.append(d)
+        call.append(d + extra)
+    flops = 2.0 * S_CHUNK * S_IN * S_OUT
+    km, cm = float(np.mean(dur)), float(np.mean(call))
+    print(f"\nheadline timed-region `{GEMM_KERNEL}` launches: {len(dur)}")
+    print(f"- kernel alone: mean {km:.1f} µs -> {flops / km / 1e6:.1f} TFLOP/s = "
+          f"{flops / km / 1e6 / MFMA_F16_PEAK:.4f} of the FP16 MFMA peak")
+    print(f"- kernel + its split-tail reduction (what one nvfp4_gemm call takes): mean {cm:.1f} µs "
+          f"-> {flops / cm / 1e6:.1f} TFLOP/s = {flops / cm / 1e6 / MFMA_F16_PEAK:.4f}")
+    for name, sl in (("Fprop", slice(0, None, 3)), ("Dgrad", slice(1, None, 3)),
+                     ("Wgrad", slice(2, None, 3))):
+        d = dur[sl]
+        print(f"- {name}: {len(d)} launches, mean {np.mean(d):.1f} µs, median {np.median(d):.1f} µs")
+
+
+# ----------------------------------------------------------------- main
 def main():
     args = parse()
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace, args.steps, args.warmup)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the sharded path is a design, not built)", file=sys.stderr)
         sys.exit(2)
-    inp = make_inputs()
-    ms_step, per, mx, mod = gpu_bench(inp, args.steps, args.warmup)
-    copy_gbs = copy_bench()
-    sweep = sweep_bench(args.steps, args.warmup)
+    import torch
+    import bit_microscaled_quantized_amd as nv
+    nv.load_library()  # fails loudly if the HIP library is missing
+    torch.cuda.set_device(0)
+
+    inp = stress_inputs()
+    head = stress_bench(torch, nv, inp, args.steps, args.warmup)
+    comps = {}
+    if not args.headline_only:
+        comps["ffn_up"] = up_bench(torch, nv, up_inputs(), args.steps, args.warmup)
+        comps["quantize_sweep"] = sweep_bench(torch, nv, args.steps)
+        comps["hbm_copy_GBps"] = round(copy_bench(torch), 1)
     if args.copy_probe_mib:
-        import torch
         # an elementwise kernel (not a DMA copy, which no counter sees) that
         # reads and writes exactly n bytes
         n = args.copy_probe_mib << 20
@@ -415,21 +610,30 @@ def main():
         torch.neg(src, out=dst)
         torch.cuda.synchronize()
         del src, dst
-    ms_step *= 1e3
 
-    gemm_flops = 2.0 * TOKENS * D_IN * D_OUT  # each of the three GEMMs
-    gemm_ms = np.mean([per["gemm_fprop"], per["gemm_dgrad"], per["gemm_wgrad"]])
-    gemm_tflops = gemm_flops / (gemm_ms * 1e-3) / 1e12
-    qb = quantize_bytes()
-    qnames = dict(w="quant_w_2d", x="quant_x_row_rht", dy="quant_dy_row_rht_sr")
-    q_ms = sum(per[qnames[k]] for k in qb)
-    q_gbs = sum(qb.values()) / (q_ms * 1e-3) / 1e9
-    value = 3 * gemm_flops / (ms_step * 1e-3) / 1e12
-
+    flops = head["gemm_flops"]
+    ms_step = head["ms_step"]
+    gemm_ms = head["gemm_ms"]
+    gemm_tflops = flops / (gemm_ms * 1e-3) / 1e12
+    q_gbs = head["q_bytes"] / (head["q_ms"] * 1e-3) / 1e9
+    value = 3 * S_CHUNKS * flops / (ms_step * 1e-3) / 1e12
     traffic = None
     if GEMM_TRAFFIC is not None and GEMM_TRAFFIC["src_sha256"] == gemm_src_sha():
         traffic = GEMM_TRAFFIC["bytes_per_launch"]
-
+    per = head["per"]
+    comps.update({
+        "quantize_GBps": round(q_gbs, 1),
+        "quantize_frac_hbm": round(q_gbs / HBM_PEAK_GBS, 4),
+        "quantize_bytes_per_call": head["q_bytes_by_call"],
+        "quantize_GBps_per_call": {k: round(b / (per[k] * 1e-3) / 1e9, 1)
+                                   for k, b in head["q_bytes_by_call"].items()},
+        "gemm_TFLOPs": round(gemm_tflops, 2),
+        "gemm_frac_mfma_f16": round(gemm_tflops / MFMA_F16_PEAK, 4),
+        "gemm_frac_mfma_fp4": round(gemm_tflops / MFMA_FP4_PEAK, 4),
+        "per_call_ms": {k: round(v, 4) for k, v in per.items()},
+    })
+    if "hbm_copy_GBps" in comps:
+        comps["quantize_frac_of_copy"] = round(q_gbs / comps["hbm_copy_GBps"], 4)
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -444,38 +648,30 @@ def main():
         "dtype": "f16",
         "data": "synthetic",
         "config": {
-            "workload": "ffn_up_fwd_bwd: X bf16 8192x5120 N(0,1), W bf16 20480x5120 N(0,0.02^2), "
-                        "dY bf16 8192x20480 N(0,1e-3^2); W 2D RNE (+transposed), X row RNE, "
-                        "dY row SR, RHT+col (dY SR, X RNE); Fprop, Dgrad, Wgrad NVFP4 GEMMs",
-            "tokens": TOKENS, "d_in": D_IN, "d_out": D_OUT,
+            "workload": "ffn_down_stress: X_in bf16 32768x20480, W bf16 5120x20480 [out x in], "
+                        "dY bf16 32768x5120, log-normal |v| = exp(2z) with random signs; W 2D RNE "
+                        "(+transposed) once; 4 chunks of 8192 tokens on one stream, each: X row RNE "
+                        "+ RHT col RNE, Fprop, dY row SR + RHT col SR, Dgrad, Wgrad (beta = 1 after "
+                        "the first chunk)",
+            "tokens": S_TOKENS, "chunk_tokens": S_CHUNK, "d_in": S_IN, "d_out": S_OUT,
         },
         "roofline": {
             "kernel": "k_gemm_nvfp4",
             "bound": "mfma",
             "achieved": round(gemm_tflops, 2),
             "peak": MFMA_F16_PEAK,
+            "peak_kind": "dense FP16 MFMA: the exact NVFP4 GEMM dequantizes to FP16 and issues "
+                         "FP16 MFMAs; the FP4-peak fraction is components.gemm_frac_mfma_fp4",
             "unit": "TFLOP/s",
             "frac": round(gemm_tflops / MFMA_F16_PEAK, 4),
             "traffic": traffic,
-            "avg_launch_ms": round(float(gemm_ms), 4),
-            "flops_per_launch": gemm_flops,
+            "avg_launch_ms": round(gemm_ms, 4),
+            "launches": head["gemm_launches"],
+            "flops_per_launch": flops,
         },
-        "components": {
-            "quantize_GBps": round(q_gbs, 1),
-            "quantize_frac_hbm": round(q_gbs / HBM_PEAK_GBS, 4),
-            "hbm_copy_GBps": round(copy_gbs, 1),
-            "quantize_frac_of_copy": round(q_gbs / copy_gbs, 4),
-            "quantize_sweep": sweep,
-            "gemm_TFLOPs": round(gemm_tflops, 2),
-            "gemm_frac_mfma_f16": round(gemm_tflops / MFMA_F16_PEAK, 4),
-            "gemm_frac_mfma_fp4": round(gemm_tflops / MFMA_FP4_PEAK, 4),
-            "per_call_ms": {k: round(v, 4) for k, v in per.items()},
-            "quantize_bytes": qb,
-            "mxfp4": mx,
-            "linear_module": mod,
-        },
+        "components": comps,
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not args.headline_only:
         out["cpu_baseline"] = cpu_baseline(inp, args.cpu_sample_tokens)
     print(json.dumps(out), flush=True)
 

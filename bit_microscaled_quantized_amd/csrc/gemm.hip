@@ -348,22 +348,36 @@ __global__ __launch_bounds__(512, 1) void k_gemm_nvfp4(
     return;
   }
   const float alpha = a_ts[0] * b_ts[0];
+  // The wave tile is written one 32 x 32 MFMA tile t = 2i + j at a time.  With
+  // beta = 1 the 16 old values a lane needs from tile t + 1 are loaded
+  // together while tile t is stored: the compiler cannot tell the loads from
+  // the stores apart (both go through c), so a load placed after a store would
+  // wait for it, one round trip per element.
+  float old[2][16];
+  auto load_old = [&](int t, float* o) {
+    const int n = n0 + wn * 64 + (t & 1) * 32 + lr;
 #pragma unroll
-  for (int i = 0; i < 4; i++)
+    for (int r = 0; r < 16; r++) {
+      const int m = m0 + wm * 128 + (t >> 1) * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+      o[r] = (m < M && n < N) ? OutElem<OutT>::load_nt(c + (int64_t)m * ldc + n) : 0.0f;
+    }
+  };
+  if (accumulate) load_old(0, old[0]);
 #pragma unroll
-    for (int j = 0; j < 2; j++) {
-      const int n = n0 + wn * 64 + j * 32 + lr;
+  for (int t = 0; t < 8; t++) {
+    if (accumulate && t + 1 < 8) load_old(t + 1, old[(t + 1) & 1]);
+    const int i = t >> 1, j = t & 1;
+    const int n = n0 + wn * 64 + j * 32 + lr;
 #pragma unroll
-      for (int r = 0; r < 16; r++) {
-        const int m = m0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-        if (m < M && n < N) {
-          OutT* p = c + (int64_t)m * ldc + n;
-          float v = alpha * acc[i][j][r];
-          if (accumulate) v += OutElem<OutT>::load(p);
-          OutElem<OutT>::store_nt(p, v);
-        }
+    for (int r = 0; r < 16; r++) {
+      const int m = m0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+      if (m < M && n < N) {
+        float v = alpha * acc[i][j][r];
+        if (accumulate) v += old[t & 1][r];
+        OutElem<OutT>::store_nt(c + (int64_t)m * ldc + n, v);
       }
     }
+  }
 }
 
 // Sum of the S partial tiles of each split tail tile in the order 0 .. S-1,

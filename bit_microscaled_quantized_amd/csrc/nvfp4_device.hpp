@@ -256,11 +256,15 @@ struct OutElem;
 template <>
 struct OutElem<float> {
   static __device__ __forceinline__ float load(const float* p) { return *p; }
+  static __device__ __forceinline__ float load_nt(const float* p) { return __builtin_nontemporal_load(p); }
   static __device__ __forceinline__ void store_nt(float* p, float v) { __builtin_nontemporal_store(v, p); }
 };
 template <>
 struct OutElem<uint16_t> {
   static __device__ __forceinline__ float load(const uint16_t* p) { return __uint_as_float((uint32_t)*p << 16); }
+  static __device__ __forceinline__ float load_nt(const uint16_t* p) {
+    return __uint_as_float((uint32_t)__builtin_nontemporal_load(p) << 16);
+  }
   static __device__ __forceinline__ void store_nt(uint16_t* p, float v) {
     __builtin_nontemporal_store((uint16_t)bf16_rne(v), p);
   }

@@ -12,14 +12,43 @@ log-normal magnitudes exp(2z) with random signs (stress case).
 """
 from __future__ import annotations
 
+import concurrent.futures
+import os
+
 import numpy as np
+
+_ROWS_PER_CHUNK = 1024  # fixed, so chunked draws do not depend on the thread count
+
+
+def _threads() -> int:
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def _by_rows(n_rows: int, fn) -> None:
+    """fn(r0, r1) over row chunks of _ROWS_PER_CHUNK, on a thread pool (numpy
+    releases the GIL inside its array loops)."""
+    chunks = [(r, min(r + _ROWS_PER_CHUNK, n_rows)) for r in range(0, n_rows, _ROWS_PER_CHUNK)]
+    if len(chunks) <= 1:
+        for c in chunks:
+            fn(*c)
+        return
+    with concurrent.futures.ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(lambda c: fn(*c), chunks))
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round FP32 to bf16 (nearest, ties to even) and return the uint16 bits."""
-    b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
-    lsb = (b >> np.uint32(16)) & np.uint32(1)
-    return ((b + np.uint32(0x7FFF) + lsb) >> np.uint32(16)).astype(np.uint16)
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x.shape, np.uint16)
+    flat_in = x.reshape(x.shape[0], -1) if x.ndim > 1 else x.reshape(1, -1)
+    flat_out = out.reshape(flat_in.shape)
+
+    def conv(r0, r1):
+        b = flat_in[r0:r1].view(np.uint32)
+        lsb = (b >> np.uint32(16)) & np.uint32(1)
+        flat_out[r0:r1] = ((b + np.uint32(0x7FFF) + lsb) >> np.uint32(16)).astype(np.uint16)
+    _by_rows(flat_in.shape[0], conv)
+    return out
 
 
 def bf16_bits_to_f32(h: np.ndarray) -> np.ndarray:
@@ -60,13 +89,23 @@ def student_t(seed: int, shape, nu: float = 3.0) -> np.ndarray:
 
 
 def lognormal_signed(seed: int, shape, sigma: float = 2.0) -> np.ndarray:
-    """|v| = exp(sigma*z), z ~ N(0,1), with an independent random sign."""
-    rng = np.random.default_rng(seed)
-    z = rng.standard_normal(shape, dtype=np.float32)
-    s = rng.integers(0, 2, size=shape, dtype=np.int8)
-    v = np.exp(np.float32(sigma) * z)
-    v[s == 1] *= np.float32(-1.0)
-    return v
+    """|v| = exp(sigma*z), z ~ N(0,1), with an independent random sign.  Drawn
+    in chunks of 1024 rows, chunk k from the k-th child of SeedSequence(seed),
+    on a thread pool (the values do not depend on the thread count)."""
+    rows = shape[0]
+    out = np.empty(shape, np.float32)
+    kids = np.random.SeedSequence(seed).spawn(-(-rows // _ROWS_PER_CHUNK))
+
+    def fill(r0, r1):
+        rng = np.random.default_rng(kids[r0 // _ROWS_PER_CHUNK])
+        sub = (r1 - r0,) + tuple(shape[1:])
+        z = rng.standard_normal(sub, dtype=np.float32)
+        neg = rng.integers(0, 2, size=sub, dtype=np.int8).astype(bool)
+        v = np.exp(np.float32(sigma) * z)
+        np.negative(v, out=v, where=neg)
+        out[r0:r1] = v
+    _by_rows(rows, fill)
+    return out
 
 
 def sign_mask16(seed: int) -> int:

@@ -70,6 +70,7 @@ def lib():
         L.ora_bf16_rne_array.argtypes, L.ora_bf16_rne_array.restype = [i64, vp, vp], None
         L.ora_gemm_f64.argtypes, L.ora_gemm_f64.restype = [i64, i64, i64, vp, vp, f64, vp], None
         L.ora_num_threads.argtypes, L.ora_num_threads.restype = [], i32
+        L.ora_set_num_threads.argtypes, L.ora_set_num_threads.restype = [i32], None
         L.ora_mx_scale_exp.argtypes, L.ora_mx_scale_exp.restype = [f32], i32
         L.ora_mx_quantize_range.argtypes = [vp, i32, i64, i64, i64, i32, i32, u64, vp, vp, i64, i64]
         L.ora_mx_quantize_range.restype = i32
@@ -132,6 +133,11 @@ def rht16(x, sign_mask: int) -> np.ndarray:
 
 def num_threads() -> int:
     return lib().ora_num_threads()
+
+
+def set_num_threads(n: int) -> None:
+    """Threads of the C oracle's OpenMP loops (results do not depend on it)."""
+    lib().ora_set_num_threads(int(n))
 
 
 # ----------------------------------------------------------------- tensors

@@ -495,6 +495,19 @@ int ora_rht_quantize(const void *x, int dtype, int64_t tokens, int64_t cols, int
                                   scales, tensor_scale, amax_out, 0, INT64_MAX);
 }
 
+/* Set the number of threads the OpenMP loops use (results do not depend on
+ * it: every loop writes independent blocks, and the amax reduction is an
+ * exact maximum). */
+void ora_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0)
+        omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* Number of threads the OpenMP loops above use (1 without OpenMP). */
 int ora_num_threads(void)
 {
