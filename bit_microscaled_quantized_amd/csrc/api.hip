@@ -231,6 +231,21 @@ nvfp4_status mxfp4_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
   return e == hipSuccess ? NVFP4_OK : NVFP4_EHIP;
 }
 
+nvfp4_status nvfp4_set_quantize_passes(int passes) {
+  if (passes != 0 && passes != 2) return NVFP4_EINVAL;
+  return nvfp4::set_quantize_passes(passes) == hipSuccess ? NVFP4_OK : NVFP4_EHIP;
+}
+
+nvfp4_status nvfp4_set_sync_spin_limit(int64_t polls) {
+  if (polls < 0) return NVFP4_EINVAL;
+  return nvfp4::set_sync_spin_limit((uint64_t)polls) == hipSuccess ? NVFP4_OK : NVFP4_EHIP;
+}
+
+nvfp4_status nvfp4_single_pass_stats(int64_t* launches, int64_t* give_ups) {
+  if (launches == nullptr || give_ups == nullptr) return NVFP4_EINVAL;
+  return nvfp4::single_pass_stats(launches, give_ups) == hipSuccess ? NVFP4_OK : NVFP4_EHIP;
+}
+
 const char* nvfp4_status_str(int status) {
   switch (status) {
     case NVFP4_OK: return "NVFP4_OK";

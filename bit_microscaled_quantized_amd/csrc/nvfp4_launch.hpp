@@ -11,6 +11,19 @@ hipError_t launch_quantize(const void* x, int dt, int64_t rows, int64_t cols, in
                            uint8_t* codes_t, uint8_t* scales_t, float* tensor_scale, float* amax,
                            hipStream_t s);
 
+// Single-pass row-1D quantization when the tensor fits in the resident
+// grid's registers (contiguous rows, stream not capturing, cooperative launch
+// available); *done tells whether it ran (nothing is enqueued otherwise).
+hipError_t try_quantize_row_1pass(const void* x, int dt, int64_t rows, int64_t cols, int64_t ld,
+                                  int rnd, uint64_t seed, uint8_t* codes, uint8_t* scales,
+                                  float* tensor_scale, float* amax, hipStream_t s, bool* done);
+// 0: automatic choice of the single-pass path, 2: always two passes.
+hipError_t set_quantize_passes(int passes);
+// Polls a single-pass workgroup makes before it gives up waiting.
+hipError_t set_sync_spin_limit(uint64_t polls);
+// Single-pass launches on the current device and their workgroups that gave up.
+hipError_t single_pass_stats(int64_t* launches, int64_t* give_ups);
+
 hipError_t launch_rht_quantize(const void* x, int dt, int64_t tokens, int64_t cols, int64_t ld,
                                uint32_t sign_mask, int rnd, uint64_t seed, uint8_t* codes,
                                uint8_t* scales, float* tensor_scale, float* amax, hipStream_t s);

@@ -976,6 +976,12 @@ hipError_t launch_quantize(const void* x, int dt, int64_t rows, int64_t cols, in
                            int layout, int rnd, uint64_t seed, uint8_t* codes, uint8_t* scales,
                            uint8_t* codes_t, uint8_t* scales_t, float* tensor_scale, float* amax,
                            hipStream_t s) {
+  if (layout == 0) {
+    bool done = false;
+    hipError_t e = try_quantize_row_1pass(x, dt, rows, cols, ld, rnd, seed, codes, scales,
+                                          tensor_scale, amax, s, &done);
+    if (e != hipSuccess || done) return e;
+  }
   k_zero_amax<<<1, 64, 0, s>>>(amax, nullptr);
   hipError_t e = dt == 0 ? launch_amax<uint16_t>(x, rows, cols, ld, amax, s)
                          : launch_amax<float>(x, rows, cols, ld, amax, s);

@@ -20,8 +20,9 @@ NVFP4_RNE, NVFP4_SR = 0, 1
 NVFP4_ROW_1D, NVFP4_COL_1D, NVFP4_TILE_2D = 0, 1, 2
 
 EXPORTED = ("nvfp4_quantize", "nvfp4_rht_quantize", "nvfp4_quantize_row_rht", "nvfp4_gemm",
-            "nvfp4_gemm_noalloc", "nvfp4_gemm_bf16", "nvfp4_dequantize", "nvfp4_gemm_workspace_size", "nvfp4_status_str",
-            "mxfp4_quantize", "mxfp4_gemm")
+            "nvfp4_gemm_noalloc", "nvfp4_gemm_bf16", "nvfp4_dequantize", "nvfp4_gemm_workspace_size",
+            "nvfp4_set_quantize_passes", "nvfp4_set_sync_spin_limit", "nvfp4_single_pass_stats",
+            "nvfp4_status_str", "mxfp4_quantize", "mxfp4_gemm")
 
 _lib = None
 
@@ -44,6 +45,11 @@ def load_library():
     if not os.path.exists(_LIB_PATH):
         raise RuntimeError(f"{_LIB_PATH} is missing: build it with "
                            "`python -m bit_microscaled_quantized_amd.build`")
+    # torch first: it ships its own HIP runtime under the same soname, and the
+    # library must bind to that one instance (the tensors and streams it is
+    # given belong to it); loaded first, the library would pull in the system
+    # runtime and torch would then find no usable GPU.
+    import torch  # noqa: F401
     L = ctypes.CDLL(_LIB_PATH)
     i64, u64, u32, i32 = ctypes.c_int64, ctypes.c_uint64, ctypes.c_uint32, ctypes.c_int
     vp, f32 = ctypes.c_void_p, ctypes.c_float
@@ -69,6 +75,12 @@ def load_library():
     L.nvfp4_dequantize.restype = i32
     L.nvfp4_gemm_workspace_size.argtypes = [i64, i64, i64, ctypes.POINTER(i64)]
     L.nvfp4_gemm_workspace_size.restype = i32
+    L.nvfp4_set_quantize_passes.argtypes = [i32]
+    L.nvfp4_set_quantize_passes.restype = i32
+    L.nvfp4_set_sync_spin_limit.argtypes = [i64]
+    L.nvfp4_set_sync_spin_limit.restype = i32
+    L.nvfp4_single_pass_stats.argtypes = [ctypes.POINTER(i64), ctypes.POINTER(i64)]
+    L.nvfp4_single_pass_stats.restype = i32
     L.nvfp4_status_str.argtypes = [i32]
     L.nvfp4_status_str.restype = ctypes.c_char_p
     _lib = L
@@ -204,3 +216,21 @@ def mxfp4_gemm(M, N, K, a_codes, a_scales, b_codes, b_scales, c, ldc, beta, work
                                    _addr(b_scales), _addr(c), ldc, float(beta), _addr(workspace),
                                    int(workspace_bytes), _stream(stream))
     return _check("mxfp4_gemm", st, raise_on_error)
+
+
+def nvfp4_set_quantize_passes(passes: int) -> int:
+    """0: single pass where it applies (default); 2: always two passes."""
+    return _check("nvfp4_set_quantize_passes", load_library().nvfp4_set_quantize_passes(passes), True)
+
+
+def nvfp4_set_sync_spin_limit(polls: int) -> int:
+    """Polls before a single-pass workgroup gives up waiting (tests force it)."""
+    return _check("nvfp4_set_sync_spin_limit", load_library().nvfp4_set_sync_spin_limit(polls), True)
+
+
+def nvfp4_single_pass_stats() -> tuple[int, int]:
+    """(single-pass launches, workgroups that gave up) on the current device."""
+    n, g = ctypes.c_int64(0), ctypes.c_int64(0)
+    _check("nvfp4_single_pass_stats",
+           load_library().nvfp4_single_pass_stats(ctypes.byref(n), ctypes.byref(g)), True)
+    return n.value, g.value

@@ -37,8 +37,10 @@
  * Conventions for every entry point:
  *   - All tensor pointers are DEVICE pointers owned by the caller.  The library
  *     allocates and frees nothing and is reentrant; calls on different streams
- *     may overlap (but not while sharing a GEMM workspace).  Its only state is
- *     a per-device cache of the compute-unit count.
+ *     may overlap (but not while sharing a GEMM workspace).  Its state is a
+ *     per-device cache of the compute-unit count and occupancy, and two static
+ *     device arrays per device: the single-pass quantize exchange slots (4 KiB)
+ *     and the split workspace of nvfp4_gemm_noalloc (64 MiB).
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
  *     work is enqueued asynchronously on it; results are visible after the
  *     caller synchronizes that stream.
@@ -94,6 +96,20 @@ typedef enum { NVFP4_ROW_1D = 0, NVFP4_COL_1D = 1, NVFP4_TILE_2D = 2 } nvfp4_lay
  *   tensor_scale, amax  one float each (device): outputs 1/S_enc and amax_t.
  *   rows, cols must be positive multiples of 16; all pointers 16-byte aligned
  *   except tensor_scale / amax (4-byte).
+ *   Passes: the tensor amax is needed before any element is encoded ("Escala
+ *   em Dois Niveis").  A contiguous (ld_x == cols) ROW_1D tensor that fits in
+ *   the registers of one resident grid (on a 256-CU MI355X up to 84 MB of
+ *   bf16, e.g. 8192 x 5120, or 42 MB of FP32) is read ONCE: a grid no larger
+ *   than what fits on the device at once keeps it on chip while its
+ *   workgroups exchange the amax through a per-(device, stream) slot of
+ *   library-owned device memory, then encodes it.  The wait is bounded: a
+ *   workgroup that waits too long (its grid partly displaced by other
+ *   streams' kernels) leaves its blocks to the last workgroup to finish, which
+ *   encodes them from memory, so the outputs are always complete.
+ *   Everything else, and any call on a stream under graph capture, takes two
+ *   passes (amax, then cast).  Both give identical outputs.  Calls on one
+ *   stream never share a slot with another stream's calls (64 slots per
+ *   device; further streams take two passes).
  */
 nvfp4_status nvfp4_quantize(const void *x, int dt, int64_t rows, int64_t cols, int64_t ld_x,
                             int layout, int rnd, uint64_t seed, uint8_t *codes, uint8_t *scales,
@@ -249,6 +265,26 @@ nvfp4_status nvfp4_dequantize(const uint8_t *codes, const uint8_t *scales, int32
  * `bytes` must not be NULL.
  */
 nvfp4_status nvfp4_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int64_t *bytes);
+
+/*
+ * Controls and counters of the single-pass quantize path (nvfp4_quantize,
+ * ROW_1D).  Process-wide settings, safe to call from any thread.
+ *   nvfp4_set_quantize_passes(passes): 0 (default) picks the single pass where
+ *     it applies; 2 always takes the two-pass path.  Other values: EINVAL.
+ *   nvfp4_set_sync_spin_limit(polls): how many times a workgroup polls the
+ *     device-wide exchange (about 1 us each) before it gives up and leaves its
+ *     blocks to the last workgroup (default 2^14, far beyond the wait of a
+ *     resident grid).  Giving up changes only the speed, never the result;
+ *     tests use it to force that path from the host.  polls >= 0.
+ *   nvfp4_single_pass_stats(launches, give_ups): on the CURRENT device since
+ *     the library was loaded, the number of single-pass launches enqueued and
+ *     of their workgroups that gave up waiting (a synchronous device read;
+ *     call after synchronizing the streams in question).  Both pointers are
+ *     host pointers.
+ */
+nvfp4_status nvfp4_set_quantize_passes(int passes);
+nvfp4_status nvfp4_set_sync_spin_limit(int64_t polls);
+nvfp4_status nvfp4_single_pass_stats(int64_t *launches, int64_t *give_ups);
 
 /* Static, human-readable name of a status code. */
 const char *nvfp4_status_str(int status);

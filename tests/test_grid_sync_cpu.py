@@ -1,0 +1,177 @@
+"""CPU emulation of the single-pass quantizer's device-wide amax exchange
+(bit_microscaled_quantized_amd/csrc/grid_sync.hpp), run before and beside the
+GPU: the header's protocol is compiled with g++ against std::atomic and each
+workgroup of a launch is a thread.  Per launch it checks that every
+workgroup either learns the exact tensor maximum and writes its own blocks,
+or gives up and has its blocks written by the last workgroup to leave (each
+block written exactly once), that nothing hangs, and that the slot is back
+at its idle state for the next launch on it.
+
+* full residency: launches of G = 1 .. 200 workgroups (random start delays)
+  on one slot, nobody gives up;
+* limited residency (at most R < G workgroups run at once, the rest start
+  only when one ends, as on a GPU whose grid is partly displaced): workgroups
+  that wait past the spin limit give up and are counted, the last one to
+  leave covers their blocks, and the next launch on the slot runs clean;
+* a spin limit of zero: only workgroups that arrive after the result is
+  published pass; the rest are covered.
+
+The same program is also built with ThreadSanitizer to check that the
+protocol has no data race."""
+import os
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HDR = os.path.join(ROOT, "bit_microscaled_quantized_amd", "csrc")
+
+SRC = r"""
+#define __host__
+#define __device__
+#include <atomic>
+#include <chrono>
+#include <condition_variable>
+#include <cstdio>
+#include <mutex>
+#include <random>
+#include <thread>
+#include <vector>
+#include "grid_sync.hpp"
+using nvfp4::GridSyncSlot;
+
+struct CpuOps {
+  static std::atomic_ref<uint32_t> at(uint32_t* p) { return std::atomic_ref<uint32_t>(*p); }
+  static void max_relaxed(uint32_t* p, uint32_t v) {
+    auto a = at(p);
+    uint32_t cur = a.load(std::memory_order_relaxed);
+    while (cur < v && !a.compare_exchange_weak(cur, v, std::memory_order_relaxed)) {
+    }
+  }
+  static uint32_t add_release(uint32_t* p, uint32_t v) { return at(p).fetch_add(v, std::memory_order_acq_rel); }
+  static uint32_t load_relaxed(uint32_t* p) { return at(p).load(std::memory_order_relaxed); }
+  static void store_relaxed(uint32_t* p, uint32_t v) { at(p).store(v, std::memory_order_relaxed); }
+  static void store_release(uint32_t* p, uint32_t v) { at(p).store(v, std::memory_order_release); }
+  static void fence_acquire() { std::atomic_thread_fence(std::memory_order_acquire); }
+  static void pause() { std::this_thread::yield(); }
+};
+
+// counting semaphore: at most `cap` workgroups resident at once
+struct Residency {
+  std::mutex mu;
+  std::condition_variable cv;
+  int free;
+  explicit Residency(int cap) : free(cap) {}
+  void enter() { std::unique_lock<std::mutex> l(mu); cv.wait(l, [&] { return free > 0; }); free--; }
+  void leave() { { std::lock_guard<std::mutex> l(mu); free++; } cv.notify_one(); }
+};
+
+static int fails = 0;
+#define CHECK(c) do { if (!(c)) { std::printf("FAIL line %d: %s\n", __LINE__, #c); fails++; } } while (0)
+
+static bool idle(const GridSyncSlot* s) {
+  for (uint32_t g = 0; g < nvfp4::kSyncGroups; g++)
+    if (s->group[g].arrive || s->group[g].amax || s->group[g].depart) return false;
+  return !s->top.arrive && !s->top.amax && !s->top.depart && !s->gave_up_n;
+}
+
+// one launch of G workgroups; returns how many gave up
+static int launch(GridSyncSlot* s, uint32_t epoch, int G, int resident, uint64_t spin,
+                  std::mt19937& rng) {
+  std::vector<uint32_t> vals(G), got(G, 0xFFFFFFFFu);
+  std::vector<int> writes(G, 0);  // how many times workgroup i's blocks were written
+  std::vector<int> ok(G, 0);
+  uint32_t want = 0;
+  for (int i = 0; i < G; i++) { vals[i] = rng() >> 1; want = vals[i] > want ? vals[i] : want; }
+  std::vector<int> delay(G);
+  for (int i = 0; i < G; i++) delay[i] = (int)(rng() % 200);
+  std::mutex wmu;
+  int lasts = 0;
+  uint32_t last_amax = 0xFFFFFFFFu;
+  Residency res(resident);
+  std::vector<std::thread> th;
+  for (int i = 0; i < G; i++)
+    th.emplace_back([&, i] {
+      res.enter();
+      std::this_thread::sleep_for(std::chrono::microseconds(delay[i]));
+      uint32_t bits = 0;
+      ok[i] = nvfp4::grid_arrive_wait<CpuOps>(s, (uint32_t)G, (uint32_t)i, vals[i], epoch, spin, &bits);
+      got[i] = bits;
+      if (ok[i]) { std::lock_guard<std::mutex> l(wmu); writes[i]++; }
+      if (nvfp4::grid_depart<CpuOps>(s, (uint32_t)G, (uint32_t)i)) {
+        uint32_t amax = 0;
+        const uint32_t n = nvfp4::grid_recover_list<CpuOps>(s, &amax);
+        std::lock_guard<std::mutex> l(wmu);
+        lasts++;
+        last_amax = amax;
+        for (uint32_t k = 0; k < n; k++) writes[s->gave_up_list[k]]++;
+        nvfp4::grid_finish<CpuOps>(s);
+      }
+      res.leave();
+    });
+  for (auto& t : th) t.join();
+  int gave_up = 0;
+  for (int i = 0; i < G; i++) {
+    if (ok[i]) CHECK(got[i] == want);
+    else gave_up++;
+    CHECK(writes[i] == 1);
+  }
+  CHECK(lasts == 1);
+  CHECK(last_amax == want);
+  CHECK(s->done == epoch);
+  CHECK(idle(s));
+  return gave_up;
+}
+
+int main() {
+  std::mt19937 rng(1234);
+  static GridSyncSlot slot;  // zero-initialized, as the device array
+  uint32_t epoch = 0;
+  // full residency, generous spin limit
+  const int Gs[] = {1, 2, 3, 15, 16, 17, 33, 64, 200};
+  for (int rep = 0; rep < 20 && !fails; rep++)
+    for (int G : Gs) {
+      CHECK(launch(&slot, ++epoch, G, G, uint64_t(1) << 22, rng) == 0);
+      if (fails) break;
+    }
+  CHECK(slot.gave_ups == 0);
+  if (fails) { std::printf("FAILED\n"); return 1; }
+  // limited residency: must end, some give up, all blocks covered, the slot recovers
+  for (int rep = 0; rep < 10; rep++) {
+    const uint32_t before = slot.gave_ups;
+    const int g = launch(&slot, ++epoch, 40, 6, 2000, rng);
+    CHECK(g >= 1 && g <= 39);
+    CHECK(slot.gave_ups == before + (uint32_t)g);
+    CHECK(launch(&slot, ++epoch, 40, 40, uint64_t(1) << 22, rng) == 0);
+    if (fails) break;
+  }
+  // spin limit zero, full residency
+  for (int rep = 0; rep < 20 && !fails; rep++) launch(&slot, ++epoch, 24, 24, 0, rng);
+  std::printf("%s\n", fails ? "FAILED" : "OK");
+  return fails ? 1 : 0;
+}
+"""
+
+
+def _build_and_run(tmp_path, extra):
+    src = tmp_path / "grid_sync_emu.cpp"
+    src.write_text(SRC)
+    exe = tmp_path / ("emu" + ("_tsan" if extra else ""))
+    cmd = ["g++", "-std=c++20", "-O1", "-g", "-pthread", "-I", HDR, *extra, "-o", str(exe), str(src)]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    env = dict(os.environ, TSAN_OPTIONS="halt_on_error=1")
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=300, env=env)
+    assert r.returncode == 0 and r.stdout.strip().endswith("OK"), r.stdout + r.stderr
+
+
+def test_grid_exchange_protocol(tmp_path):
+    _build_and_run(tmp_path, [])
+
+
+def test_grid_exchange_protocol_threadsanitizer(tmp_path):
+    probe = subprocess.run(["g++", "-fsanitize=thread", "-x", "c++", "-", "-o", os.devnull],
+                           input="int main(){return 0;}", capture_output=True, text=True)
+    if probe.returncode != 0:
+        pytest.skip("g++ has no ThreadSanitizer here")
+    _build_and_run(tmp_path, ["-fsanitize=thread"])

@@ -234,3 +234,14 @@ def test_gemm_noalloc_argument_errors():
     assert gn(c=FAKE + 4) == b.NVFP4_EALIGN
     assert gn(ldc=258) == b.NVFP4_EALIGN
     assert "static" in nv.nvfp4_status_str(b.NVFP4_ESCRATCH)
+
+
+def test_single_pass_controls():
+    L = b.load_library()
+    assert L.nvfp4_set_quantize_passes(1) == b.NVFP4_EINVAL
+    assert L.nvfp4_set_quantize_passes(3) == b.NVFP4_EINVAL
+    assert L.nvfp4_set_quantize_passes(2) == b.NVFP4_OK
+    assert L.nvfp4_set_quantize_passes(0) == b.NVFP4_OK
+    assert L.nvfp4_set_sync_spin_limit(-1) == b.NVFP4_EINVAL
+    assert L.nvfp4_set_sync_spin_limit(1 << 24) == b.NVFP4_OK
+    assert L.nvfp4_single_pass_stats(None, None) == b.NVFP4_EINVAL
