@@ -57,6 +57,7 @@ def lib():
         L.ora_encode_scale.argtypes, L.ora_encode_scale.restype = [f32], f32
         L.ora_block_scale.argtypes, L.ora_block_scale.restype = [f32, f32], i32
         L.ora_element_scale.argtypes, L.ora_element_scale.restype = [i32, f32], f32
+        L.ora_block_scale_array.argtypes, L.ora_block_scale_array.restype = [vp, i64, f32, vp], None
         L.ora_quantize_range.argtypes = [vp, i32, i64, i64, i64, i32, i32, u64, vp, vp, vp, vp,
                                          vp, vp, i64, i64]
         L.ora_quantize_range.restype = i32
@@ -118,6 +119,14 @@ def encode_scale(amax_t: float) -> float:
 
 def block_scale(amax_b: float, s_enc: float) -> int:
     return lib().ora_block_scale(amax_b, s_enc)
+
+
+def block_scale_array(amax_b: np.ndarray, s_enc: float) -> np.ndarray:
+    """block_scale of every entry of an FP32 array of block maxima."""
+    a = np.ascontiguousarray(amax_b, dtype=np.float32)
+    out = np.empty(a.shape, np.uint8)
+    lib().ora_block_scale_array(_ptr(a), a.size, s_enc, _ptr(out))
+    return out
 
 
 def element_scale(e_b: int, s_enc: float) -> float:

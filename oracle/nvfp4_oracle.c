@@ -247,6 +247,15 @@ int ora_block_scale(float amax_b, float s_enc)
     return ora_e4m3_rne_satfinite(sb);
 }
 
+/* ora_block_scale over an array of block maxima (OpenMP over entries). */
+void ora_block_scale_array(const float *amax_b, int64_t n, float s_enc, uint8_t *out)
+{
+    int64_t i;
+#pragma omp parallel for schedule(static)
+    for (i = 0; i < n; i++)
+        out[i] = (uint8_t)ora_block_scale(amax_b[i], s_enc);
+}
+
 /* Multiplier that maps a block's values onto the E2M1 grid. */
 float ora_element_scale(int e_b, float s_enc)
 {

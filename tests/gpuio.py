@@ -1,5 +1,7 @@
 """Helpers for the GPU tests: move seeded numpy inputs to the device, call the
-HIP library through its C ABI (the Python binding), and bring results back."""
+HIP library through its C ABI (the Python binding), and bring results back.
+Every output buffer they hand to the library sits between 4 KiB guard zones
+that are checked after the call."""
 from __future__ import annotations
 
 import numpy as np
@@ -28,6 +30,35 @@ def host(t) -> np.ndarray:
     return t.cpu().numpy()
 
 
+GUARD = 4096    # bytes of guard zone on each side of every output buffer
+PATTERN = 0xA5  # the guard bytes
+
+
+class Guarded:
+    """Output buffers with 4 KiB guard zones before and after them.  Each
+    buffer is a view into a larger allocation whose guard bytes hold PATTERN;
+    check() asserts that no call wrote outside the buffers it was given."""
+
+    def __init__(self):
+        self.bufs = []
+
+    def alloc(self, shape, dtype, fill=None):
+        torch = torch_cuda()
+        n = int(np.prod(shape)) * torch.empty((), dtype=dtype).element_size()
+        base = torch.full((n + 2 * GUARD,), PATTERN, dtype=torch.uint8, device="cuda")
+        t = base[GUARD:GUARD + n].view(dtype).view(shape)
+        if fill is not None:
+            t.fill_(fill)
+        self.bufs.append((base, n))
+        return t
+
+    def check(self):
+        for base, n in self.bufs:
+            head, tail = base[:GUARD], base[GUARD + n:]
+            assert bool((head == PATTERN).all()) and bool((tail == PATTERN).all()), \
+                "a kernel wrote outside its output buffer"
+
+
 def gpu_quantize(x: np.ndarray, layout: int, rnd: int = 0, seed: int = 0, ld: int | None = None,
                  transpose: bool = True) -> dict:
     """Quantize x (rows x cols; bf16 bits or fp32) on the GPU.  With ld > cols
@@ -41,25 +72,27 @@ def gpu_quantize(x: np.ndarray, layout: int, rnd: int = 0, seed: int = 0, ld: in
     else:
         ld = cols
         xd = to_dev(x)
-    u8 = dict(dtype=torch.uint8, device="cuda")
+    g = Guarded()
+    u8 = torch.uint8
     if layout == nv.NVFP4_COL_1D:
-        codes = torch.empty((cols, rows // 2), **u8)
-        scales = torch.empty((cols, rows // 16), **u8)
+        codes = g.alloc((cols, rows // 2), u8)
+        scales = g.alloc((cols, rows // 16), u8)
     elif layout == nv.NVFP4_ROW_1D:
-        codes = torch.empty((rows, cols // 2), **u8)
-        scales = torch.empty((rows, cols // 16), **u8)
+        codes = g.alloc((rows, cols // 2), u8)
+        scales = g.alloc((rows, cols // 16), u8)
     else:
-        codes = torch.empty((rows, cols // 2), **u8)
-        scales = torch.empty((rows // 16, cols // 16), **u8)
+        codes = g.alloc((rows, cols // 2), u8)
+        scales = g.alloc((rows // 16, cols // 16), u8)
     codes_t = scales_t = None
     if layout == nv.NVFP4_TILE_2D and transpose:
-        codes_t = torch.empty((cols, rows // 2), **u8)
-        scales_t = torch.empty((cols // 16, rows // 16), **u8)
-    ts = torch.empty(1, dtype=torch.float32, device="cuda")
-    am = torch.empty(1, dtype=torch.float32, device="cuda")
+        codes_t = g.alloc((cols, rows // 2), u8)
+        scales_t = g.alloc((cols // 16, rows // 16), u8)
+    ts = g.alloc((1,), torch.float32)
+    am = g.alloc((1,), torch.float32)
     nv.nvfp4_quantize(xd, dtype_code(x), rows, cols, ld, layout, rnd, seed, codes, scales,
                       codes_t, scales_t, ts, am)
     torch.cuda.synchronize()
+    g.check()
     out = dict(codes=host(codes), scales=host(scales), tensor_scale=float(host(ts)[0]),
                amax=float(host(am)[0]), dev=dict(codes=codes, scales=scales, ts=ts,
                                                  codes_t=codes_t, scales_t=scales_t))
@@ -72,13 +105,15 @@ def gpu_rht_quantize(x: np.ndarray, sign_mask: int, rnd: int = 0, seed: int = 0)
     torch = torch_cuda()
     tokens, cols = x.shape
     xd = to_dev(x)
-    codes = torch.empty((cols, tokens // 2), dtype=torch.uint8, device="cuda")
-    scales = torch.empty((cols, tokens // 16), dtype=torch.uint8, device="cuda")
-    ts = torch.empty(1, dtype=torch.float32, device="cuda")
-    am = torch.empty(1, dtype=torch.float32, device="cuda")
+    g = Guarded()
+    codes = g.alloc((cols, tokens // 2), torch.uint8)
+    scales = g.alloc((cols, tokens // 16), torch.uint8)
+    ts = g.alloc((1,), torch.float32)
+    am = g.alloc((1,), torch.float32)
     nv.nvfp4_rht_quantize(xd, dtype_code(x), tokens, cols, cols, sign_mask, rnd, seed, codes,
                           scales, ts, am)
     torch.cuda.synchronize()
+    g.check()
     return dict(codes=host(codes), scales=host(scales), tensor_scale=float(host(ts)[0]),
                 amax=float(host(am)[0]), dev=dict(codes=codes, scales=scales, ts=ts))
 
@@ -90,14 +125,15 @@ def gpu_quantize_row_rht(x: np.ndarray, sign_mask: int, row_rnd: int, row_seed: 
     torch = torch_cuda()
     tokens, cols = x.shape
     xd = to_dev(x)
-    u8 = dict(dtype=torch.uint8, device="cuda")
-    f32 = dict(dtype=torch.float32, device="cuda")
-    rc, rs = torch.empty((tokens, cols // 2), **u8), torch.empty((tokens, cols // 16), **u8)
-    hc, hs = torch.empty((cols, tokens // 2), **u8), torch.empty((cols, tokens // 16), **u8)
-    rts, ram, hts, ham = (torch.empty(1, **f32) for _ in range(4))
+    g = Guarded()
+    u8 = torch.uint8
+    rc, rs = g.alloc((tokens, cols // 2), u8), g.alloc((tokens, cols // 16), u8)
+    hc, hs = g.alloc((cols, tokens // 2), u8), g.alloc((cols, tokens // 16), u8)
+    rts, ram, hts, ham = (g.alloc((1,), torch.float32) for _ in range(4))
     nv.nvfp4_quantize_row_rht(xd, dtype_code(x), tokens, cols, cols, row_rnd, row_seed, rc, rs, rts, ram,
                               sign_mask, rht_rnd, rht_seed, hc, hs, hts, ham)
     torch.cuda.synchronize()
+    g.check()
     row = dict(codes=host(rc), scales=host(rs), tensor_scale=float(host(rts)[0]), amax=float(host(ram)[0]),
                dev=dict(codes=rc, scales=rs, ts=rts))
     rht = dict(codes=host(hc), scales=host(hs), tensor_scale=float(host(hts)[0]), amax=float(host(ham)[0]),
@@ -110,28 +146,32 @@ def gpu_mx_quantize(x: np.ndarray, layout: int, rnd: int = 0, seed: int = 0) -> 
     torch = torch_cuda()
     rows, cols = x.shape
     xd = to_dev(x)
-    u8 = dict(dtype=torch.uint8, device="cuda")
+    g = Guarded()
     if layout == nv.NVFP4_COL_1D:
-        codes = torch.empty((cols, rows // 2), **u8)
-        scales = torch.empty((cols, rows // 32), **u8)
+        codes = g.alloc((cols, rows // 2), torch.uint8)
+        scales = g.alloc((cols, rows // 32), torch.uint8)
     else:
-        codes = torch.empty((rows, cols // 2), **u8)
-        scales = torch.empty((rows, cols // 32), **u8)
+        codes = g.alloc((rows, cols // 2), torch.uint8)
+        scales = g.alloc((rows, cols // 32), torch.uint8)
     nv.mxfp4_quantize(xd, dtype_code(x), rows, cols, cols, layout, rnd, seed, codes, scales)
     torch.cuda.synchronize()
+    g.check()
     return dict(codes=host(codes), scales=host(scales), dev=dict(codes=codes, scales=scales))
 
 
 def gpu_mx_gemm(M, N, K, a: dict, b: dict, c0: np.ndarray | None = None, beta: float = 0.0,
                 workspace="auto") -> np.ndarray:
     torch = torch_cuda()
-    c = torch.zeros((M, N), dtype=torch.float32, device="cuda") if c0 is None else \
-        to_dev(np.ascontiguousarray(c0, dtype=np.float32))
+    g = Guarded()
+    c = g.alloc((M, N), torch.float32, fill=0.0)
+    if c0 is not None:
+        c.copy_(to_dev(np.ascontiguousarray(c0, dtype=np.float32)))
     if isinstance(workspace, str):
         workspace = nv.nvfp4_gemm_workspace_size(M, N, K)
-    ws = torch.full((workspace // 4,), float("nan"), dtype=torch.float32, device="cuda") if workspace else None
+    ws = g.alloc((workspace // 4,), torch.float32, fill=float("nan")) if workspace else None
     nv.mxfp4_gemm(M, N, K, a["codes"], a["scales"], b["codes"], b["scales"], c, N, beta, workspace=ws)
     torch.cuda.synchronize()
+    g.check()
     return host(c)
 
 
@@ -142,19 +182,20 @@ def gpu_gemm(M, N, K, a: dict, b: dict, b_rowdiv: int, c0: np.ndarray | None = N
     workspace: "auto" allocates the size the library asks for, None passes NULL,
     an int passes a workspace of that many bytes."""
     torch = torch_cuda()
-    if c0 is None:
-        c = torch.zeros((M, N), dtype=torch.float32, device="cuda")
-    else:
-        c = to_dev(np.ascontiguousarray(c0, dtype=np.float32))
+    g = Guarded()
+    c = g.alloc((M, N), torch.float32, fill=0.0)
+    if c0 is not None:
+        c.copy_(to_dev(np.ascontiguousarray(c0, dtype=np.float32)))
     if isinstance(workspace, str):
         workspace = nv.nvfp4_gemm_workspace_size(M, N, K)
     ws = None
     if workspace:
         # filled with NaN so that a partial tile the kernel failed to write shows
-        ws = torch.full((workspace // 4,), float("nan"), dtype=torch.float32, device="cuda")
+        ws = g.alloc((workspace // 4,), torch.float32, fill=float("nan"))
     nv.nvfp4_gemm(M, N, K, a["codes"], a["scales"], a["ts"], b["codes"], b["scales"], b_rowdiv,
                   b["ts"], c, N, beta, workspace=ws)
     torch.cuda.synchronize()
+    g.check()
     return host(c)
 
 

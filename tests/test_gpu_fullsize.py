@@ -12,7 +12,9 @@ times (LinearStep), checked on sampled outputs the oracle computes one by one:
   stream, W quantized once, Wgrad accumulated with beta = 1.
 
 The oracle takes each tensor amax over the whole tensor and encodes only the
-sampled lines; codes and scales are compared bit for bit on those lines.  GEMM
+sampled lines (16 blocks of 16 lines per tensor dimension: first, last and
+random middle ones; 6 token blocks per step); codes and scales are compared
+bit for bit on those lines.  GEMM
 references are FP64 products of the oracle's own dequantized lines, compared
 with the GPU output on the sampled row x column blocks (relative Frobenius
 error <= 1e-5)."""
@@ -91,7 +93,7 @@ def test_quantize_sweep_fullsize(ora, which, rnd):
     x = synth.f32_to_bf16_bits(synth.quantize_sweep(which))
     seed = 1234 + which
     g = gpuio.gpu_quantize(x, nv.NVFP4_ROW_1D, rnd, seed)
-    starts = _starts(x.shape[0], 4, which)
+    starts = _starts(x.shape[0], 16, which)
     lines = OracleLines(lambda ln: ora.quantize(x, ora.ROW_1D, rnd, seed, lines=ln), starts)
     _check(g["codes"], g["scales"], g["tensor_scale"], g["amax"], lines, starts)
 
@@ -104,7 +106,7 @@ def test_wgrad_rht_fullsize(ora):
     gdy = gpuio.gpu_rht_quantize(dy, mask, nv.NVFP4_SR, seed)
     gx = gpuio.gpu_rht_quantize(x, mask, nv.NVFP4_RNE, 0)
     c = gpuio.gpu_gemm(C, C, T, gdy["dev"], gx["dev"], 1)
-    rs, cs = _starts(C, 3, 1), _starts(C, 3, 2)
+    rs, cs = _starts(C, 16, 1), _starts(C, 16, 2)
     ly = OracleLines(lambda ln: ora.rht_quantize(dy, mask, ora.SR, seed, lines=ln), rs)
     lx = OracleLines(lambda ln: ora.rht_quantize(x, mask, ora.RNE, 0, lines=ln), cs)
     _check(gdy["codes"], gdy["scales"], gdy["tensor_scale"], gdy["amax"], ly, rs)
@@ -150,7 +152,7 @@ def test_ffn_up_step_fullsize(ora):
     st.step(gpuio.to_dev(x), gpuio.to_dev(w), gpuio.to_dev(dy), nv.NVFP4_BF16, mask, s_row, s_col)
     torch.cuda.synchronize()
     ow = ora.quantize(w, ora.TILE_2D, ora.RNE)
-    ts_, ti, to = _starts(T, 3, 3), _starts(IN, 3, 4), _starts(OUT, 3, 5)
+    ts_, ti, to = _starts(T, 6, 3), _starts(IN, 16, 4), _starts(OUT, 16, 5)
     ldt, lxt = _check_step(ora, st, x, w, dy, mask, s_row, s_col, ts_, ti, to, ow)
     _gemm_block(ora, _host(st.dw), ldt.deq(ora), lxt.deq(ora), _idx(to), _idx(ti))
 
@@ -171,7 +173,7 @@ def test_ffn_down_stress_chunked(ora):
     st = LinearStep(T, IN, OUT)
     st.quantize_weight(gpuio.to_dev(w), nv.NVFP4_BF16)
     ow = ora.quantize(w, ora.TILE_2D, ora.RNE)
-    ts_, ti, to = _starts(T, 3, 6), _starts(IN, 3, 7), _starts(OUT, 3, 8)
+    ts_, ti, to = _starts(T, 6, 6), _starts(IN, 16, 7), _starts(OUT, 16, 8)
     dw_ref = None
     for ch in range(4):
         xs = np.ascontiguousarray(x_in[ch * T:(ch + 1) * T])

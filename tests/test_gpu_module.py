@@ -77,9 +77,11 @@ def test_dequantize_2d_and_transposed(ora, out_dt):
     dts = torch.tensor([ts], dtype=torch.float32, device="cuda")
     tdt = torch.float32 if out_dt == nv.NVFP4_F32 else torch.bfloat16
     for codes, scales, (r, c) in ((q["codes"], q["scales"], (320, 192)), (q["codes_t"], q["scales_t"], (192, 320))):
-        out = torch.empty((r, c), dtype=tdt, device="cuda")
+        gd = gpuio.Guarded()
+        out = gd.alloc((r, c), tdt)
         nv.nvfp4_dequantize(gpuio.to_dev(codes), gpuio.to_dev(scales), 16, dts, r, c, out_dt, out, c)
         torch.cuda.synchronize()
+        gd.check()
         if out_dt == nv.NVFP4_F32:
             assert np.array_equal(out.cpu().numpy(), ora.dequant_f32(codes, scales, ts, 16))
         else:
@@ -112,11 +114,13 @@ def test_gemm_bf16_output(ora, M, N, K):
     da, db = _dev_q(torch, qa), _dev_q(torch, qb)
     ref = ora.gemm_f64(ora.dequant(qa["codes"], qa["scales"], qa["tensor_scale"]),
                        ora.dequant(qb["codes"], qb["scales"], qb["tensor_scale"], 16))
-    c = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
-    ws = torch.empty(max(nv.nvfp4_gemm_workspace_size(M, N, K), 16), dtype=torch.uint8, device="cuda")
+    gd = gpuio.Guarded()
+    c = gd.alloc((M, N), torch.bfloat16)
+    ws = gd.alloc((max(nv.nvfp4_gemm_workspace_size(M, N, K), 16),), torch.uint8)
     nv.nvfp4_gemm_bf16(M, N, K, da["codes"], da["scales"], da["ts"], db["codes"], db["scales"], 16,
                        db["ts"], c, N, 0.0, workspace=ws)
     torch.cuda.synchronize()
+    gd.check()
     _close_bf16(c.cpu().view(torch.int16).numpy().view(np.uint16), ref, f"{M}x{N}x{K}")
 
     # beta = 1: the BF16 values already in C are widened, added in FP32, rounded once
