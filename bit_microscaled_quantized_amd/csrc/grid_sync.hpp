@@ -42,7 +42,8 @@ struct alignas(128) SyncLine {
   uint32_t arrive;
   uint32_t amax;  // FP32 bits of a non-negative maximum (integer order = float order)
   uint32_t depart;
-  uint32_t pad[29];
+  uint32_t amax2;  // a second maximum (grid_max_arrive)
+  uint32_t pad[28];
 };
 
 struct GridSyncSlot {
@@ -141,6 +142,36 @@ __host__ __device__ inline uint32_t grid_recover_list(GridSyncSlot* s, uint32_t*
 template <typename Ops>
 __host__ __device__ inline void grid_finish(GridSyncSlot* s) {
   Ops::store_relaxed(&s->gave_up_n, 0u);
+}
+
+// A grid-wide maximum without waiting (the amax passes of the two-pass
+// path): every workgroup contributes two maxima through the same two-level
+// lines; the one that arrives last overall gets both results (returns true)
+// and writes them wherever they are needed, and the lines it used are back
+// at zero.  No workgroup waits, so any grid size and any residency works.
+template <typename Ops>
+__host__ __device__ inline bool grid_max_arrive(GridSyncSlot* s, uint32_t G, uint32_t w, uint32_t m0,
+                                                uint32_t m1, uint32_t* r0, uint32_t* r1) {
+  const uint32_t g = w % kSyncGroups;
+  SyncLine* gl = &s->group[g];
+  Ops::max_relaxed(&gl->amax, m0);
+  Ops::max_relaxed(&gl->amax2, m1);
+  if (Ops::add_release(&gl->arrive, 1u) != sync_group_size(G, g) - 1u) return false;
+  Ops::fence_acquire();
+  const uint32_t g0 = Ops::load_relaxed(&gl->amax), g1 = Ops::load_relaxed(&gl->amax2);
+  Ops::store_relaxed(&gl->amax, 0u);
+  Ops::store_relaxed(&gl->amax2, 0u);
+  Ops::store_relaxed(&gl->arrive, 0u);
+  Ops::max_relaxed(&s->top.amax, g0);
+  Ops::max_relaxed(&s->top.amax2, g1);
+  if (Ops::add_release(&s->top.arrive, 1u) != sync_groups_used(G) - 1u) return false;
+  Ops::fence_acquire();
+  *r0 = Ops::load_relaxed(&s->top.amax);
+  *r1 = Ops::load_relaxed(&s->top.amax2);
+  Ops::store_relaxed(&s->top.amax, 0u);
+  Ops::store_relaxed(&s->top.amax2, 0u);
+  Ops::store_relaxed(&s->top.arrive, 0u);
+  return true;
 }
 
 }  // namespace nvfp4

@@ -17,6 +17,9 @@ hipError_t launch_quantize(const void* x, int dt, int64_t rows, int64_t cols, in
 hipError_t try_quantize_row_1pass(const void* x, int dt, int64_t rows, int64_t cols, int64_t ld,
                                   int rnd, uint64_t seed, uint8_t* codes, uint8_t* scales,
                                   float* tensor_scale, float* amax, hipStream_t s, bool* done);
+struct GridSyncSlot;
+// The per-(device, stream) exchange slot, or nullptr where none may be used.
+GridSyncSlot* stream_sync_slot(hipStream_t s);
 // 0: automatic choice of the single-pass path, 2: always two passes.
 hipError_t set_quantize_passes(int passes);
 // Polls a single-pass workgroup makes before it gives up waiting.

@@ -14,8 +14,10 @@
 // stores stay contiguous.  Each workgroup first tabulates S_enc / dec(e) for
 // the 127 finite E4M3 codes in LDS, so a block scale costs one division by 6
 // (a multiply and two FMAs) and one table read.
+#include "grid_sync.hpp"
 #include "nvfp4_device.hpp"
 #include "nvfp4_launch.hpp"
+#include "sync_ops.hpp"
 
 namespace nvfp4 {
 
@@ -38,10 +40,14 @@ __device__ __forceinline__ void atomic_max_if_larger(uint32_t r, float* amax) {
   if (r > __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) atomicMax(a, r);
 }
 
-// Per-block maxima of non-negative float bit patterns (m1 only if amax1 is
-// not null) -> one atomicMax each.
-__device__ __forceinline__ void block_atomic_max(uint32_t m0, float* amax0, uint32_t m1 = 0u,
-                                                 float* amax1 = nullptr) {
+// The workgroup's maxima of non-negative float bit patterns (m1 only if
+// amax1 is not null) into the tensor amax outputs.  With an exchange slot the
+// grid's maxima meet on its two-level lines (no workgroup waits) and the last
+// workgroup to arrive writes both outputs, so the outputs need no clearing
+// beforehand; without one (a stream under graph capture), one atomicMax each
+// into outputs cleared by k_zero_amax.
+__device__ __forceinline__ void block_atomic_max(uint32_t m0, float* amax0, uint32_t m1, float* amax1,
+                                                 GridSyncSlot* slot) {
   __shared__ uint32_t red[2][8];
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
@@ -60,8 +66,17 @@ __device__ __forceinline__ void block_atomic_max(uint32_t m0, float* amax0, uint
       r0 = max(r0, red[0][w]);
       r1 = max(r1, red[1][w]);
     }
-    atomic_max_if_larger(r0, amax0);
-    if (amax1 != nullptr) atomic_max_if_larger(r1, amax1);
+    if (slot != nullptr) {
+      const uint32_t G = gridDim.x * gridDim.y, id = blockIdx.y * gridDim.x + blockIdx.x;
+      uint32_t t0 = 0u, t1 = 0u;
+      if (grid_max_arrive<DeviceOps>(slot, G, id, r0, r1, &t0, &t1)) {
+        DeviceOps::store_relaxed(reinterpret_cast<uint32_t*>(amax0), t0);
+        if (amax1 != nullptr) DeviceOps::store_relaxed(reinterpret_cast<uint32_t*>(amax1), t1);
+      }
+    } else {
+      atomic_max_if_larger(r0, amax0);
+      if (amax1 != nullptr) atomic_max_if_larger(r1, amax1);
+    }
   }
 }
 
@@ -69,7 +84,7 @@ __device__ __forceinline__ void block_atomic_max(uint32_t m0, float* amax0, uint
 // thread takes UNROLL 16-byte chunks per round, contiguous across the block.
 template <typename T, int UNROLL>
 __global__ __launch_bounds__(256) void k_amax(const T* __restrict__ x, int64_t rows, int64_t cols,
-                                              int64_t ld, float* amax) {
+                                              int64_t ld, float* amax, GridSyncSlot* slot) {
   constexpr int EPC = 16 / sizeof(T);  // elements per 16-byte chunk
   const int64_t cpr = cols / EPC;       // chunks per row
   uint32_t m = 0u;
@@ -102,7 +117,7 @@ __global__ __launch_bounds__(256) void k_amax(const T* __restrict__ x, int64_t r
     }
   }
   if constexpr (sizeof(T) == 2) m <<= 16;
-  block_atomic_max(m, amax);
+  block_atomic_max(m, amax, 0u, nullptr, slot);
 }
 
 // ---------------------------------------------------------------------------
@@ -606,7 +621,7 @@ __device__ __forceinline__ void rht_amax_patch(const QuadTile<T>& t, uint32_t si
 template <typename T>
 __global__ __launch_bounds__(256) void k_rht_amax(const T* __restrict__ x, int64_t rows,
                                                   int64_t cols, int64_t ld, uint32_t sign_mask,
-                                                  float* amax, float* amax_plain) {
+                                                  float* amax, float* amax_plain, GridSyncSlot* slot) {
   const uint32_t quads = (uint32_t)(cols / 4);            // column quads per 16-token band
   const uint32_t units = (uint32_t)(rows / 16) * quads;   // patches (< 2^26: elements < 2^32)
   const uint32_t stride = gridDim.x * 256u;
@@ -631,7 +646,7 @@ __global__ __launch_bounds__(256) void k_rht_amax(const T* __restrict__ x, int64
   }
   // max |RN(u / 4)| = RN(max |u| / 4): rounding is monotone
   am = 0.25f * am;
-  block_atomic_max(__float_as_uint(am), amax, __float_as_uint(ap), amax_plain);
+  block_atomic_max(__float_as_uint(am), amax, __float_as_uint(ap), amax_plain, slot);
 }
 
 // 16 consecutive elements as loaded (bf16: two 16-byte words; fp32: four),
@@ -858,9 +873,13 @@ static int cu_count() {
   return n;
 }
 
+// Without an exchange slot for the stream (graph capture) the outputs are
+// cleared first and every workgroup maxes into them atomically.
 template <typename T>
 static hipError_t launch_amax(const void* x, int64_t rows, int64_t cols, int64_t ld, float* amax,
                               hipStream_t s) {
+  GridSyncSlot* slot = stream_sync_slot(s);
+  if (slot == nullptr) k_zero_amax<<<1, 64, 0, s>>>(amax, nullptr);
   constexpr int EPC = 16 / sizeof(T);
   constexpr int UNROLL = 8;
   if (ld == cols) {  // contiguous: one long row
@@ -880,7 +899,7 @@ static hipError_t launch_amax(const void* x, int64_t rows, int64_t cols, int64_t
     const int64_t rounds = (units + 2047) / 2048;
     grid = dim3(grid_cap((units + rounds - 1) / rounds, 2048), grid_cap(rows, 65535));
   }
-  k_amax<T, UNROLL><<<grid, 256, 0, s>>>(static_cast<const T*>(x), rows, cols, ld, amax);
+  k_amax<T, UNROLL><<<grid, 256, 0, s>>>(static_cast<const T*>(x), rows, cols, ld, amax, slot);
   return hipGetLastError();
 }
 
@@ -938,7 +957,8 @@ static hipError_t launch_cast(const void* x, int dt, int64_t rows, int64_t cols,
 // RHT amax pass (plus the plain amax into amax_plain when it is not null).
 static hipError_t launch_rht_amax(const void* x, int dt, int64_t tokens, int64_t cols, int64_t ld,
                                   uint32_t sign_mask, float* amax, float* amax_plain, hipStream_t s) {
-  k_zero_amax<<<1, 64, 0, s>>>(amax, amax_plain);
+  GridSyncSlot* slot = stream_sync_slot(s);
+  if (slot == nullptr) k_zero_amax<<<1, 64, 0, s>>>(amax, amax_plain);
   // patches of 16 tokens x 4 columns; at most 2048 workgroups, rounds
   // balanced (capping the grid at the resident count was 1-5 % slower here)
   const int64_t units = (tokens / 16) * (cols / 4);
@@ -947,10 +967,10 @@ static hipError_t launch_rht_amax(const void* x, int dt, int64_t tokens, int64_t
   const unsigned grid = grid_cap((wgs + rounds - 1) / rounds, 2048);
   if (dt == 0)
     k_rht_amax<uint16_t><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(x), tokens, cols, ld,
-                                              sign_mask, amax, amax_plain);
+                                              sign_mask, amax, amax_plain, slot);
   else
     k_rht_amax<float><<<grid, 256, 0, s>>>(static_cast<const float*>(x), tokens, cols, ld, sign_mask,
-                                           amax, amax_plain);
+                                           amax, amax_plain, slot);
   return hipGetLastError();
 }
 
@@ -982,7 +1002,6 @@ hipError_t launch_quantize(const void* x, int dt, int64_t rows, int64_t cols, in
                                           tensor_scale, amax, s, &done);
     if (e != hipSuccess || done) return e;
   }
-  k_zero_amax<<<1, 64, 0, s>>>(amax, nullptr);
   hipError_t e = dt == 0 ? launch_amax<uint16_t>(x, rows, cols, ld, amax, s)
                          : launch_amax<float>(x, rows, cols, ld, amax, s);
   if (e != hipSuccess) return e;

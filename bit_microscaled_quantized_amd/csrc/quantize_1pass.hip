@@ -27,46 +27,13 @@
 #include <mutex>
 
 #include "grid_sync.hpp"
+#include "sync_ops.hpp"
 #include "nvfp4_device.hpp"
 #include "nvfp4_launch.hpp"
 
 namespace nvfp4 {
 
 namespace {
-
-// Device-scope atomics for the exchange.  It communicates only through the
-// slot's atomics and device-coherent loads and stores, which gfx950 performs
-// at the device's coherence point (past the per-XCD L2), so release and
-// acquire need no cache maintenance: release waits until this wave's earlier
-// memory operations have been performed (s_waitcnt), acquire keeps the
-// compiler from moving the following loads above the one that observed the
-// flag.  Agent-scope C++ fences would instead write back and invalidate the
-// XCD's whole L2 in every workgroup, stalling the loads of the others on that
-// XCD (measured: 80 instead of 19 us of load phase on an 84 MB tensor).
-struct DeviceOps {
-  static __device__ void drain() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-  static __device__ void max_relaxed(uint32_t* p, uint32_t v) {
-    __hip_atomic_fetch_max(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  static __device__ uint32_t add_release(uint32_t* p, uint32_t v) {
-    drain();
-    const uint32_t old = __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    drain();
-    return old;
-  }
-  static __device__ uint32_t load_relaxed(uint32_t* p) {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  static __device__ void store_relaxed(uint32_t* p, uint32_t v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  static __device__ void store_release(uint32_t* p, uint32_t v) {
-    drain();
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  static __device__ void fence_acquire() { asm volatile("" ::: "memory"); }
-  static __device__ void pause() { __builtin_amdgcn_s_sleep(8); }
-};
 
 // Exchange slots, one per (device, stream) in use: calls on one stream run in
 // order, so a slot is never used by two launches at once.  Each device holds
@@ -323,6 +290,20 @@ int slot_of(int dev, void* stream) {
 }
 
 }  // namespace
+
+// The exchange slot of (current device, stream) for the amax passes of the
+// two-pass path, or nullptr (stream under graph capture, set-up failed, or
+// all slots of the device taken by other streams).
+GridSyncSlot* stream_sync_slot(hipStream_t s) {
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &cap) != hipSuccess || cap != hipStreamCaptureStatusNone) return nullptr;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_mu);
+  if (!device_setup(dev)) return nullptr;
+  const int i = slot_of(dev, s);
+  return i < 0 ? nullptr : g_slots[dev] + i;
+}
 
 // Try the single-pass row-1D quantization; *done = false (and nothing
 // enqueued) when it does not apply: strided rows, a tensor larger than the

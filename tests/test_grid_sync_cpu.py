@@ -14,7 +14,11 @@ at its idle state for the next launch on it.
   that wait past the spin limit give up and are counted, the last one to
   leave covers their blocks, and the next launch on the slot runs clean;
 * a spin limit of zero: only workgroups that arrive after the result is
-  published pass; the rest are covered.
+  published pass; the rest are covered;
+* the no-wait grid maximum of the two-pass amax kernels (two maxima per
+  workgroup, any residency): exactly one workgroup, the last to arrive, gets
+  both exact maxima, and the slot is idle after it, interleaved on the same
+  slot with single-pass launches as on one stream.
 
 The same program is also built with ThreadSanitizer to check that the
 protocol has no data race."""
@@ -71,8 +75,8 @@ static int fails = 0;
 
 static bool idle(const GridSyncSlot* s) {
   for (uint32_t g = 0; g < nvfp4::kSyncGroups; g++)
-    if (s->group[g].arrive || s->group[g].amax || s->group[g].depart) return false;
-  return !s->top.arrive && !s->top.amax && !s->top.depart && !s->gave_up_n;
+    if (s->group[g].arrive || s->group[g].amax || s->group[g].depart || s->group[g].amax2) return false;
+  return !s->top.arrive && !s->top.amax && !s->top.depart && !s->top.amax2 && !s->gave_up_n;
 }
 
 // one launch of G workgroups; returns how many gave up
@@ -123,6 +127,43 @@ static int launch(GridSyncSlot* s, uint32_t epoch, int G, int resident, uint64_t
   return gave_up;
 }
 
+// one two-pass amax launch of G workgroups, at most `resident` at once
+static void max_launch(GridSyncSlot* s, int G, int resident, std::mt19937& rng) {
+  std::vector<uint32_t> v0(G), v1(G);
+  uint32_t w0 = 0, w1 = 0;
+  for (int i = 0; i < G; i++) {
+    v0[i] = rng() >> 1;
+    v1[i] = (rng() >> 1) & (rng() % 2 ? 0x7FFFFFFFu : 0xFFFFu);
+    w0 = v0[i] > w0 ? v0[i] : w0;
+    w1 = v1[i] > w1 ? v1[i] : w1;
+  }
+  std::vector<int> delay(G);
+  for (int i = 0; i < G; i++) delay[i] = (int)(rng() % 100);
+  std::mutex mu;
+  int lasts = 0;
+  uint32_t r0 = 0, r1 = 0;
+  Residency res(resident);
+  std::vector<std::thread> th;
+  for (int i = 0; i < G; i++)
+    th.emplace_back([&, i] {
+      res.enter();
+      std::this_thread::sleep_for(std::chrono::microseconds(delay[i]));
+      uint32_t a = 0, b = 0;
+      if (nvfp4::grid_max_arrive<CpuOps>(s, (uint32_t)G, (uint32_t)i, v0[i], v1[i], &a, &b)) {
+        std::lock_guard<std::mutex> l(mu);
+        lasts++;
+        r0 = a;
+        r1 = b;
+      }
+      res.leave();
+    });
+  for (auto& t : th) t.join();
+  CHECK(lasts == 1);
+  CHECK(r0 == w0);
+  CHECK(r1 == w1);
+  CHECK(idle(s));
+}
+
 int main() {
   std::mt19937 rng(1234);
   static GridSyncSlot slot;  // zero-initialized, as the device array
@@ -147,6 +188,14 @@ int main() {
   }
   // spin limit zero, full residency
   for (int rep = 0; rep < 20 && !fails; rep++) launch(&slot, ++epoch, 24, 24, 0, rng);
+  // no-wait grid maxima, alternating with single-pass launches on the slot
+  const int Ms[] = {1, 2, 15, 16, 17, 31, 100, 300};
+  for (int rep = 0; rep < 8 && !fails; rep++)
+    for (int G : Ms) {
+      max_launch(&slot, G, rep % 2 ? 4 : G, rng);
+      CHECK(launch(&slot, ++epoch, 20, 20, uint64_t(1) << 22, rng) == 0);
+      if (fails) break;
+    }
   std::printf("%s\n", fails ? "FAILED" : "OK");
   return fails ? 1 : 0;
 }
