@@ -474,57 +474,53 @@ __global__ __launch_bounds__(256) void k_cast_col1d(const T* __restrict__ x, int
 // tile mapping.  The row block of 16 columns spans the lane pair (co, co^1):
 // each lane holds 8 of its values, one shuffle combines the two half maxima,
 // and each lane encodes its 8 values (4 code bytes per row).
-template <typename T, int RR, int RH>
-__global__ __launch_bounds__(256) void k_cast_row_rht(
-    const T* __restrict__ x, int64_t rows, int64_t cols, int64_t ld, uint32_t sign_mask,
-    const float* __restrict__ row_amax, uint8_t* __restrict__ row_codes,
-    uint8_t* __restrict__ row_scales, float* __restrict__ row_ts, uint32_t row_key,
-    const float* __restrict__ rht_amax, uint8_t* __restrict__ rht_codes,
-    uint8_t* __restrict__ rht_scales, float* __restrict__ rht_ts, uint32_t rht_key) {
-  __shared__ __align__(16) uint8_t lcodes[kColCols][kColTok / 2];
-  __shared__ __align__(16) uint8_t lscales[kColCols][kColTok / 16];
-  __shared__ float rtab_row[128];
-  __shared__ float rtab_rht[128];
-  const float s_row = encode_scale(row_amax[0]);
-  const float s_rht = encode_scale(rht_amax[0]);
-  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
-    row_ts[0] = 1.0f / s_row;
-    rht_ts[0] = 1.0f / s_rht;
-  }
-  if (threadIdx.x < 128)
-    rtab_row[threadIdx.x] = element_scale(threadIdx.x, s_row);
-  else
-    rtab_rht[threadIdx.x - 128] = element_scale(threadIdx.x - 128, s_rht);
-  __syncthreads();
+struct RowRhtArgs {
+  int64_t rows, cols, ld;
+  uint32_t sign_mask;
+  uint8_t* row_codes;
+  uint8_t* row_scales;
+  uint32_t row_key;
+  uint8_t* rht_codes;
+  uint8_t* rht_scales;
+  uint32_t rht_key;
+};
 
-  // XCD-aware tile order: the hardware deals workgroups round-robin over the
-  // 8 XCDs, so each XCD takes a contiguous range of tiles instead.  The two
-  // tiles that write the two halves of each row-copy line then run on the
-  // same XCD one after the other, and their halves meet in its L2.
-  const uint32_t G = gridDim.x * gridDim.y;
-  const uint32_t bid = blockIdx.y * gridDim.x + blockIdx.x;
-  const uint32_t xcd = bid & 7u, per = G >> 3, rem = G & 7u;
-  const uint32_t id = xcd < rem ? xcd * (per + 1) + (bid >> 3) : rem * (per + 1) + (xcd - rem) * per + (bid >> 3);
-  const int64_t t0 = (int64_t)(id / gridDim.x) * kColTok;
-  const int64_t c0 = (int64_t)(id % gridDim.x) * kColCols;
+// Where this thread's 16 x 8 patch of tile `id` (row-major over the
+// 256-token x 128-column tiles) starts, and whether it lies in the tensor.
+// The lane pair (co, co^1) agrees on validity (cols % 16 == 0); an invalid
+// thread loads the first patch instead (in bounds) and stores nothing.
+template <typename T>
+__device__ __forceinline__ const T* row_rht_patch(const T* x, const RowRhtArgs& a, uint32_t id,
+                                                  uint32_t tiles_x, bool& valid) {
+  const int64_t tg = (int64_t)(id / tiles_x) * kColTok + 16 * ((int)threadIdx.x / kColOct);
+  const int64_t cc = (int64_t)(id % tiles_x) * kColCols + 8 * ((int)threadIdx.x % kColOct);
+  valid = tg < a.rows && cc < a.cols;
+  return valid ? x + tg * a.ld + cc : x;
+}
+
+// Both encodings of one loaded tile.  Ends with every thread past its LDS
+// reads, so the next tile may reuse the staging arrays.
+template <typename T, int RR, int RH>
+__device__ __forceinline__ void row_rht_tile(ColTile<T>& tile, bool valid, uint32_t id,
+                                             uint32_t tiles_x, const RowRhtArgs& a, float s_row,
+                                             float s_rht, const float* rtab_row,
+                                             const float* rtab_rht,
+                                             uint8_t (*lcodes)[kColTok / 2],
+                                             uint8_t (*lscales)[kColTok / 16]) {
+  const int64_t t0 = (int64_t)(id / tiles_x) * kColTok;
+  const int64_t c0 = (int64_t)(id % tiles_x) * kColCols;
   const int co = (int)threadIdx.x % kColOct;
   const int g = (int)threadIdx.x / kColOct;
   const int64_t tg = t0 + 16 * g;
   const int64_t cc = c0 + 8 * co;
-  // the lane pair (co, co^1) agrees on validity (cols % 16 == 0); an invalid
-  // thread loads the first patch instead (in bounds) and stores nothing
-  const bool valid = tg < rows && cc < cols;
-
-  ColTile<T> tile;
-  tile.load(valid ? x + tg * ld + cc : x, ld);
 
   // row copy: rows tg .. tg + 15, columns cc .. cc + 7 of this lane; the
   // output addresses and the hash index step by one row per iteration
-  const int64_t rbytes = cols / 2, rscales = cols / 16;
-  uint8_t* crow = row_codes + tg * rbytes + cc / 2;
-  uint8_t* srow = row_scales + tg * rscales + cc / 16;
-  uint32_t pair = (uint32_t)(tg * cols + cc) >> 1;  // elements < 2^32 (host check)
-  const uint32_t pair_step = (uint32_t)cols >> 1;
+  const int64_t rbytes = a.cols / 2, rscales = a.cols / 16;
+  uint8_t* crow = a.row_codes + tg * rbytes + cc / 2;
+  uint8_t* srow = a.row_scales + tg * rscales + cc / 16;
+  uint32_t pair = (uint32_t)(tg * a.cols + cc) >> 1;  // elements < 2^32 (host check)
+  const uint32_t pair_step = (uint32_t)a.cols >> 1;
 #pragma unroll
   for (int j = 0; j < 16; j++) {
     float v[8];
@@ -539,7 +535,7 @@ __global__ __launch_bounds__(256) void k_cast_row_rht(
     float sv[8];
 #pragma unroll
     for (int e = 0; e < 8; e++) sv[e] = v[e] * r_b;
-    const uint32_t w = encode8<RR>(sv, row_key, pair);
+    const uint32_t w = encode8<RR>(sv, a.row_key, pair);
     if (valid) {
       st_nt(crow, w);
       if ((co & 1) == 0) *srow = (uint8_t)e_b;
@@ -553,10 +549,57 @@ __global__ __launch_bounds__(256) void k_cast_row_rht(
   // compiler converts them again one column at a time instead of keeping
   // the row copy's 128 converted values live (which costs ~50 VGPRs).
   tile.opaque();
-  col_encode_any<T, RH, true>(tile, rows, tg, cc, g, co, sign_mask, s_rht, rtab_rht, rht_key, lcodes,
-                              lscales);
+  col_encode_any<T, RH, true>(tile, a.rows, tg, cc, g, co, a.sign_mask, s_rht, rtab_rht, a.rht_key,
+                              lcodes, lscales);
   __syncthreads();
-  col_store(rows, cols, t0, c0, lcodes, lscales, rht_codes, rht_scales);
+  col_store(a.rows, a.cols, t0, c0, lcodes, lscales, a.rht_codes, a.rht_scales);
+  __syncthreads();
+}
+
+template <typename T>
+__device__ __forceinline__ void row_rht_prologue(const float* row_amax, const float* rht_amax,
+                                                 float* row_ts, float* rht_ts, float& s_row,
+                                                 float& s_rht, float* rtab_row, float* rtab_rht) {
+  s_row = encode_scale(row_amax[0]);
+  s_rht = encode_scale(rht_amax[0]);
+  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
+    row_ts[0] = 1.0f / s_row;
+    rht_ts[0] = 1.0f / s_rht;
+  }
+  if (threadIdx.x < 128)
+    rtab_row[threadIdx.x] = element_scale(threadIdx.x, s_row);
+  else
+    rtab_rht[threadIdx.x - 128] = element_scale(threadIdx.x - 128, s_rht);
+  __syncthreads();
+}
+
+// One tile per workgroup.  XCD-aware tile order: the hardware deals
+// workgroups round-robin over the 8 XCDs, so each XCD takes a contiguous
+// range of tiles instead.  The two tiles that write the two halves of each
+// row-copy line then run on the same XCD one after the other, and their
+// halves meet in its L2.
+template <typename T, int RR, int RH>
+__global__ __launch_bounds__(256) void k_cast_row_rht(const T* __restrict__ x, RowRhtArgs a,
+                                                      const float* __restrict__ row_amax,
+                                                      float* __restrict__ row_ts,
+                                                      const float* __restrict__ rht_amax,
+                                                      float* __restrict__ rht_ts) {
+  __shared__ __align__(16) uint8_t lcodes[kColCols][kColTok / 2];
+  __shared__ __align__(16) uint8_t lscales[kColCols][kColTok / 16];
+  __shared__ float rtab_row[128];
+  __shared__ float rtab_rht[128];
+  float s_row, s_rht;
+  row_rht_prologue<T>(row_amax, rht_amax, row_ts, rht_ts, s_row, s_rht, rtab_row, rtab_rht);
+
+  const uint32_t G = gridDim.x * gridDim.y;
+  const uint32_t bid = blockIdx.y * gridDim.x + blockIdx.x;
+  const uint32_t xcd = bid & 7u, per = G >> 3, rem = G & 7u;
+  const uint32_t id = xcd < rem ? xcd * (per + 1) + (bid >> 3) : rem * (per + 1) + (xcd - rem) * per + (bid >> 3);
+  bool valid;
+  ColTile<T> tile;
+  tile.load(row_rht_patch(x, a, id, gridDim.x, valid), a.ld);
+  row_rht_tile<T, RR, RH>(tile, valid, id, gridDim.x, a, s_row, s_rht, rtab_row, rtab_rht, lcodes,
+                          lscales);
 }
 
 // amax of the RHT output (and, if amax_plain is not null, of the input itself,
@@ -1031,17 +1074,18 @@ hipError_t launch_quantize_row_rht(const void* x, int dt, int64_t tokens, int64_
   hipError_t e = launch_rht_amax(x, dt, tokens, cols, ld, sign_mask, rht_amax, row_amax, s);
   if (e != hipSuccess) return e;
   // both casts from one read of x
-  dim3 grid((unsigned)((cols + kColCols - 1) / kColCols), (unsigned)((tokens + kColTok - 1) / kColTok));
-  const uint32_t row_key = sr_key(row_seed), rht_key = sr_key(rht_seed);
-#define ROW_RHT_LAUNCH(T, RR, RH)                                                                   \
-  k_cast_row_rht<T, RR, RH><<<grid, 256, 0, s>>>(static_cast<const T*>(x), tokens, cols, ld, sign_mask, \
-                                                 row_amax, row_codes, row_scales, row_ts, row_key,  \
-                                                 rht_amax, rht_codes, rht_scales, rht_ts, rht_key)
+  const uint32_t tiles_x = (uint32_t)((cols + kColCols - 1) / kColCols);
+  const uint32_t tiles_y = (uint32_t)((tokens + kColTok - 1) / kColTok);
+  const RowRhtArgs a{tokens, cols, ld, sign_mask, row_codes, row_scales, sr_key(row_seed),
+                     rht_codes, rht_scales, sr_key(rht_seed)};
+#define ROW_RHT_LAUNCH(T, RR, RH)                                                                 \
+  k_cast_row_rht<T, RR, RH><<<dim3(tiles_x, tiles_y), 256, 0, s>>>(static_cast<const T*>(x), a,   \
+                                                                row_amax, row_ts, rht_amax, rht_ts)
 #define ROW_RHT_RND(T)                                             \
   if (row_rnd == 0) {                                              \
-    if (rht_rnd == 0) ROW_RHT_LAUNCH(T, 0, 0); else ROW_RHT_LAUNCH(T, 0, 1); \
+    if (rht_rnd == 0) { ROW_RHT_LAUNCH(T, 0, 0); } else { ROW_RHT_LAUNCH(T, 0, 1); } \
   } else {                                                         \
-    if (rht_rnd == 0) ROW_RHT_LAUNCH(T, 1, 0); else ROW_RHT_LAUNCH(T, 1, 1); \
+    if (rht_rnd == 0) { ROW_RHT_LAUNCH(T, 1, 0); } else { ROW_RHT_LAUNCH(T, 1, 1); } \
   }
   if (dt == 0) {
     ROW_RHT_RND(uint16_t)
