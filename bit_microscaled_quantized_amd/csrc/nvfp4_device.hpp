@@ -25,17 +25,16 @@ __device__ __forceinline__ float encode_scale(float amax_t) {
   return fminf(2688.0f / amax_t, kFltMax);
 }
 
-// E4M3 code of sb >= 0: nearest finite value, ties to the even code,
-// saturating at 448 (0x7E).  Subnormal codes k * 2^-9 (k <= 8, code 8 being
-// the smallest normal 2^-6) come from rounding sb * 2^9 to an integer; normal
-// codes from rounding the FP32 mantissa to 3 bits.  Both are computed and one
-// is selected (no branches).
+// E4M3 code of sb >= 0: nearest finite value, ties to the even code.  The
+// gfx950 conversion to OCP E4M3 does it in one instruction: it equals the
+// nearest-even search (subnormal codes k * 2^-9 included) on every FP32
+// input up to 464, the rounding boundary above 448, and gives NaN beyond.
+// Inputs stay below 449 here: sb is RN(RN(amax_b / 6) * S_enc) with
+// amax_b <= amax_t and S_enc <= 2688 / amax_t.  The second element converted
+// is 0 and the upper half word is the zero passed in, so the result is the
+// code itself.
 __device__ __forceinline__ uint32_t e4m3_encode(float sb) {
-  const uint32_t b = __float_as_uint(sb);
-  const uint32_t r = b + 0x7FFFFu + ((b >> 20) & 1u);
-  const uint32_t normal = min((r >> 20) - (120u << 3), 0x7Eu);
-  const uint32_t sub = (uint32_t)__builtin_rintf(sb * 512.0f);
-  return __builtin_unpredictable(sb < 0.015625f) ? sub : normal;
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(sb, 0.0f, 0, false);
 }
 
 // Value of a finite non-negative E4M3 code.

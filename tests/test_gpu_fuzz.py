@@ -5,11 +5,13 @@
   layout (row-1D, column-1D, 2D with its transposed copy, RHT column, fused
   row + RHT), RNE and SR, bf16 and FP32, and four value distributions; codes,
   scales, tensor scale and amax bit for bit against the oracle.
-* Block-scale sweep: every FP32 block maximum in [0, 2688] (1.16e9 values) as
-  its own 16-element block [amax_b, 0, ..., 0] of an FP32 tensor whose amax is
-  2688, so S_enc = 1 and the device computes e_b = E4M3((amax_b / 6) * 1) for
-  every FP32 input of the division and the encoder up to the saturation point;
-  the scale bytes are compared with the oracle's nearest-even search."""
+* Block-scale sweeps: every FP32 block maximum in [0, amax_t] (over 1.1e9
+  values each) as its own 16-element block [amax_b, 0, ..., 0] of an FP32
+  tensor whose amax is amax_t, for amax_t = 2688 (S_enc = 1) and 1792
+  (S_enc = 1.5), so the device computes e_b = E4M3(RN(amax_b / 6) * S_enc)
+  for every FP32 input of the division and a wide cover of the encoder's
+  inputs up to the top code; the scale bytes are compared with the oracle's
+  nearest-even search."""
 import numpy as np
 import pytest
 
@@ -79,13 +81,19 @@ def test_shape_fuzz(ora, case):
         _same(g_rht, ora.rht_quantize(x, mask, 1 - rnd, seed + 1))
 
 
-def test_block_scale_every_fp32_amax_up_to_2688(ora):
+@pytest.mark.parametrize("amax_t", [2688.0, 1792.0])
+def test_block_scale_every_fp32_block_amax(ora, amax_t):
+    """Every FP32 block maximum in [0, amax_t] in its own block; amax_t = 2688
+    gives S_enc = 1 (e_b = E4M3(RN(amax_b / 6))) and 1792 gives S_enc = 1.5
+    (e_b = E4M3(RN(RN(amax_b / 6) * 1.5))), so between them the scale codes
+    of most FP32 inputs of the encoder up to 448 are seen."""
     torch = gpuio.torch_cuda()
-    top = int(np.float32(2688.0).view(np.uint32))  # inclusive
+    top = int(np.float32(amax_t).view(np.uint32))  # inclusive
+    s_enc = np.float32(2688.0) / np.float32(amax_t)
     chunk = 1 << 26
-    rows = chunk + 16  # the last 16 rows: one block holding 2688, the rest zero
+    rows = chunk + 16  # the last 16 rows: one block holding amax_t, the rest zero
     x = torch.zeros((rows, 16), dtype=torch.float32, device="cuda")
-    x[chunk, 0] = 2688.0
+    x[chunk, 0] = amax_t
     u8 = dict(dtype=torch.uint8, device="cuda")
     codes = torch.empty((rows, 8), **u8)
     scales = torch.empty((rows, 1), **u8)
@@ -100,11 +108,11 @@ def test_block_scale_every_fp32_amax_up_to_2688(ora):
         nv.nvfp4_quantize(x, nv.NVFP4_F32, rows, 16, 16, nv.NVFP4_ROW_1D, nv.NVFP4_RNE, 0, codes,
                           scales, None, None, ts, am)
         torch.cuda.synchronize()
-        assert float(am.item()) == 2688.0 and float(ts.item()) == 1.0
+        assert float(am.item()) == amax_t and np.float32(ts.item()) == np.float32(1.0) / s_enc
         got = scales[:n, 0].cpu().numpy()
         amax_b = np.arange(start, start + n, dtype=np.uint64).astype(np.uint32).view(np.float32)
-        want = ora.block_scale_array(amax_b, 1.0)
+        want = ora.block_scale_array(amax_b, float(s_enc))
         assert np.array_equal(got, want), gpuio.first_diff(got, want)
-        assert int(scales[chunk, 0].item()) == 0x7E  # 2688 / 6 = 448: the top code
+        assert int(scales[chunk, 0].item()) == 0x7E  # amax_t / 6 * S_enc = 448: the top code
         checked += n
     assert checked == top + 1
