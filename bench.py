@@ -27,6 +27,7 @@ and on all cores and its FP64 contraction.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
     python bench.py --summarize-trace <rocprofv3 kernel_trace.csv> [--steps K --warmup W]
+    python bench.py --summarize-pmc <rocprofv3 counter_collection.csv> ...
 """
 from __future__ import annotations
 
@@ -87,6 +88,9 @@ def parse():
     p.add_argument("--copy-probe-mib", type=int, default=0,
                    help="also run one plain device copy of this many MiB (calibrates "
                         "the FETCH_SIZE / WRITE_SIZE counters against known bytes)")
+    p.add_argument("--summarize-pmc", nargs="+", default=None,
+                   help="summarize rocprofv3 --pmc counter_collection CSVs of a "
+                        "--headline-only --copy-probe-mib 1024 run and exit")
     p.add_argument("--summarize-trace", default=None,
                    help="summarize a rocprofv3 kernel-trace CSV of a bench run instead of running")
     return p.parse_args()
@@ -578,11 +582,116 @@ def summarize_trace(path, steps, warmup):
         print(f"- {name}: {len(d)} launches, mean {np.mean(d):.1f} µs, median {np.median(d):.1f} µs")
 
 
+# ----------------------------------------------------------------- counter summary
+def _headline_labels():
+    """(short kernel name, workgroups) -> (label, algorithmic bytes read, written)
+    for the launches of one headline step on a 256-CU device; the Wgrad
+    figures average its beta = 0 launch and its three beta = 1 launches."""
+    T, I, O = S_CHUNK, S_IN, S_OUT
+
+    def q_out(rows, cols):  # codes + scales of one NVFP4 copy
+        return rows * cols // 2 + rows * cols // 16
+
+    def rht_amax_grid(tokens, cols):
+        units = (tokens // 16) * (cols // 4)
+        wgs = -(-units // 256)
+        rounds = -(-wgs // 2048)
+        return min(-(-wgs // rounds), 2048)
+
+    w_in, x_in, d_in = O * I * 2, T * I * 2, T * O * 2
+    wg_acc = 0.75 * O * I * 4
+    return {
+        ("k_amax<unsigned short, 8>", 1024): ("W amax (5120x20480)", w_in, 0),
+        ("k_cast_tile2d<unsigned short, 0>", (O // 256) * (I // 64)):
+            ("W 2D cast + transposed copy", w_in, 2 * q_out(O, I) - 2 * (O * I // 16) + 2 * (O * I // 256)),
+        ("k_rht_amax<unsigned short>", rht_amax_grid(T, I)): ("X RHT + plain amax (8192x20480)", x_in, 0),
+        ("k_cast_row_rht<unsigned short, 0, 0>", (I // 128) * (T // 256)):
+            ("X row + RHT column cast, RNE", x_in, 2 * q_out(T, I)),
+        ("k_rht_amax<unsigned short>", rht_amax_grid(T, O)): ("dY RHT + plain amax (8192x5120)", d_in, 0),
+        ("k_cast_row_rht<unsigned short, 1, 1>", (O // 128) * (T // 256)):
+            ("dY row + RHT column cast, SR", d_in, 2 * q_out(T, O)),
+        ("k_gemm_nvfp4<float>", 768): ("Fprop 8192x5120x20480", q_out(T, I) + O * I // 2 + O * I // 256,
+                                       T * O * 4),
+        ("k_gemm_nvfp4<float>", 2560): ("Dgrad 8192x20480x5120", q_out(T, O) + O * I // 2 + O * I // 256,
+                                        T * I * 4),
+        ("k_gemm_nvfp4<float>", 1792): ("Wgrad 5120x20480x8192 (3 of 4 with beta = 1)",
+                                        q_out(O, T) + q_out(I, T) + wg_acc, O * I * 4),
+    }
+
+
+def summarize_pmc(paths):
+    """Markdown summary of rocprofv3 --pmc counter_collection CSVs of
+    `bench.py --headline-only --copy-probe-mib 1024`: per kernel and grid the
+    mean counter values per dispatch; FETCH_SIZE / WRITE_SIZE scaled by what
+    they read for the copy probe (reads and writes 1 GiB) and set against the
+    launch's algorithmic bytes; VALU instructions per element for the
+    quantize kernels."""
+    groups = {}
+    for path in paths:
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                wgs = int(r["Grid_Size"]) // max(int(r["Workgroup_Size"]), 1)
+                key = (_kernel_short(r["Kernel_Name"]), wgs)
+                g = groups.setdefault(key, {})
+                g.setdefault(r["Counter_Name"], {})[r["Dispatch_Id"]] = float(r["Counter_Value"])
+    probe = [g for (k, _), g in groups.items() if "neg_kernel" in k]
+    gib_kib = float(1 << 20)
+    fetch_f = write_f = None
+    if probe:
+        if "FETCH_SIZE" in probe[0]:
+            fetch_f = gib_kib / np.mean(list(probe[0]["FETCH_SIZE"].values()))
+        if "WRITE_SIZE" in probe[0]:
+            write_f = gib_kib / np.mean(list(probe[0]["WRITE_SIZE"].values()))
+    print("Calibration (copy probe: 1 GiB read, 1 GiB written): "
+          f"FETCH_SIZE factor {fetch_f if fetch_f is None else round(fetch_f, 3)}, "
+          f"WRITE_SIZE factor {write_f if write_f is None else round(write_f, 3)}\n")
+    labels = _headline_labels()
+    elems = {"W": S_OUT * S_IN, "X": S_CHUNK * S_IN, "dY": S_CHUNK * S_OUT}
+    print("| kernel | workgroups | launch | dispatches | FETCH KiB | WRITE KiB | HBM MB read / written "
+          "| algorithmic MB read / written | HBM / algorithmic | VALU per element |")
+    print("|---|---:|---|---:|---:|---:|---:|---:|---:|---:|")
+    gemm_bytes, gemm_n = 0.0, 0
+    for (k, wgs), g in sorted(groups.items(), key=lambda kv: (kv[0][0], kv[0][1])):
+        if not (k.startswith("k_") or "neg_kernel" in k):
+            continue
+        n = max(len(v) for v in g.values())
+        fk = np.mean(list(g["FETCH_SIZE"].values())) if "FETCH_SIZE" in g else None
+        wk = np.mean(list(g["WRITE_SIZE"].values())) if "WRITE_SIZE" in g else None
+        rd = fk * 1024 * fetch_f if fk is not None and fetch_f else None
+        wr = wk * 1024 * write_f if wk is not None and write_f else None
+        lab, ar, aw = labels.get((k, wgs), ("", None, None))
+        ratio = ""
+        if rd is not None and wr is not None and ar is not None:
+            ratio = f"{(rd + wr) / (ar + aw):.2f}"
+            if k == GEMM_KERNEL:
+                gemm_bytes += (rd + wr) * n
+                gemm_n += n
+        valu = ""
+        if "SQ_INSTS_VALU" in g and lab[:2] in ("W ", "X ", "dY"):
+            e = elems[lab.split()[0]]
+            valu = f"{np.mean(list(g['SQ_INSTS_VALU'].values())) * 64 / e:.1f}"
+        f = lambda v, d=0: "" if v is None else f"{v:.{d}f}"
+        amb = "" if ar is None else f"{ar / 1e6:.1f} / {aw / 1e6:.1f}"
+        hbm = "" if rd is None or wr is None else f"{rd / 1e6:.1f} / {wr / 1e6:.1f}"
+        print(f"| `{k}` | {wgs} | {lab} | {n} | {f(fk)} | {f(wk)} | {hbm} | {amb} | {ratio} | {valu} |")
+    if gemm_n:
+        print(f"\n`{GEMM_KERNEL}`: mean HBM bytes per launch over {gemm_n} headline launches: "
+              f"{gemm_bytes / gemm_n:.4e} (sources sha256 {gemm_src_sha()})")
+    sq = [(k, g) for k, g in groups.items() if k[0] == GEMM_KERNEL and "SQ_INSTS_MFMA" in g]
+    for (k, wgs), g in sq:
+        m = {c: np.mean(list(v.values())) for c, v in g.items()}
+        line = ", ".join(f"{c} {v:.4g}" for c, v in sorted(m.items()))
+        print(f"- `{k}` {wgs} workgroups ({labels.get((k, wgs), ('',))[0]}): {line}")
+
+
 # ----------------------------------------------------------------- main
 def main():
     args = parse()
     if args.summarize_trace:
         summarize_trace(args.summarize_trace, args.steps, args.warmup)
+        return
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "

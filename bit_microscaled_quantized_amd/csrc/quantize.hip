@@ -815,14 +815,14 @@ __global__ __launch_bounds__(256) void k_cast_tile2d(const T* __restrict__ x, in
                                                      uint8_t* __restrict__ scales_t,
                                                      float* __restrict__ tensor_scale, uint32_t key) {
   __shared__ __align__(16) uint8_t lt[64][128];  // [local column][packed codes of the 256 rows]
+  __shared__ __align__(16) uint8_t lsc[16][4];   // [tile row][tile column] scale codes
   __shared__ float rtab[128];
   const float s_enc = encode_scale(amax[0]);
   if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) tensor_scale[0] = 1.0f / s_enc;
   fill_scale_table(rtab, s_enc);
   __syncthreads();
 
-  // consecutive workgroups take consecutive row regions of one column strip,
-  // so the transposed rows they write are contiguous in codes_t
+  // consecutive workgroups take consecutive row regions of one column strip
   const int64_t r0 = (int64_t)blockIdx.x * 256;
   const int64_t c0 = (int64_t)blockIdx.y * 64;
   const int wave = threadIdx.x >> 6;
@@ -861,13 +861,8 @@ __global__ __launch_bounds__(256) void k_cast_tile2d(const T* __restrict__ x, in
     for (int e = 0; e < 16; e++) sv[e] = v[e] * r_b;
     const uint2 w = encode16<RND>(sv, key, (uint32_t)(r * cols + c) >> 1);
     uint32_t w0 = w.x, w1 = w.y;
-    if (tile_valid) {
-      *reinterpret_cast<uint2*>(codes + r * (cols / 2) + c / 2) = make_uint2(w0, w1);
-      if (rr == 0) {
-        scales[(r / 16) * (cols / 16) + c / 16] = (uint8_t)e_b;
-        if (scales_t) scales_t[(c / 16) * (rows / 16) + r / 16] = (uint8_t)e_b;
-      }
-    }
+    if (tile_valid) *reinterpret_cast<uint2*>(codes + r * (cols / 2) + c / 2) = make_uint2(w0, w1);
+    if (rr == 0) lsc[tr][tc] = (uint8_t)e_b;  // stored below, where the tile is in the tensor
     if (codes_t != nullptr) {
       // every lane of the wave takes part in the exchange (an invalid tile's
       // codes land in staging slots that are never stored)
@@ -876,24 +871,60 @@ __global__ __launch_bounds__(256) void k_cast_tile2d(const T* __restrict__ x, in
       *reinterpret_cast<uint2*>(&lt[16 * tc + rr][8 * tr]) = make_uint2(w0, w1);
     }
   }
-  if (codes_t == nullptr) return;
   __syncthreads();
+  // Scale codes from LDS in whole pieces (single bytes from every tile would
+  // each leave the L2 as a partial write): a row of `scales` gets the
+  // region's 4 codes as one dword, a row of `scales_t` its 16 as 16 bytes.
+  {
+    const int64_t nr = rows / 16, nc = cols / 16, br0 = r0 / 16, bc0 = c0 / 16;
+    const int t = (int)threadIdx.x;
+    if (t < 16 && br0 + t < nr) {
+      uint8_t* dst = scales + (br0 + t) * nc + bc0;
+      const int n = (int)min((int64_t)4, nc - bc0);
+      if (n == 4 && (((br0 + t) * nc + bc0) & 3) == 0) {
+        *reinterpret_cast<uint32_t*>(dst) = *reinterpret_cast<const uint32_t*>(lsc[t]);
+      } else {
+        for (int k = 0; k < n; k++) dst[k] = lsc[t][k];
+      }
+    } else if (scales_t != nullptr && t >= 64 && t < 68 && bc0 + (t - 64) < nc) {
+      const int q = t - 64;
+      uint8_t* dst = scales_t + (bc0 + q) * nr + br0;
+      const int n = (int)min((int64_t)16, nr - br0);
+      uint32_t wv[4];
+#pragma unroll
+      for (int k = 0; k < 4; k++)
+        wv[k] = (uint32_t)lsc[4 * k][q] | ((uint32_t)lsc[4 * k + 1][q] << 8) |
+                ((uint32_t)lsc[4 * k + 2][q] << 16) | ((uint32_t)lsc[4 * k + 3][q] << 24);
+      if (n == 16 && (((bc0 + q) * nr + br0) & 15) == 0) {
+        *reinterpret_cast<uint4*>(dst) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+      } else {
+        for (int k = 0; k < n; k++) dst[k] = (uint8_t)(wv[k >> 2] >> (8 * (k & 3)));
+      }
+    }
+  }
+  if (codes_t == nullptr) return;
   // codes_t: 64 rows (local columns) of up to 128 bytes; 4 threads per row,
-  // 32 bytes each, so each row's line is written by one wave
+  // each storing 16-byte pieces q and q + 4, so each store instruction covers
+  // 64 contiguous bytes of a row (non-temporal stores are not merged in L2:
+  // pieces with gaps between them would each leave as a partial write)
   const int lc = threadIdx.x >> 2;
   const int q = threadIdx.x & 3;
   const int64_t ct = c0 + lc;
   if (ct >= cols) return;
   const int64_t row_bytes = rows / 2;
-  const int64_t off = r0 / 2 + 32 * q;  // byte offset in the output row
-  uint8_t* dst = codes_t + ct * row_bytes + off;
-  const uint8_t* src = &lt[lc][32 * q];
-  if (off + 32 <= row_bytes && ((ct * row_bytes + off) & 15) == 0) {
-    st_nt(dst, reinterpret_cast<const uint4*>(src)[0]);
-    st_nt(dst + 16, reinterpret_cast<const uint4*>(src)[1]);
-  } else {
-    for (int k = 0; k < 4 && off + 8 * k < row_bytes; k++)
-      st_nt(dst + 8 * k, reinterpret_cast<const uint2*>(src)[k]);
+#pragma unroll
+  for (int k = 0; k < 2; k++) {
+    const int piece = 4 * k + q;
+    const int64_t off = r0 / 2 + 16 * piece;  // byte offset in the output row
+    if (off >= row_bytes) break;
+    uint8_t* dst = codes_t + ct * row_bytes + off;
+    const uint8_t* src = &lt[lc][16 * piece];
+    if (off + 16 <= row_bytes && ((ct * row_bytes + off) & 15) == 0) {
+      st_nt(dst, *reinterpret_cast<const uint4*>(src));
+    } else {  // row_bytes is a multiple of 8
+      st_nt(dst, reinterpret_cast<const uint2*>(src)[0]);
+      if (off + 16 <= row_bytes) st_nt(dst + 8, reinterpret_cast<const uint2*>(src)[1]);
+    }
   }
 }
 
