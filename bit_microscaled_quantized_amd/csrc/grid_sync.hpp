@@ -9,26 +9,34 @@
 // line) and only the last workgroup of each group touches the top line.
 //
 // One launch (epoch e, a nonzero number the host makes unique per slot):
-//   arrive : w maxes its amax into its group's `amax`, then adds 1 to the
-//            group's `arrive` (after its max is performed).  The group's last
-//            arriver reads the group max, resets the group's fields, maxes it
-//            into the top `amax` and adds 1 to the top `arrive`; the last
-//            group arriver reads the tensor amax, resets the top, publishes
-//            it in `result` and sets `done` = e.
-//   wait   : every workgroup polls `done` == e, at most spin_limit polls.  One
-//            that gives up records its index in `gave_up_list` and counts in
-//            `gave_ups` (a running total the host can read).
-//   depart : after encoding its own blocks (or giving up), w adds 1 to its
-//            group's `depart`; the group's last departer adds 1 to the top
-//            `depart`; the last one overall has seen every workgroup arrive
-//            and leave, so `result` is final and the give-up list complete:
-//            it encodes the blocks of the workgroups that gave up (from
-//            memory), writes the tensor-level outputs, and clears the list.
+//   arrive  : w maxes its amax into its group's `amax`, then adds 1 to the
+//             group's `arrive` (after its max is performed).  The group's
+//             last arriver reads the group max, resets the group's fields,
+//             maxes it into the top `amax` and adds 1 to the top `arrive`;
+//             the last group arriver -- the publisher -- reads the tensor
+//             amax, resets the top, stores it in `result`, closes the gate
+//             (below) and sets `done` = e.
+//   wait    : every other workgroup polls `done` == e, at most spin_limit
+//             polls, then tries to give up through the gate.
+//   gate    : one word, [epoch bits 31:14 | closed bit 13 | count 12:0].  A
+//             workgroup gives up by a compare-and-swap that adds 1 to the
+//             count of this epoch's open gate (a word of another epoch reads
+//             as open with count 0); the count before its swap is its index
+//             in `gave_up_list`, where it then stores w + 1, and it leaves
+//             without encoding.  The publisher closes the gate by a
+//             compare-and-swap that sets the closed bit; the count it closes
+//             on is exactly the number of workgroups that gave up, since no
+//             swap can add to a closed gate: a workgroup whose swap fails on
+//             a closed gate reads `result` and goes on normally.
+//   recover : after its own blocks, the publisher encodes the blocks of the
+//             workgroups in gave_up_list[0 .. count) (from memory; it waits
+//             for each entry to be stored) and clears those entries.
 // So a launch whose grid is not all resident at once never hangs and never
 // leaves outputs unwritten: workgroups that wait too long leave their blocks
-// to the last one, which runs after all have arrived.  Every field the next
-// launch on the slot relies on is back at zero when the launch ends (`done`
-// is compared with the epoch, so it needs no reset).
+// to the publisher, which runs after all have arrived.  No workgroup has to
+// wait for the others to finish.  When the launch ends, the lines and the
+// list are back at zero; `done` and the gate carry the epoch, so they need
+// no reset.
 #pragma once
 
 #include <stdint.h>
@@ -41,8 +49,8 @@ constexpr uint32_t kSyncMaxGrid = 4096;  // workgroups per launch
 struct alignas(128) SyncLine {
   uint32_t arrive;
   uint32_t amax;  // FP32 bits of a non-negative maximum (integer order = float order)
-  uint32_t depart;
-  uint32_t amax2;  // a second maximum (grid_max_arrive)
+  uint32_t depart;  // unused (kept zero)
+  uint32_t amax2;   // a second maximum (grid_max_arrive)
   uint32_t pad[28];
 };
 
@@ -51,15 +59,27 @@ struct GridSyncSlot {
   SyncLine top;
   alignas(128) uint32_t done;  // epoch of the last published result
   uint32_t result;             // tensor amax bits of that epoch
-  alignas(128) uint32_t gave_up_n;   // workgroups of this launch in gave_up_list
-  uint32_t gave_ups;                 // running total over all launches
-  alignas(128) uint32_t gave_up_list[kSyncMaxGrid];
+  alignas(128) uint32_t gate;  // [epoch 31:14 | closed 13 | count 12:0]
+  uint32_t gave_ups;           // running total over all launches
+  alignas(128) uint32_t gave_up_list[kSyncMaxGrid];  // w + 1, 0 = empty
 };
+
+constexpr uint32_t kGateClosed = 1u << 13;
+constexpr uint32_t kGateCount = kGateClosed - 1u;
+
+__host__ __device__ inline uint32_t gate_tag(uint32_t epoch) { return epoch << 14; }
+
+// This epoch's view of a gate word: another epoch's word is an open gate
+// with count 0.
+__host__ __device__ inline uint32_t gate_view(uint32_t g, uint32_t epoch) {
+  return (g & ~(kGateClosed | kGateCount)) == gate_tag(epoch) ? g : gate_tag(epoch);
+}
 
 // Ops (all device-scope):
 //   static void max_relaxed(uint32_t* p, uint32_t v);
 //   static uint32_t add_release(uint32_t* p, uint32_t v);  // after this thread's earlier
 //                                                          // atomics; returns the old value
+//   static bool cas_release(uint32_t* p, uint32_t& expected, uint32_t desired);
 //   static uint32_t load_relaxed(uint32_t* p);
 //   static void store_release(uint32_t* p, uint32_t v);   // after earlier atomics
 //   static void store_relaxed(uint32_t* p, uint32_t v);
@@ -74,13 +94,19 @@ __host__ __device__ inline uint32_t sync_groups_used(uint32_t G) {
   return G < kSyncGroups ? G : kSyncGroups;
 }
 
-// Arrive with this workgroup's maximum and wait for the tensor amax.  Called
-// by one thread per workgroup.  True: *amax_bits holds the tensor amax.
-// False: the workgroup gave up (recorded); it must not write its outputs.
+enum GridRole : uint32_t { kGridWaited = 0, kGridGaveUp = 1, kGridPublisher = 2 };
+
+// Arrive with this workgroup's maximum and obtain the tensor amax.  Called by
+// one thread per workgroup.  kGridWaited / kGridPublisher: *amax_bits holds
+// the tensor amax and the workgroup encodes its blocks; the publisher then
+// also covers the *recover workgroups in gave_up_list (grid_recovered) and
+// writes the tensor-level outputs.  kGridGaveUp: recorded; the workgroup
+// must not write its outputs.
 template <typename Ops>
-__host__ __device__ inline bool grid_arrive_wait(GridSyncSlot* s, uint32_t G, uint32_t w,
-                                                 uint32_t my_max, uint32_t epoch,
-                                                 uint64_t spin_limit, uint32_t* amax_bits) {
+__host__ __device__ inline GridRole grid_arrive_wait(GridSyncSlot* s, uint32_t G, uint32_t w,
+                                                     uint32_t my_max, uint32_t epoch,
+                                                     uint64_t spin_limit, uint32_t* amax_bits,
+                                                     uint32_t* recover) {
   const uint32_t g = w % kSyncGroups;
   SyncLine* gl = &s->group[g];
   Ops::max_relaxed(&gl->amax, my_max);
@@ -97,51 +123,56 @@ __host__ __device__ inline bool grid_arrive_wait(GridSyncSlot* s, uint32_t G, ui
       Ops::store_relaxed(&s->top.amax, 0u);
       Ops::store_relaxed(&s->top.arrive, 0u);
       Ops::store_relaxed(&s->result, tm);
+      uint32_t cur = Ops::load_relaxed(&s->gate);
+      for (;;) {
+        const uint32_t v = gate_view(cur, epoch);
+        if (Ops::cas_release(&s->gate, cur, v | kGateClosed)) {
+          *recover = v & kGateCount;
+          break;
+        }
+      }
       Ops::store_release(&s->done, epoch);
+      *amax_bits = tm;
+      return kGridPublisher;
     }
   }
+  *recover = 0u;
   for (uint64_t n = 0;; n++) {
-    if (Ops::load_relaxed(&s->done) == epoch) {
-      Ops::fence_acquire();
-      *amax_bits = Ops::load_relaxed(&s->result);
-      return true;
+    if (Ops::load_relaxed(&s->done) == epoch) break;
+    if (n >= spin_limit) {
+      uint32_t cur = Ops::load_relaxed(&s->gate);
+      for (;;) {
+        const uint32_t v = gate_view(cur, epoch);
+        if (v & kGateClosed) break;  // published meanwhile: result is stored
+        if (Ops::cas_release(&s->gate, cur, v + 1u)) {
+          Ops::store_release(&s->gave_up_list[v & kGateCount], w + 1u);
+          Ops::add_release(&s->gave_ups, 1u);
+          return kGridGaveUp;
+        }
+      }
+      break;
     }
-    if (n >= spin_limit) break;
     Ops::pause();
   }
-  const uint32_t i = Ops::add_release(&s->gave_up_n, 1u);
-  Ops::store_relaxed(&s->gave_up_list[i], w);
-  Ops::add_release(&s->gave_ups, 1u);
-  return false;
-}
-
-// Leave the launch (after this workgroup's own encoding, or after giving up).
-// True for the last workgroup to leave: it must then call grid_recover_list
-// to learn which workgroups gave up, encode their blocks, write the tensor
-// outputs, and call grid_finish.
-template <typename Ops>
-__host__ __device__ inline bool grid_depart(GridSyncSlot* s, uint32_t G, uint32_t w) {
-  const uint32_t g = w % kSyncGroups;
-  SyncLine* gl = &s->group[g];
-  if (Ops::add_release(&gl->depart, 1u) != sync_group_size(G, g) - 1u) return false;
-  Ops::store_relaxed(&gl->depart, 0u);
-  if (Ops::add_release(&s->top.depart, 1u) != sync_groups_used(G) - 1u) return false;
-  Ops::store_relaxed(&s->top.depart, 0u);
   Ops::fence_acquire();
-  return true;
-}
-
-// For the last departer: the tensor amax and the number of workgroups that
-// gave up (their indices are gave_up_list[0 .. n)).
-template <typename Ops>
-__host__ __device__ inline uint32_t grid_recover_list(GridSyncSlot* s, uint32_t* amax_bits) {
   *amax_bits = Ops::load_relaxed(&s->result);
-  return Ops::load_relaxed(&s->gave_up_n);
+  return kGridWaited;
 }
 
+// The publisher's recovery: the workgroup that took entry i of the give-up
+// list (waiting for its store, at most spin_limit polls; UINT32_MAX if it
+// never came), the entry cleared for the next launch.
 template <typename Ops>
-__host__ __device__ inline void grid_finish(GridSyncSlot* s) {
-  Ops::store_relaxed(&s->gave_up_n, 0u);
+__host__ __device__ inline uint32_t grid_recovered(GridSyncSlot* s, uint32_t i, uint64_t spin_limit) {
+  for (uint64_t n = 0;; n++) {
+    const uint32_t e = Ops::load_relaxed(&s->gave_up_list[i]);
+    if (e != 0u) {
+      Ops::store_relaxed(&s->gave_up_list[i], 0u);
+      return e - 1u;
+    }
+    if (n >= spin_limit) return 0xFFFFFFFFu;
+    Ops::pause();
+  }
 }
 
 // A grid-wide maximum without waiting (the amax passes of the two-pass

@@ -15,10 +15,12 @@
 // The grid never exceeds the number of workgroups that fit on the device at
 // once, so normally all arrive within microseconds.  The wait is bounded all
 // the same: a workgroup that waits too long (its grid partly displaced by
-// other streams' kernels) leaves its blocks to the last workgroup to finish,
-// which encodes them from memory once the amax is known, so the outputs are
-// always complete.  A cooperative launch would give co-residency outright
-// but costs ~14 us per call on this runtime, most of the single pass's gain.
+// other streams' kernels) gives up and leaves its blocks to the publisher
+// (the last workgroup to arrive), which encodes them from memory once its
+// own are done, so the outputs are always complete.  No workgroup waits for
+// the others to finish.  A cooperative launch would give co-residency
+// outright but costs ~14 us per call on this runtime, most of the single
+// pass's gain.
 //
 // Layout: contiguous rows only (ld == cols), seen as one sequence of 16-element
 // blocks; wave v of the grid holds blocks (v * rounds + r) * 64 + lane, so
@@ -142,7 +144,7 @@ __global__ __launch_bounds__(256, 2) void k_quant_row_1pass(
     uint32_t key, GridSyncSlot* slot, uint32_t epoch, uint64_t spin_limit) {
   __shared__ float rtab[128];
   __shared__ uint32_t wave_max[4];
-  __shared__ uint32_t sh_amax, sh_ok, sh_last, sh_n;
+  __shared__ uint32_t sh_amax, sh_role, sh_n;
   const uint32_t G = gridDim.x;
   const uint32_t tid = threadIdx.x, lane = tid & 63u;
   const uint32_t wave = blockIdx.x * 4u + (tid >> 6);
@@ -168,62 +170,50 @@ __global__ __launch_bounds__(256, 2) void k_quant_row_1pass(
   __syncthreads();
   if (tid == 0) {
     const uint32_t wm = max(max(wave_max[0], wave_max[1]), max(wave_max[2], wave_max[3]));
-    uint32_t bits = 0u;
-    sh_ok = grid_arrive_wait<DeviceOps>(slot, G, blockIdx.x, wm, epoch, spin_limit, &bits) ? 1u : 0u;
-    sh_amax = bits;
-  }
-  __syncthreads();
-
-  // phase 2: encode from registers (a workgroup that gave up leaves its
-  // blocks to the last one to depart)
-  if (sh_ok) {
-    const float s_enc = encode_scale(__uint_as_float(sh_amax));
-    fill_scale_table(rtab, s_enc);
-    __syncthreads();
-#pragma unroll
-    for (int r = 0; r < NB; r++) {
-      const uint32_t b = block_of(wave, rounds, r, lane);
-      if (r < (int)rounds && b < nblocks)
-        encode_store<T, RND>(blk[r], bmax[r], b, s_enc, rtab, key, codes, scales);
-    }
-  }
-  if (tid == 0) {
-    const bool last = grid_depart<DeviceOps>(slot, G, blockIdx.x);
     uint32_t bits = 0u, n = 0u;
-    if (last) n = grid_recover_list<DeviceOps>(slot, &bits);
-    sh_last = last ? 1u : 0u;
+    sh_role = grid_arrive_wait<DeviceOps>(slot, G, blockIdx.x, wm, epoch, spin_limit, &bits, &n);
     sh_amax = bits;
     sh_n = n;
   }
   __syncthreads();
-  if (!sh_last) return;
+  // a workgroup that gave up leaves its blocks to the publisher
+  if (sh_role == kGridGaveUp) return;
 
-  // the last workgroup to depart: the tensor outputs, and the blocks of the
-  // workgroups that gave up, read again from memory
+  // phase 2: encode from registers
   const float amax_t = __uint_as_float(sh_amax);
   const float s_enc = encode_scale(amax_t);
+  fill_scale_table(rtab, s_enc);
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < NB; r++) {
+    const uint32_t b = block_of(wave, rounds, r, lane);
+    if (r < (int)rounds && b < nblocks)
+      encode_store<T, RND>(blk[r], bmax[r], b, s_enc, rtab, key, codes, scales);
+  }
+  if (sh_role != kGridPublisher) return;
+
+  // the publisher: the tensor outputs, and the blocks of the workgroups that
+  // gave up, read again from memory
   if (tid == 0) {
     tensor_scale[0] = 1.0f / s_enc;
     amax_out[0] = amax_t;
   }
-  if (sh_n > 0u) {
-    __syncthreads();  // every wave is past its own use of rtab
-    fill_scale_table(rtab, s_enc);
+  for (uint32_t i = 0; i < sh_n; i++) {
+    __shared__ uint32_t sh_w;
+    if (tid == 0) sh_w = grid_recovered<DeviceOps>(slot, i, uint64_t(1) << 22);
     __syncthreads();
-    for (uint32_t i = 0; i < sh_n; i++) {
-      const uint32_t w = DeviceOps::load_relaxed(&slot->gave_up_list[i]);
-      for (uint32_t r = 0; r < rounds; r++) {
-        const uint32_t b = block_of(w * 4u + (tid >> 6), rounds, r, lane);
-        if (b < nblocks) {
-          Blk<T> one;
-          one.load(x + (size_t)b * 16);
-          encode_store<T, RND>(one, one.absmax_bits(), b, s_enc, rtab, key, codes, scales);
-        }
+    const uint32_t w = sh_w;
+    __syncthreads();
+    if (w >= G) continue;  // never stored (cannot happen: the entry follows its swap)
+    for (uint32_t r = 0; r < rounds; r++) {
+      const uint32_t b = block_of(w * 4u + (tid >> 6), rounds, r, lane);
+      if (b < nblocks) {
+        Blk<T> one;
+        one.load(x + (size_t)b * 16);
+        encode_store<T, RND>(one, one.absmax_bits(), b, s_enc, rtab, key, codes, scales);
       }
     }
-    __syncthreads();
   }
-  if (tid == 0) grid_finish<DeviceOps>(slot);
 }
 
 // Blocks per lane of the two instances: 20 for bf16 (160 data VGPRs at two

@@ -1,18 +1,18 @@
 """CPU emulation of the single-pass quantizer's device-wide amax exchange
 (bit_microscaled_quantized_amd/csrc/grid_sync.hpp), run before and beside the
 GPU: the header's protocol is compiled with g++ against std::atomic and each
-workgroup of a launch is a thread.  Per launch it checks that every
-workgroup either learns the exact tensor maximum and writes its own blocks,
-or gives up and has its blocks written by the last workgroup to leave (each
-block written exactly once), that nothing hangs, and that the slot is back
-at its idle state for the next launch on it.
+workgroup of a launch is a thread.  Per launch it checks that exactly one
+workgroup publishes, that every workgroup either learns the exact tensor
+maximum and writes its own blocks, or gives up and has its blocks written by
+the publisher (each block written exactly once), that nothing hangs, and
+that the slot is back at its idle state for the next launch on it.
 
 * full residency: launches of G = 1 .. 200 workgroups (random start delays)
   on one slot, nobody gives up;
 * limited residency (at most R < G workgroups run at once, the rest start
   only when one ends, as on a GPU whose grid is partly displaced): workgroups
-  that wait past the spin limit give up and are counted, the last one to
-  leave covers their blocks, and the next launch on the slot runs clean;
+  that wait past the spin limit give up and are counted, the publisher
+  covers their blocks, and the next launch on the slot runs clean;
 * a spin limit of zero: only workgroups that arrive after the result is
   published pass; the rest are covered;
 * the no-wait grid maximum of the two-pass amax kernels (two maxima per
@@ -53,6 +53,9 @@ struct CpuOps {
     }
   }
   static uint32_t add_release(uint32_t* p, uint32_t v) { return at(p).fetch_add(v, std::memory_order_acq_rel); }
+  static bool cas_release(uint32_t* p, uint32_t& expected, uint32_t desired) {
+    return at(p).compare_exchange_strong(expected, desired, std::memory_order_acq_rel);
+  }
   static uint32_t load_relaxed(uint32_t* p) { return at(p).load(std::memory_order_relaxed); }
   static void store_relaxed(uint32_t* p, uint32_t v) { at(p).store(v, std::memory_order_relaxed); }
   static void store_release(uint32_t* p, uint32_t v) { at(p).store(v, std::memory_order_release); }
@@ -76,7 +79,9 @@ static int fails = 0;
 static bool idle(const GridSyncSlot* s) {
   for (uint32_t g = 0; g < nvfp4::kSyncGroups; g++)
     if (s->group[g].arrive || s->group[g].amax || s->group[g].depart || s->group[g].amax2) return false;
-  return !s->top.arrive && !s->top.amax && !s->top.depart && !s->top.amax2 && !s->gave_up_n;
+  for (uint32_t i = 0; i < nvfp4::kSyncMaxGrid; i++)
+    if (s->gave_up_list[i]) return false;
+  return !s->top.arrive && !s->top.amax && !s->top.depart && !s->top.amax2;
 }
 
 // one launch of G workgroups; returns how many gave up
@@ -98,18 +103,22 @@ static int launch(GridSyncSlot* s, uint32_t epoch, int G, int resident, uint64_t
     th.emplace_back([&, i] {
       res.enter();
       std::this_thread::sleep_for(std::chrono::microseconds(delay[i]));
-      uint32_t bits = 0;
-      ok[i] = nvfp4::grid_arrive_wait<CpuOps>(s, (uint32_t)G, (uint32_t)i, vals[i], epoch, spin, &bits);
+      uint32_t bits = 0, n = 0;
+      const nvfp4::GridRole role =
+          nvfp4::grid_arrive_wait<CpuOps>(s, (uint32_t)G, (uint32_t)i, vals[i], epoch, spin, &bits, &n);
+      ok[i] = role != nvfp4::kGridGaveUp;
       got[i] = bits;
       if (ok[i]) { std::lock_guard<std::mutex> l(wmu); writes[i]++; }
-      if (nvfp4::grid_depart<CpuOps>(s, (uint32_t)G, (uint32_t)i)) {
-        uint32_t amax = 0;
-        const uint32_t n = nvfp4::grid_recover_list<CpuOps>(s, &amax);
+      if (role == nvfp4::kGridPublisher) {
+        std::vector<uint32_t> ws;
+        for (uint32_t k = 0; k < n; k++) ws.push_back(nvfp4::grid_recovered<CpuOps>(s, k, uint64_t(1) << 22));
         std::lock_guard<std::mutex> l(wmu);
         lasts++;
-        last_amax = amax;
-        for (uint32_t k = 0; k < n; k++) writes[s->gave_up_list[k]]++;
-        nvfp4::grid_finish<CpuOps>(s);
+        last_amax = bits;
+        for (uint32_t w : ws) {
+          CHECK(w < (uint32_t)G);
+          if (w < (uint32_t)G) writes[w]++;
+        }
       }
       res.leave();
     });
