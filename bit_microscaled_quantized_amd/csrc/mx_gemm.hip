@@ -236,35 +236,23 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mxfp4(
   const int mb = m0 + wm * 128 + 4 * h;
   const int nb = n0 + wn * 128 + lr;
   float* cb = c + (int64_t)mb * ldc + nb;
-  // One 32 x 32 tile t = 4i + j at a time; with beta = 1 its 16 old values
-  // per lane are loaded together while the previous tile is stored (a load
-  // after a store through the same pointer would wait for it).
-  float old[16];
-  auto load_old = [&](int t) {
-    const int i = t >> 2, j = t & 3;
-    const bool n_ok = nb + j * 32 < N;
 #pragma unroll
-    for (int r = 0; r < 16; r++) {
-      const int dm = i * 32 + 8 * (r >> 2) + (r & 3);
-      old[r] = (n_ok && mb + dm < M) ? __builtin_nontemporal_load(cb + (int64_t)dm * ldc + j * 32) : 0.0f;
-    }
-  };
+  for (int i = 0; i < 4; i++)
 #pragma unroll
-  for (int t = 0; t < 16; t++) {
-    const int i = t >> 2, j = t & 3;
-    if (accumulate) load_old(t);
-    const bool n_ok = nb + j * 32 < N;
+    for (int j = 0; j < 4; j++) {
+      const bool n_ok = nb + j * 32 < N;
 #pragma unroll
-    for (int r = 0; r < 16; r++) {
-      const int dm = i * 32 + 8 * (r >> 2) + (r & 3);
-      if (n_ok && mb + dm < M) {
-        float v = acc[i][j][r];
-        if (accumulate) v += old[r];
-        __builtin_nontemporal_store(v, cb + (int64_t)dm * ldc + j * 32);
+      for (int r = 0; r < 16; r++) {
+        const int dm = i * 32 + 8 * (r >> 2) + (r & 3);
+        if (n_ok && mb + dm < M) {
+          float* p = cb + (int64_t)dm * ldc + j * 32;
+          float v = acc[i][j][r];
+          if (accumulate) v += *p;
+          __builtin_nontemporal_store(v, p);
+        }
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_sched_barrier(0);
-  }
 }
 
 
