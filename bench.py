@@ -61,7 +61,8 @@ U_TOKENS, U_IN, U_OUT = 8192, 5120, 20480
 # scaled by what the same counter reads for the 1 GiB read + 1 GiB write
 # elementwise probe.  Valid only for the kernel sources with this hash; any
 # other source reports null.
-GEMM_TRAFFIC = None
+GEMM_TRAFFIC = {"src_sha256": "c107f307063b53ad995bae3696362a61740c07f59d76d7b64952dd27c67b6ace",
+                "bytes_per_launch": 1.2631e9}
 GEMM_SOURCES = ("gemm.hip", "gemm_tiling.hpp")
 
 GEMM_KERNEL = "k_gemm_nvfp4<float>"
@@ -540,19 +541,26 @@ def summarize_trace(path, steps, warmup):
     NVFP4 GEMM launches of the headline's timed steps (the first `warmup`
     steps' launches skipped, the next 2 x `steps` steps' taken: wall-timed
     and event-timed), each with the split-tail reduction that follows it."""
-    rows = []
+    rows, grids = [], []
     with open(path) as f:
         for r in csv.DictReader(f):
             rows.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]),
                          _kernel_short(r["Kernel_Name"])))
-    rows.sort()
+            grids.append((int(r["Grid_Size_X"]) // max(int(r["Workgroup_Size_X"]), 1),
+                          int(r["Grid_Size_Y"]) // max(int(r["Workgroup_Size_Y"]), 1)))
+    order = sorted(range(len(rows)), key=lambda i: rows[i])
+    rows = [rows[i] for i in order]
+    grids = [grids[i] for i in order]
     stats = {}
-    for s, e, k in rows:
-        stats.setdefault(k, []).append((e - s) / 1e3)
-    print("| kernel | calls | mean µs | median µs | total ms |")
-    print("|---|---:|---:|---:|---:|")
-    for k, v in sorted(stats.items(), key=lambda kv: -sum(kv[1])):
-        print(f"| `{k}` | {len(v)} | {np.mean(v):.1f} | {np.median(v):.1f} | {sum(v) / 1e3:.3f} |")
+    for (s, e, k), g in zip(rows, grids):
+        stats.setdefault((k, g), []).append((e - s) / 1e3)
+    total = sum(sum(v) for v in stats.values())
+    print("| kernel | grid (workgroups x by y) | calls | mean µs | median µs | total ms | % of kernel time |")
+    print("|---|---|---:|---:|---:|---:|---:|")
+    for (k, g), v in sorted(stats.items(), key=lambda kv: -sum(kv[1])):
+        name = k if len(k) <= 60 else k[:57] + "..."
+        print(f"| `{name}` | {g[0]}x{g[1]} | {len(v)} | {np.mean(v):.1f} | {np.median(v):.1f} | "
+              f"{sum(v) / 1e3:.3f} | {100 * sum(v) / total:.1f} |")
     per_step = 3 * S_CHUNKS
     gem = [(i, s, e) for i, (s, e, k) in enumerate(rows) if k == GEMM_KERNEL]
     first, n = warmup * per_step, 2 * steps * per_step
