@@ -39,8 +39,10 @@
  *     allocates and frees nothing and is reentrant; calls on different streams
  *     may overlap (but not while sharing a GEMM workspace).  Its state is a
  *     per-device cache of the compute-unit count and occupancy, and two static
- *     device arrays per device: the single-pass quantize exchange slots (4 KiB)
- *     and the split workspace of nvfp4_gemm_noalloc (64 MiB).
+ *     device arrays per device: the exchange slots of the quantize calls' amax
+ *     reductions (64 slots of 18.4 KiB, one per stream in use, with a host
+ *     epoch counter each) and the split workspace of nvfp4_gemm_noalloc
+ *     (64 MiB).
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
  *     work is enqueued asynchronously on it; results are visible after the
  *     caller synchronizes that stream.
@@ -104,8 +106,9 @@ typedef enum { NVFP4_ROW_1D = 0, NVFP4_COL_1D = 1, NVFP4_TILE_2D = 2 } nvfp4_lay
  *   workgroups exchange the amax through a per-(device, stream) slot of
  *   library-owned device memory, then encodes it.  The wait is bounded: a
  *   workgroup that waits too long (its grid partly displaced by other
- *   streams' kernels) leaves its blocks to the last workgroup to finish, which
- *   encodes them from memory, so the outputs are always complete.
+ *   streams' kernels) leaves its blocks to the workgroup that publishes the
+ *   amax (the last to arrive), which encodes them from memory after its own,
+ *   so the outputs are always complete.
  *   Everything else, and any call on a stream under graph capture, takes two
  *   passes (amax, then cast).  Both give identical outputs.  Calls on one
  *   stream never share a slot with another stream's calls (64 slots per
