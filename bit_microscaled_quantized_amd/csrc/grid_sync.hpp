@@ -14,20 +14,21 @@
 //             last arriver reads the group max, resets the group's fields,
 //             maxes it into the top `amax` and adds 1 to the top `arrive`;
 //             the last group arriver -- the publisher -- reads the tensor
-//             amax, resets the top, stores it in `result`, closes the gate
-//             (below) and sets `done` = e.
-//   wait    : every other workgroup polls `done` == e, at most spin_limit
-//             polls, then tries to give up through the gate.
-//   gate    : one word, [epoch bits 31:14 | closed bit 13 | count 12:0].  A
-//             workgroup gives up by a compare-and-swap that adds 1 to the
-//             count of this epoch's open gate (a word of another epoch reads
-//             as open with count 0); the count before its swap is its index
-//             in `gave_up_list`, where it then stores w + 1, and it leaves
-//             without encoding.  The publisher closes the gate by a
-//             compare-and-swap that sets the closed bit; the count it closes
-//             on is exactly the number of workgroups that gave up, since no
-//             swap can add to a closed gate: a workgroup whose swap fails on
-//             a closed gate reads `result` and goes on normally.
+//             amax, resets the top and publishes the amax through the gate.
+//   gate    : one 64-bit word, [amax 63:32 | epoch bits 31:14 | closed bit 13
+//             | count 12:0]; a word of another epoch reads as this epoch's
+//             open gate with count 0.  The publisher swaps in (amax, e,
+//             closed, 0) with one atomic exchange; the word it takes out
+//             holds the number of workgroups of this epoch that gave up.
+//   wait    : every other workgroup polls the gate until it is closed for e
+//             (the amax comes with it), at most spin_limit polls, then tries
+//             to give up: a compare-and-swap that adds 1 to the count of the
+//             still-open gate.  The count before its swap is its index in
+//             `gave_up_list`, where it then stores w + 1, and it leaves
+//             without encoding.  No swap can add to a closed gate, so the
+//             count the publisher takes out is exactly the set that gave up;
+//             a workgroup whose swap fails on a closed gate takes the amax
+//             from it and goes on normally.
 //   recover : after its own blocks, the publisher encodes the blocks of the
 //             workgroups in gave_up_list[0 .. count) (from memory; it waits
 //             for each entry to be stored) and clears those entries.
@@ -35,8 +36,7 @@
 // leaves outputs unwritten: workgroups that wait too long leave their blocks
 // to the publisher, which runs after all have arrived.  No workgroup has to
 // wait for the others to finish.  When the launch ends, the lines and the
-// list are back at zero; `done` and the gate carry the epoch, so they need
-// no reset.
+// list are back at zero; the gate carries the epoch, so it needs no reset.
 #pragma once
 
 #include <stdint.h>
@@ -49,37 +49,37 @@ constexpr uint32_t kSyncMaxGrid = 4096;  // workgroups per launch
 struct alignas(128) SyncLine {
   uint32_t arrive;
   uint32_t amax;  // FP32 bits of a non-negative maximum (integer order = float order)
-  uint32_t depart;  // unused (kept zero)
-  uint32_t amax2;   // a second maximum (grid_max_arrive)
-  uint32_t pad[28];
+  uint32_t amax2;  // a second maximum (grid_max_arrive)
+  uint32_t pad[29];
 };
 
 struct GridSyncSlot {
   SyncLine group[kSyncGroups];
   SyncLine top;
-  alignas(128) uint32_t done;  // epoch of the last published result
-  uint32_t result;             // tensor amax bits of that epoch
-  alignas(128) uint32_t gate;  // [epoch 31:14 | closed 13 | count 12:0]
+  alignas(128) uint64_t gate;  // [amax 63:32 | epoch 31:14 | closed 13 | count 12:0]
   uint32_t gave_ups;           // running total over all launches
   alignas(128) uint32_t gave_up_list[kSyncMaxGrid];  // w + 1, 0 = empty
 };
 
-constexpr uint32_t kGateClosed = 1u << 13;
-constexpr uint32_t kGateCount = kGateClosed - 1u;
+constexpr uint64_t kGateClosed = 1u << 13;
+constexpr uint64_t kGateCount = kGateClosed - 1u;
+constexpr uint64_t kGateTagMask = 0xFFFFC000ull;
 
-__host__ __device__ inline uint32_t gate_tag(uint32_t epoch) { return epoch << 14; }
+__host__ __device__ inline uint64_t gate_tag(uint32_t epoch) { return (uint64_t)(epoch << 14); }
 
 // This epoch's view of a gate word: another epoch's word is an open gate
 // with count 0.
-__host__ __device__ inline uint32_t gate_view(uint32_t g, uint32_t epoch) {
-  return (g & ~(kGateClosed | kGateCount)) == gate_tag(epoch) ? g : gate_tag(epoch);
+__host__ __device__ inline uint64_t gate_view(uint64_t g, uint32_t epoch) {
+  return (g & kGateTagMask) == gate_tag(epoch) ? g : gate_tag(epoch);
 }
 
 // Ops (all device-scope):
 //   static void max_relaxed(uint32_t* p, uint32_t v);
 //   static uint32_t add_release(uint32_t* p, uint32_t v);  // after this thread's earlier
 //                                                          // atomics; returns the old value
-//   static bool cas_release(uint32_t* p, uint32_t& expected, uint32_t desired);
+//   static bool cas64(uint64_t* p, uint64_t& expected, uint64_t desired);
+//   static uint64_t exchange64(uint64_t* p, uint64_t v);
+//   static uint64_t load64(uint64_t* p);
 //   static uint32_t load_relaxed(uint32_t* p);
 //   static void store_release(uint32_t* p, uint32_t v);   // after earlier atomics
 //   static void store_relaxed(uint32_t* p, uint32_t v);
@@ -122,29 +122,26 @@ __host__ __device__ inline GridRole grid_arrive_wait(GridSyncSlot* s, uint32_t G
       const uint32_t tm = Ops::load_relaxed(&s->top.amax);
       Ops::store_relaxed(&s->top.amax, 0u);
       Ops::store_relaxed(&s->top.arrive, 0u);
-      Ops::store_relaxed(&s->result, tm);
-      uint32_t cur = Ops::load_relaxed(&s->gate);
-      for (;;) {
-        const uint32_t v = gate_view(cur, epoch);
-        if (Ops::cas_release(&s->gate, cur, v | kGateClosed)) {
-          *recover = v & kGateCount;
-          break;
-        }
-      }
-      Ops::store_release(&s->done, epoch);
+      const uint64_t old = Ops::exchange64(&s->gate, ((uint64_t)tm << 32) | gate_tag(epoch) | kGateClosed);
+      *recover = (uint32_t)(gate_view(old, epoch) & kGateCount);
       *amax_bits = tm;
       return kGridPublisher;
     }
   }
   *recover = 0u;
+  uint64_t cur = 0;
   for (uint64_t n = 0;; n++) {
-    if (Ops::load_relaxed(&s->done) == epoch) break;
+    cur = gate_view(Ops::load64(&s->gate), epoch);
+    if (cur & kGateClosed) break;
     if (n >= spin_limit) {
-      uint32_t cur = Ops::load_relaxed(&s->gate);
       for (;;) {
-        const uint32_t v = gate_view(cur, epoch);
-        if (v & kGateClosed) break;  // published meanwhile: result is stored
-        if (Ops::cas_release(&s->gate, cur, v + 1u)) {
+        uint64_t expected = Ops::load64(&s->gate);
+        const uint64_t v = gate_view(expected, epoch);
+        if (v & kGateClosed) {  // published meanwhile
+          cur = v;
+          break;
+        }
+        if (Ops::cas64(&s->gate, expected, v + 1u)) {
           Ops::store_release(&s->gave_up_list[v & kGateCount], w + 1u);
           Ops::add_release(&s->gave_ups, 1u);
           return kGridGaveUp;
@@ -154,8 +151,7 @@ __host__ __device__ inline GridRole grid_arrive_wait(GridSyncSlot* s, uint32_t G
     }
     Ops::pause();
   }
-  Ops::fence_acquire();
-  *amax_bits = Ops::load_relaxed(&s->result);
+  *amax_bits = (uint32_t)(cur >> 32);
   return kGridWaited;
 }
 

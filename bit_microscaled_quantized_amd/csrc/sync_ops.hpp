@@ -37,14 +37,20 @@ struct DeviceOps {
     drain();
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  // compare-and-swap after this wave's earlier memory operations; true if
-  // *p held `expected` (then it holds `desired`), else `expected` = *p
-  static __device__ bool cas_release(uint32_t* p, uint32_t& expected, uint32_t desired) {
+  // 64-bit compare-and-swap after this wave's earlier memory operations;
+  // true if *p held `expected` (then it holds `desired`), else `expected` = *p
+  static __device__ bool cas64(uint64_t* p, uint64_t& expected, uint64_t desired) {
     drain();
     const bool ok = __hip_atomic_compare_exchange_strong(p, &expected, desired, __ATOMIC_RELAXED,
                                                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     drain();
     return ok;
+  }
+  static __device__ uint64_t exchange64(uint64_t* p, uint64_t v) {
+    return __hip_atomic_exchange(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  static __device__ uint64_t load64(uint64_t* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   static __device__ void fence_acquire() { asm volatile("" ::: "memory"); }
   static __device__ void pause() { __builtin_amdgcn_s_sleep(8); }

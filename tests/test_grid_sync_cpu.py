@@ -53,9 +53,12 @@ struct CpuOps {
     }
   }
   static uint32_t add_release(uint32_t* p, uint32_t v) { return at(p).fetch_add(v, std::memory_order_acq_rel); }
-  static bool cas_release(uint32_t* p, uint32_t& expected, uint32_t desired) {
-    return at(p).compare_exchange_strong(expected, desired, std::memory_order_acq_rel);
+  static std::atomic_ref<uint64_t> at64(uint64_t* p) { return std::atomic_ref<uint64_t>(*p); }
+  static bool cas64(uint64_t* p, uint64_t& expected, uint64_t desired) {
+    return at64(p).compare_exchange_strong(expected, desired, std::memory_order_acq_rel);
   }
+  static uint64_t exchange64(uint64_t* p, uint64_t v) { return at64(p).exchange(v, std::memory_order_acq_rel); }
+  static uint64_t load64(uint64_t* p) { return at64(p).load(std::memory_order_acquire); }
   static uint32_t load_relaxed(uint32_t* p) { return at(p).load(std::memory_order_relaxed); }
   static void store_relaxed(uint32_t* p, uint32_t v) { at(p).store(v, std::memory_order_relaxed); }
   static void store_release(uint32_t* p, uint32_t v) { at(p).store(v, std::memory_order_release); }
@@ -78,10 +81,10 @@ static int fails = 0;
 
 static bool idle(const GridSyncSlot* s) {
   for (uint32_t g = 0; g < nvfp4::kSyncGroups; g++)
-    if (s->group[g].arrive || s->group[g].amax || s->group[g].depart || s->group[g].amax2) return false;
+    if (s->group[g].arrive || s->group[g].amax || s->group[g].amax2) return false;
   for (uint32_t i = 0; i < nvfp4::kSyncMaxGrid; i++)
     if (s->gave_up_list[i]) return false;
-  return !s->top.arrive && !s->top.amax && !s->top.depart && !s->top.amax2;
+  return !s->top.arrive && !s->top.amax && !s->top.amax2;
 }
 
 // one launch of G workgroups; returns how many gave up
@@ -131,7 +134,10 @@ static int launch(GridSyncSlot* s, uint32_t epoch, int G, int resident, uint64_t
   }
   CHECK(lasts == 1);
   CHECK(last_amax == want);
-  CHECK(s->done == epoch);
+  // the gate is closed for this epoch and carries the tensor amax
+  CHECK((s->gate & nvfp4::kGateTagMask) == nvfp4::gate_tag(epoch));
+  CHECK((s->gate & nvfp4::kGateClosed) != 0);
+  CHECK((uint32_t)(s->gate >> 32) == want);
   CHECK(idle(s));
   return gave_up;
 }
