@@ -14,6 +14,8 @@
 // stores stay contiguous.  Each workgroup first tabulates S_enc / dec(e) for
 // the 127 finite E4M3 codes in LDS, so a block scale costs one division by 6
 // (a multiply and two FMAs) and one table read.
+#include <algorithm>
+
 #include "grid_sync.hpp"
 #include "nvfp4_device.hpp"
 #include "nvfp4_launch.hpp"
@@ -1028,17 +1030,34 @@ static hipError_t launch_cast(const void* x, int dt, int64_t rows, int64_t cols,
   return hipGetLastError();
 }
 
+// Workgroups of k_rht_amax that fit on the current device at once.
+template <typename T>
+static int rht_amax_occupancy() {
+  static const int occ = [] {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_rht_amax<T>, 256, 0) != hipSuccess) n = 0;
+    return n;
+  }();
+  return occ;
+}
+
+static int64_t rht_amax_resident(int dt) {
+  const int occ = dt == 0 ? rht_amax_occupancy<uint16_t>() : rht_amax_occupancy<float>();
+  return (int64_t)std::max(occ, 1) * cu_count();
+}
+
 // RHT amax pass (plus the plain amax into amax_plain when it is not null).
 static hipError_t launch_rht_amax(const void* x, int dt, int64_t tokens, int64_t cols, int64_t ld,
                                   uint32_t sign_mask, float* amax, float* amax_plain, hipStream_t s) {
   GridSyncSlot* slot = stream_sync_slot(s);
   if (slot == nullptr) k_zero_amax<<<1, 64, 0, s>>>(amax, amax_plain);
-  // patches of 16 tokens x 4 columns; at most 2048 workgroups, rounds
-  // balanced (capping the grid at the resident count was 1-5 % slower here)
+  // patches of 16 tokens x 4 columns, at most one grid of resident
+  // workgroups walking them (A/B on one box: 8192x5120 RHT call 42.6 -> 41.5
+  // us, 8192x20480 SR 171.3 -> 165.5 us, against balanced rounds of up to
+  // 2048 workgroups, which leave a partial last round of workgroups)
   const int64_t units = (tokens / 16) * (cols / 4);
   const int64_t wgs = (units + 255) / 256;
-  const int64_t rounds = (wgs + 2047) / 2048;
-  const unsigned grid = grid_cap((wgs + rounds - 1) / rounds, 2048);
+  const unsigned grid = grid_cap(std::min<int64_t>(wgs, rht_amax_resident(dt)), 2048);
   if (dt == 0)
     k_rht_amax<uint16_t><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(x), tokens, cols, ld,
                                               sign_mask, amax, amax_plain, slot);
