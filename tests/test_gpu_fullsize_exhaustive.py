@@ -9,7 +9,11 @@ tensors, with the oracle run over whole tensors (C, OpenMP) and FP64 BLAS.
   Frobenius error <= 1e-5 against the FP64 product of the oracle's own
   dequantized operands;
 * quantize-only tensors (bf16 8192x5120, which takes the single pass, and
-  8192x20480, two passes; N(0,1) with 0.1 % 100x outliers), RNE and SR.
+  8192x20480, two passes; N(0,1) with 0.1 % 100x outliers), RNE and SR;
+* the FFN up-projection layer (X 8192x5120, W 20480x5120, dY 8192x20480):
+  its five quantizations and three GEMMs;
+* the Wgrad case (dY, X 8192x5120 Student-t(3), RHT + column-1D, dY SR):
+  both quantizations and dW.
 
 Codes, scales, tensor scale and amax are compared bit for bit."""
 import numpy as np
@@ -89,3 +93,59 @@ def test_quantize_only_every_code(ora, which, rnd):
     x = synth.f32_to_bf16_bits(synth.quantize_sweep(which))
     seed = 4321 + which
     _same(gpuio.gpu_quantize(x, nv.NVFP4_ROW_1D, rnd, seed), ora.quantize(x, ora.ROW_1D, rnd, seed))
+
+
+@pytest.fixture(scope="module")
+def ffn_up_step(ora):
+    """The FFN up-projection layer: X 8192x5120, W 20480x5120, dY 8192x20480."""
+    d = synth.ffn_up()
+    x = synth.f32_to_bf16_bits(d["x"])
+    w = synth.f32_to_bf16_bits(d["w"])
+    dy = synth.f32_to_bf16_bits(d["dy"])
+    mask, sr, sc = d["sign_mask"], d["sr_seed_row"], d["sr_seed_col"]
+    g = dict(w=gpuio.gpu_quantize(w, nv.NVFP4_TILE_2D))
+    g["x_row"], g["x_rht"] = gpuio.gpu_quantize_row_rht(x, mask, nv.NVFP4_RNE, 0, nv.NVFP4_RNE, 0)
+    g["d_row"], g["d_rht"] = gpuio.gpu_quantize_row_rht(dy, mask, nv.NVFP4_SR, sr, nv.NVFP4_SR, sc)
+    o = dict(w=ora.quantize(w, ora.TILE_2D, ora.RNE), x_row=ora.quantize(x, ora.ROW_1D, ora.RNE),
+             x_rht=ora.rht_quantize(x, mask, ora.RNE), d_row=ora.quantize(dy, ora.ROW_1D, ora.SR, sr),
+             d_rht=ora.rht_quantize(dy, mask, ora.SR, sc))
+    return dict(g=g, o=o, shape=(x.shape[0], x.shape[1], w.shape[0]))
+
+
+def test_ffn_up_quantize_every_code(ffn_up_step):
+    g, o = ffn_up_step["g"], ffn_up_step["o"]
+    _same(g["w"], o["w"], KEYS + ("codes_t", "scales_t"))
+    for k in ("x_row", "x_rht", "d_row", "d_rht"):
+        _same(g[k], o[k])
+
+
+@pytest.mark.parametrize("which", ["fprop", "dgrad", "wgrad"])
+def test_ffn_up_gemm_every_output(ora, ffn_up_step, which):
+    g, o = ffn_up_step["g"], ffn_up_step["o"]
+    t, i, f = ffn_up_step["shape"]  # tokens, d_in (hidden), d_out (ffn)
+    if which == "fprop":  # Y = X W^T: t x f, K = i
+        c = gpuio.gpu_gemm(t, f, i, g["x_row"]["dev"], g["w"]["dev"], 16)
+        _gemm_check(ora, c, o["x_row"], 1, o["w"]["codes"], o["w"]["scales"], o["w"]["tensor_scale"], 16)
+    elif which == "dgrad":  # dX = dY W: t x i, K = f
+        bw = dict(codes=g["w"]["dev"]["codes_t"], scales=g["w"]["dev"]["scales_t"], ts=g["w"]["dev"]["ts"])
+        c = gpuio.gpu_gemm(t, i, f, g["d_row"]["dev"], bw, 16)
+        _gemm_check(ora, c, o["d_row"], 1, o["w"]["codes_t"], o["w"]["scales_t"],
+                    o["w"]["tensor_scale"], 16)
+    else:  # dW = RHT(dY)^T RHT(X): f x i, K = t
+        c = gpuio.gpu_gemm(f, i, t, g["d_rht"]["dev"], g["x_rht"]["dev"], 1)
+        _gemm_check(ora, c, o["d_rht"], 1, o["x_rht"]["codes"], o["x_rht"]["scales"],
+                    o["x_rht"]["tensor_scale"], 1)
+
+
+def test_wgrad_case_every_output(ora):
+    """dY, X bf16 8192x5120 Student-t(3); RHT + column-1D (dY SR, X RNE); dW = dY^T X."""
+    d = synth.wgrad_rht()
+    dy, x = synth.f32_to_bf16_bits(d["dy"]), synth.f32_to_bf16_bits(d["x"])
+    mask, seed = d["sign_mask"], d["sr_seed"]
+    gd, gx = gpuio.gpu_rht_quantize(dy, mask, nv.NVFP4_SR, seed), gpuio.gpu_rht_quantize(x, mask)
+    od, ox = ora.rht_quantize(dy, mask, ora.SR, seed), ora.rht_quantize(x, mask)
+    _same(gd, od)
+    _same(gx, ox)
+    t, c_ = dy.shape
+    c = gpuio.gpu_gemm(c_, c_, t, gd["dev"], gx["dev"], 1)
+    _gemm_check(ora, c, od, 1, ox["codes"], ox["scales"], ox["tensor_scale"], 1)
