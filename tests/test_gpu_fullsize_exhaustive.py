@@ -13,7 +13,9 @@ tensors, with the oracle run over whole tensors (C, OpenMP) and FP64 BLAS.
 * the FFN up-projection layer (X 8192x5120, W 20480x5120, dY 8192x20480):
   its five quantizations and three GEMMs;
 * the Wgrad case (dY, X 8192x5120 Student-t(3), RHT + column-1D, dY SR):
-  both quantizations and dW.
+  both quantizations and dW;
+* the MXFP4 comparison step on the FFN up-projection tensors: six
+  quantizations and three GEMMs.
 
 Codes, scales, tensor scale and amax are compared bit for bit."""
 import numpy as np
@@ -149,3 +151,32 @@ def test_wgrad_case_every_output(ora):
     t, c_ = dy.shape
     c = gpuio.gpu_gemm(c_, c_, t, gd["dev"], gx["dev"], 1)
     _gemm_check(ora, c, od, 1, ox["codes"], ox["scales"], ox["tensor_scale"], 1)
+
+
+def test_mxfp4_ffn_up_every_output(ora):
+    """The MXFP4 comparison step on the FFN up-projection tensors, as bench.py
+    runs it: W, X and dY in row and column layouts (dY with SR), Fprop, Dgrad
+    and Wgrad; every code and scale, every GEMM output."""
+    d = synth.ffn_up()
+    x = synth.f32_to_bf16_bits(d["x"])
+    w = synth.f32_to_bf16_bits(d["w"])
+    dy = synth.f32_to_bf16_bits(d["dy"])
+    sr, sc = d["sr_seed_row"], d["sr_seed_col"]
+    R, C = nv.NVFP4_ROW_1D, nv.NVFP4_COL_1D
+    q = {}
+    for name, t, layout, rnd, seed in (("w_r", w, R, 0, 0), ("w_c", w, C, 0, 0), ("x_r", x, R, 0, 0),
+                                       ("x_c", x, C, 0, 0), ("d_r", dy, R, 1, sr), ("d_c", dy, C, 1, sc)):
+        g = gpuio.gpu_mx_quantize(t, layout, rnd, seed)
+        o = ora.mx_quantize(t, ora.ROW_1D if layout == R else ora.COL_1D, rnd, seed)
+        assert np.array_equal(g["codes"], o["codes"]), f"{name} codes: {gpuio.first_diff(g['codes'], o['codes'])}"
+        assert np.array_equal(g["scales"], o["scales"]), f"{name} scales"
+        q[name] = (g, o)
+    tok, hid = x.shape
+    ffn = w.shape[0]
+    for a, b, (M, N, K) in (("x_r", "w_r", (tok, ffn, hid)), ("d_r", "w_c", (tok, hid, ffn)),
+                            ("d_c", "x_c", (ffn, hid, tok))):
+        (ga, oa), (gb, ob) = q[a], q[b]
+        c = gpuio.gpu_mx_gemm(M, N, K, ga["dev"], gb["dev"])
+        ref = ora.gemm_f64(ora.mx_dequant(oa["codes"], oa["scales"]), ora.mx_dequant(ob["codes"], ob["scales"]))
+        err = gpuio.rel_fro(c, ref)
+        assert err <= TOL, (a, b, err)
