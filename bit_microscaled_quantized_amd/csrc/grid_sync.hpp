@@ -29,6 +29,12 @@
 //             count the publisher takes out is exactly the set that gave up;
 //             a workgroup whose swap fails on a closed gate takes the amax
 //             from it and goes on normally.
+//   second  : a launch may exchange a second maximum (the fused row + RHT
+//             cast needs the amax of the input and of its transform).  It
+//             travels through the lines' `amax2` fields, and the publisher
+//             stores [max2 | epoch] into `result2` before it swaps the gate
+//             (the swap is ordered after that store); a workgroup that sees
+//             the gate closed reads it from there.
 //   recover : after its own blocks, the publisher encodes the blocks of the
 //             workgroups in gave_up_list[0 .. count) (from memory; it waits
 //             for each entry to be stored) and clears those entries.
@@ -57,6 +63,7 @@ struct GridSyncSlot {
   SyncLine group[kSyncGroups];
   SyncLine top;
   alignas(128) uint64_t gate;  // [amax 63:32 | epoch 31:14 | closed 13 | count 12:0]
+  uint64_t result2;            // [second maximum 63:32 | epoch 31:0]
   uint32_t gave_ups;           // running total over all launches
   alignas(128) uint32_t gave_up_list[kSyncMaxGrid];  // w + 1, 0 = empty
 };
@@ -79,6 +86,8 @@ __host__ __device__ inline uint64_t gate_view(uint64_t g, uint32_t epoch) {
 //                                                          // atomics; returns the old value
 //   static bool cas64(uint64_t* p, uint64_t& expected, uint64_t desired);
 //   static uint64_t exchange64(uint64_t* p, uint64_t v);
+//   static uint64_t exchange64_release(uint64_t* p, uint64_t v);  // after earlier stores
+//   static void store64_relaxed(uint64_t* p, uint64_t v);
 //   static uint64_t load64(uint64_t* p);
 //   static uint32_t load_relaxed(uint32_t* p);
 //   static void store_release(uint32_t* p, uint32_t v);   // after earlier atomics
@@ -96,33 +105,59 @@ __host__ __device__ inline uint32_t sync_groups_used(uint32_t G) {
 
 enum GridRole : uint32_t { kGridWaited = 0, kGridGaveUp = 1, kGridPublisher = 2 };
 
-// Arrive with this workgroup's maximum and obtain the tensor amax.  Called by
-// one thread per workgroup.  kGridWaited / kGridPublisher: *amax_bits holds
-// the tensor amax and the workgroup encodes its blocks; the publisher then
-// also covers the *recover workgroups in gave_up_list (grid_recovered) and
-// writes the tensor-level outputs.  kGridGaveUp: recorded; the workgroup
-// must not write its outputs.
+// The second maximum of this epoch from result2 (stored before the gate was
+// closed, so the first read normally has it; at most spin_limit more polls).
+template <typename Ops>
+__host__ __device__ inline uint32_t grid_second(GridSyncSlot* s, uint32_t epoch, uint64_t spin_limit) {
+  uint64_t r = Ops::load64(&s->result2);
+  for (uint64_t n = 0; (uint32_t)r != epoch && n < spin_limit; n++) {
+    Ops::pause();
+    r = Ops::load64(&s->result2);
+  }
+  return (uint32_t)(r >> 32);
+}
+
+// Arrive with this workgroup's maximum (and, with amax2_bits not null, a
+// second one) and obtain the tensor maxima.  Called by one thread per
+// workgroup.  kGridWaited / kGridPublisher: *amax_bits (and *amax2_bits)
+// hold the tensor maxima and the workgroup encodes its blocks; the publisher
+// then also covers the *recover workgroups in gave_up_list (grid_recovered)
+// and writes the tensor-level outputs.  kGridGaveUp: recorded; the
+// workgroup must not write its outputs.
 template <typename Ops>
 __host__ __device__ inline GridRole grid_arrive_wait(GridSyncSlot* s, uint32_t G, uint32_t w,
                                                      uint32_t my_max, uint32_t epoch,
                                                      uint64_t spin_limit, uint32_t* amax_bits,
-                                                     uint32_t* recover) {
+                                                     uint32_t* recover, uint32_t my_max2 = 0u,
+                                                     uint32_t* amax2_bits = nullptr) {
+  const bool two = amax2_bits != nullptr;
   const uint32_t g = w % kSyncGroups;
   SyncLine* gl = &s->group[g];
   Ops::max_relaxed(&gl->amax, my_max);
+  if (two) Ops::max_relaxed(&gl->amax2, my_max2);
   if (Ops::add_release(&gl->arrive, 1u) == sync_group_size(G, g) - 1u) {
     // last of the group: every member's max is performed before its arrival
     Ops::fence_acquire();
     const uint32_t gm = Ops::load_relaxed(&gl->amax);
+    const uint32_t gm2 = two ? Ops::load_relaxed(&gl->amax2) : 0u;
     Ops::store_relaxed(&gl->amax, 0u);
+    if (two) Ops::store_relaxed(&gl->amax2, 0u);
     Ops::store_relaxed(&gl->arrive, 0u);
     Ops::max_relaxed(&s->top.amax, gm);
+    if (two) Ops::max_relaxed(&s->top.amax2, gm2);
     if (Ops::add_release(&s->top.arrive, 1u) == sync_groups_used(G) - 1u) {
       Ops::fence_acquire();
       const uint32_t tm = Ops::load_relaxed(&s->top.amax);
       Ops::store_relaxed(&s->top.amax, 0u);
+      if (two) {
+        const uint32_t tm2 = Ops::load_relaxed(&s->top.amax2);
+        Ops::store_relaxed(&s->top.amax2, 0u);
+        Ops::store64_relaxed(&s->result2, ((uint64_t)tm2 << 32) | epoch);
+        *amax2_bits = tm2;
+      }
       Ops::store_relaxed(&s->top.arrive, 0u);
-      const uint64_t old = Ops::exchange64(&s->gate, ((uint64_t)tm << 32) | gate_tag(epoch) | kGateClosed);
+      const uint64_t gate = ((uint64_t)tm << 32) | gate_tag(epoch) | kGateClosed;
+      const uint64_t old = two ? Ops::exchange64_release(&s->gate, gate) : Ops::exchange64(&s->gate, gate);
       *recover = (uint32_t)(gate_view(old, epoch) & kGateCount);
       *amax_bits = tm;
       return kGridPublisher;
@@ -152,6 +187,10 @@ __host__ __device__ inline GridRole grid_arrive_wait(GridSyncSlot* s, uint32_t G
     Ops::pause();
   }
   *amax_bits = (uint32_t)(cur >> 32);
+  if (two) {
+    Ops::fence_acquire();
+    *amax2_bits = grid_second<Ops>(s, epoch, spin_limit);
+  }
   return kGridWaited;
 }
 

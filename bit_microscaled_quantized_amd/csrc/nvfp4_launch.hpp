@@ -12,14 +12,27 @@ hipError_t launch_quantize(const void* x, int dt, int64_t rows, int64_t cols, in
                            hipStream_t s);
 
 // Single-pass row-1D quantization when the tensor fits in the resident
-// grid's registers (contiguous rows, stream not capturing, cooperative launch
-// available); *done tells whether it ran (nothing is enqueued otherwise).
+// grid's registers (contiguous rows, stream not capturing, an exchange slot
+// free); *done tells whether it ran (nothing is enqueued otherwise).
 hipError_t try_quantize_row_1pass(const void* x, int dt, int64_t rows, int64_t cols, int64_t ld,
                                   int rnd, uint64_t seed, uint8_t* codes, uint8_t* scales,
                                   float* tensor_scale, float* amax, hipStream_t s, bool* done);
 struct GridSyncSlot;
 // The per-(device, stream) exchange slot, or nullptr where none may be used.
 GridSyncSlot* stream_sync_slot(hipStream_t s);
+// What one single-pass launch on (current device, stream) needs: its
+// exchange slot, a fresh epoch and the spin limit.  single_pass_ticket
+// returns false (nothing reserved) where no single pass may run: two passes
+// forced, a stream under graph capture, or no slot free on the device.
+// single_pass_launched counts a launch that was enqueued with the ticket.
+struct SinglePassTicket {
+  GridSyncSlot* slot;
+  uint32_t epoch;
+  uint64_t spin;
+  int dev;
+};
+bool single_pass_ticket(hipStream_t s, SinglePassTicket* t);
+void single_pass_launched(const SinglePassTicket& t);
 // 0: automatic choice of the single-pass path, 2: always two passes.
 hipError_t set_quantize_passes(int passes);
 // Polls a single-pass workgroup makes before it gives up waiting.

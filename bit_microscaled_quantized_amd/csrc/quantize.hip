@@ -575,6 +575,13 @@ __device__ __forceinline__ void row_rht_prologue(const float* row_amax, const fl
   __syncthreads();
 }
 
+// Workgroup bid's place when each of the 8 XCDs (dealt workgroups
+// round-robin by the hardware) takes a contiguous range of [0, G).
+__device__ __forceinline__ uint32_t xcd_contiguous(uint32_t bid, uint32_t G) {
+  const uint32_t xcd = bid & 7u, per = G >> 3, rem = G & 7u;
+  return xcd < rem ? xcd * (per + 1) + (bid >> 3) : rem * (per + 1) + (xcd - rem) * per + (bid >> 3);
+}
+
 // One tile per workgroup.  XCD-aware tile order: the hardware deals
 // workgroups round-robin over the 8 XCDs, so each XCD takes a contiguous
 // range of tiles instead.  The two tiles that write the two halves of each
@@ -593,15 +600,141 @@ __global__ __launch_bounds__(256) void k_cast_row_rht(const T* __restrict__ x, R
   float s_row, s_rht;
   row_rht_prologue<T>(row_amax, rht_amax, row_ts, rht_ts, s_row, s_rht, rtab_row, rtab_rht);
 
-  const uint32_t G = gridDim.x * gridDim.y;
-  const uint32_t bid = blockIdx.y * gridDim.x + blockIdx.x;
-  const uint32_t xcd = bid & 7u, per = G >> 3, rem = G & 7u;
-  const uint32_t id = xcd < rem ? xcd * (per + 1) + (bid >> 3) : rem * (per + 1) + (xcd - rem) * per + (bid >> 3);
+  const uint32_t id = xcd_contiguous(blockIdx.y * gridDim.x + blockIdx.x, gridDim.x * gridDim.y);
   bool valid;
   ColTile<T> tile;
   tile.load(row_rht_patch(x, a, id, gridDim.x, valid), a.ld);
   row_rht_tile<T, RR, RH>(tile, valid, id, gridDim.x, a, s_row, s_rht, rtab_row, rtab_rht, lcodes,
                           lscales);
+}
+
+// Single-pass form of the fused call for a bf16 tensor that fits on chip
+// (the tensor amax is needed before any block can be encoded, so the
+// two-pass form reads the input twice).  The grid is at most the resident
+// workgroup count (three per CU, up to 168 VGPRs per lane); the workgroup
+// with place L (XCD-contiguous, as above) holds tiles [L * tiles / G,
+// (L + 1) * tiles / G) of the 256 x 128 tiles, at most kRowRht1Tiles, in
+// registers:
+//   phase 1: both tiles' loads first, then the maxima of |x| and of the
+//            unnormalized transform |u| over the workgroup's patches;
+//   exchange: both maxima through grid_sync.hpp (bounded wait: a workgroup
+//            that waits too long leaves its tiles to the publisher, the last
+//            to arrive, which encodes them from memory after its own);
+//   phase 2: the two-pass kernel's tile body on each held tile, so both
+//            copies are identical to that path's.
+// Round-to-nearest-even on both copies only: with stochastic rounding the
+// encode is bound by its VALU work, which the two-pass form overlaps with
+// the reads and this one cannot.
+constexpr int kRowRht1Tiles = 2;
+
+__global__ __launch_bounds__(256, 3) void k_row_rht_1pass(
+    const uint16_t* __restrict__ x, RowRhtArgs a, uint32_t tiles, uint32_t tiles_x,
+    float* __restrict__ row_ts, float* __restrict__ row_amax, float* __restrict__ rht_ts,
+    float* __restrict__ rht_amax, GridSyncSlot* slot, uint32_t epoch, uint64_t spin_limit) {
+  __shared__ __align__(16) uint8_t lcodes[kColCols][kColTok / 2];
+  __shared__ __align__(16) uint8_t lscales[kColCols][kColTok / 16];
+  __shared__ float rtab_row[128];
+  __shared__ float rtab_rht[128];
+  __shared__ uint32_t wave_max[2][4];
+  __shared__ uint32_t sh_x, sh_u, sh_role, sh_n;
+  const uint32_t G = gridDim.x;
+  const uint32_t tid = threadIdx.x, lane = tid & 63u;
+  const uint32_t L = xcd_contiguous(blockIdx.x, G);
+  const uint32_t first = (uint32_t)((uint64_t)L * tiles / G);
+  const uint32_t n = (uint32_t)((uint64_t)(L + 1) * tiles / G) - first;  // 1 or 2
+
+  // phase 1: both loads first (a workgroup with one tile loads it twice, the
+  // second copy in bounds and never used), then the two maxima.  Two named
+  // tiles rather than an array: every access is then to a fixed register,
+  // never to a stack copy.
+  ColTile<uint16_t> t0, t1;
+  bool v0, v1;
+  t0.load(row_rht_patch(x, a, first, tiles_x, v0), a.ld);
+  t1.load(row_rht_patch(x, a, first + n - 1u, tiles_x, v1), a.ld);
+  v1 = v1 && n > 1u;
+  float mx = 0.0f, mu = 0.0f;
+  auto maxima = [&](const ColTile<uint16_t>& t) {
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+      float u[16];
+      t.template column<true>(k, u, a.sign_mask);  // sign flips do not change |x|
+#pragma unroll
+      for (int j = 0; j < 16; j++) mx = fmaxf(mx, fabsf(u[j]));
+      fwht16(u);  // the 1/4 is applied once, to the maximum
+#pragma unroll
+      for (int j = 0; j < 16; j++) mu = fmaxf(mu, fabsf(u[j]));
+    }
+  };
+  if (v0) maxima(t0);
+  if (v1) maxima(t1);
+  // keep the tiles in registers through the exchange (the loads are of
+  // read-only memory, so the compiler would otherwise read them again)
+  t0.opaque();
+  t1.opaque();
+  // non-negative floats: integer order is float order
+  uint32_t bx = __float_as_uint(mx), bu = __float_as_uint(0.25f * mu);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    bx = max(bx, (uint32_t)__shfl_xor(bx, off));
+    bu = max(bu, (uint32_t)__shfl_xor(bu, off));
+  }
+  if (lane == 0) {
+    wave_max[0][tid >> 6] = bx;
+    wave_max[1][tid >> 6] = bu;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    const uint32_t wx = max(max(wave_max[0][0], wave_max[0][1]), max(wave_max[0][2], wave_max[0][3]));
+    const uint32_t wu = max(max(wave_max[1][0], wave_max[1][1]), max(wave_max[1][2], wave_max[1][3]));
+    uint32_t gx = 0u, gu = 0u, nrec = 0u;
+    sh_role = grid_arrive_wait<DeviceOps>(slot, G, L, wx, epoch, spin_limit, &gx, &nrec, wu, &gu);
+    sh_x = gx;
+    sh_u = gu;
+    sh_n = nrec;
+  }
+  __syncthreads();
+  if (sh_role == kGridGaveUp) return;  // the publisher encodes this workgroup's tiles
+
+  // phase 2: both encodings of every held tile
+  const float amax_x = __uint_as_float(sh_x), amax_u = __uint_as_float(sh_u);
+  const float s_row = encode_scale(amax_x), s_rht = encode_scale(amax_u);
+  if (tid < 128)
+    rtab_row[tid] = element_scale(tid, s_row);
+  else
+    rtab_rht[tid - 128] = element_scale(tid - 128, s_rht);
+  __syncthreads();
+  row_rht_tile<uint16_t, 0, 0>(t0, v0, first, tiles_x, a, s_row, s_rht, rtab_row, rtab_rht, lcodes,
+                               lscales);
+  if (n > 1u)
+    row_rht_tile<uint16_t, 0, 0>(t1, v1, first + 1, tiles_x, a, s_row, s_rht, rtab_row, rtab_rht,
+                                 lcodes, lscales);
+  if (sh_role != kGridPublisher) return;
+
+  // the publisher: the tensor outputs, and the tiles of the workgroups that
+  // gave up, read again from memory
+  if (tid == 0) {
+    row_ts[0] = 1.0f / s_row;
+    row_amax[0] = amax_x;
+    rht_ts[0] = 1.0f / s_rht;
+    rht_amax[0] = amax_u;
+  }
+  for (uint32_t i = 0; i < sh_n; i++) {
+    __shared__ uint32_t sh_w;
+    if (tid == 0) sh_w = grid_recovered<DeviceOps>(slot, i, uint64_t(1) << 22);
+    __syncthreads();
+    const uint32_t w = sh_w;
+    __syncthreads();
+    if (w >= G) continue;  // never stored (cannot happen: the entry follows its swap)
+    const uint32_t f = (uint32_t)((uint64_t)w * tiles / G);
+    const uint32_t e = (uint32_t)((uint64_t)(w + 1) * tiles / G);
+    for (uint32_t id = f; id < e; id++) {
+      bool ok;
+      ColTile<uint16_t> one;
+      one.load(row_rht_patch(x, a, id, tiles_x, ok), a.ld);
+      row_rht_tile<uint16_t, 0, 0>(one, ok, id, tiles_x, a, s_row, s_rht, rtab_row, rtab_rht,
+                                   lcodes, lscales);
+    }
+  }
 }
 
 // amax of the RHT output (and, if amax_plain is not null, of the input itself,
@@ -1112,8 +1245,46 @@ hipError_t launch_rht_quantize(const void* x, int dt, int64_t tokens, int64_t co
                          amax, s);
 }
 
-// Both quantizations of one tensor: one read for the two amaxes, then the
-// row cast and the RHT column cast.
+// Workgroups of k_row_rht_1pass that fit on one compute unit.
+static int row_rht_1pass_occupancy() {
+  static const int occ = [] {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_row_rht_1pass, 256, 0) != hipSuccess) n = 0;
+    return n;
+  }();
+  return occ;
+}
+
+// The single-pass fused call where it applies (bf16 input, RNE on both
+// copies, tiles that fit in the resident grid's registers, an exchange slot
+// free); *done = false and nothing enqueued otherwise.
+static hipError_t try_row_rht_1pass(const void* x, int dt, uint32_t tiles_x, uint32_t tiles_y,
+                                    int row_rnd, int rht_rnd, const RowRhtArgs& a, float* row_ts,
+                                    float* row_amax, float* rht_ts, float* rht_amax,
+                                    hipStream_t s, bool* done) {
+  *done = false;
+  if (dt != 0 || row_rnd != 0 || rht_rnd != 0) return hipSuccess;
+  const int occ = row_rht_1pass_occupancy();
+  if (occ < 1) return hipSuccess;
+  const int64_t tiles = (int64_t)tiles_x * tiles_y;
+  const int64_t resident = std::min<int64_t>((int64_t)occ * cu_count(), kSyncMaxGrid);
+  if (tiles > resident * kRowRht1Tiles) return hipSuccess;  // does not fit on chip
+  SinglePassTicket tk;
+  if (!single_pass_ticket(s, &tk)) return hipSuccess;
+  // every resident workgroup (more loads in flight), each with one or two tiles
+  const unsigned grid = (unsigned)std::min<int64_t>(resident, tiles);
+  k_row_rht_1pass<<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(x), a, (uint32_t)tiles, tiles_x,
+                                       row_ts, row_amax, rht_ts, rht_amax, tk.slot, tk.epoch, tk.spin);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  *done = true;
+  single_pass_launched(tk);
+  return hipSuccess;
+}
+
+// Both quantizations of one tensor: in one pass where the tensor fits on
+// chip, else one read for the two amaxes, then the row cast and the RHT
+// column cast.
 hipError_t launch_quantize_row_rht(const void* x, int dt, int64_t tokens, int64_t cols, int64_t ld,
                                    int row_rnd, uint64_t row_seed, uint8_t* row_codes,
                                    uint8_t* row_scales, float* row_ts, float* row_amax,
@@ -1121,13 +1292,17 @@ hipError_t launch_quantize_row_rht(const void* x, int dt, int64_t tokens, int64_
                                    uint8_t* rht_codes, uint8_t* rht_scales, float* rht_ts,
                                    float* rht_amax, hipStream_t s) {
   sign_mask &= 0xFFFFu;
-  hipError_t e = launch_rht_amax(x, dt, tokens, cols, ld, sign_mask, rht_amax, row_amax, s);
-  if (e != hipSuccess) return e;
-  // both casts from one read of x
   const uint32_t tiles_x = (uint32_t)((cols + kColCols - 1) / kColCols);
   const uint32_t tiles_y = (uint32_t)((tokens + kColTok - 1) / kColTok);
   const RowRhtArgs a{tokens, cols, ld, sign_mask, row_codes, row_scales, sr_key(row_seed),
                      rht_codes, rht_scales, sr_key(rht_seed)};
+  bool done = false;
+  hipError_t e = try_row_rht_1pass(x, dt, tiles_x, tiles_y, row_rnd, rht_rnd, a, row_ts, row_amax,
+                                   rht_ts, rht_amax, s, &done);
+  if (e != hipSuccess || done) return e;
+  e = launch_rht_amax(x, dt, tokens, cols, ld, sign_mask, rht_amax, row_amax, s);
+  if (e != hipSuccess) return e;
+  // both casts from one read of x
 #define ROW_RHT_LAUNCH(T, RR, RH)                                                                 \
   k_cast_row_rht<T, RR, RH><<<dim3(tiles_x, tiles_y), 256, 0, s>>>(static_cast<const T*>(x), a,   \
                                                                 row_amax, row_ts, rht_amax, rht_ts)

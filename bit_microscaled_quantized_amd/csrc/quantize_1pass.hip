@@ -295,6 +295,28 @@ GridSyncSlot* stream_sync_slot(hipStream_t s) {
   return i < 0 ? nullptr : g_slots[dev] + i;
 }
 
+bool single_pass_ticket(hipStream_t s, SinglePassTicket* t) {
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &cap) != hipSuccess || cap != hipStreamCaptureStatusNone) return false;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return false;
+  std::lock_guard<std::mutex> lock(g_mu);
+  if (g_passes == 2 || !device_setup(dev)) return false;
+  const int si = slot_of(dev, s);
+  if (si < 0) return false;
+  if (++g_epoch[dev][si] == 0u) g_epoch[dev][si] = 1u;  // 0 is the zeroed slot's value
+  t->slot = g_slots[dev] + si;
+  t->epoch = g_epoch[dev][si];
+  t->spin = g_spin_limit;
+  t->dev = dev;
+  return true;
+}
+
+void single_pass_launched(const SinglePassTicket& t) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  g_launches[t.dev]++;
+}
+
 // Try the single-pass row-1D quantization; *done = false (and nothing
 // enqueued) when it does not apply: strided rows, a tensor larger than the
 // resident grid holds, a stream under graph capture, or all exchange slots of
@@ -304,24 +326,16 @@ hipError_t try_quantize_row_1pass(const void* x, int dt, int64_t rows, int64_t c
                                   float* tensor_scale, float* amax, hipStream_t s, bool* done) {
   *done = false;
   if (ld != cols) return hipSuccess;
-  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
-  if (hipStreamIsCapturing(s, &cap) != hipSuccess || cap != hipStreamCaptureStatusNone)
-    return hipSuccess;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return hipSuccess;
-  GridSyncSlot* slot = nullptr;
-  int per_cu = 0, cus = 0, si = -1;
-  uint64_t spin = 0;
+  int per_cu = 0, cus = 0;
   {
     std::lock_guard<std::mutex> lock(g_mu);
-    if (g_passes == 2 || !device_setup(dev)) return hipSuccess;
+    if (!device_setup(dev)) return hipSuccess;
     per_cu = g_res[dev].per_cu[dt == 0 ? 0 : 1][rnd];
     cus = g_res[dev].cus;
-    si = per_cu > 0 ? slot_of(dev, s) : -1;
-    if (si < 0) return hipSuccess;
-    slot = g_slots[dev] + si;
-    spin = g_spin_limit;
   }
+  if (per_cu < 1) return hipSuccess;
   const int NB = dt == 0 ? blocks_per_lane<uint16_t>() : blocks_per_lane<float>();
   const int64_t nblocks = rows * cols / 16;
   const int64_t lanes_needed = (nblocks + NB - 1) / NB;
@@ -333,12 +347,11 @@ hipError_t try_quantize_row_1pass(const void* x, int dt, int64_t rows, int64_t c
   grid = std::min<int64_t>(max_grid, std::max<int64_t>(grid, (nblocks + 255) / 256));
   const uint32_t rounds = (uint32_t)((nblocks + grid * 256 - 1) / (grid * 256));
   const uint32_t key = sr_key(seed);
-  uint32_t epoch = 0;
-  {
-    std::lock_guard<std::mutex> lock(g_mu);
-    if (++g_epoch[dev][si] == 0u) g_epoch[dev][si] = 1u;  // 0 is the zeroed slot's value
-    epoch = g_epoch[dev][si];
-  }
+  SinglePassTicket tk;
+  if (!single_pass_ticket(s, &tk)) return hipSuccess;
+  GridSyncSlot* slot = tk.slot;
+  const uint32_t epoch = tk.epoch;
+  const uint64_t spin = tk.spin;
   const uint32_t nb32 = (uint32_t)nblocks;
   if (dt == 0) {
     if (rnd == 0)
@@ -362,8 +375,7 @@ hipError_t try_quantize_row_1pass(const void* x, int dt, int64_t rows, int64_t c
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   *done = true;
-  std::lock_guard<std::mutex> lock(g_mu);
-  g_launches[dev]++;
+  single_pass_launched(tk);
   return hipSuccess;
 }
 

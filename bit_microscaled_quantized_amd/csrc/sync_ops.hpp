@@ -49,6 +49,13 @@ struct DeviceOps {
   static __device__ uint64_t exchange64(uint64_t* p, uint64_t v) {
     return __hip_atomic_exchange(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
+  static __device__ uint64_t exchange64_release(uint64_t* p, uint64_t v) {
+    drain();
+    return __hip_atomic_exchange(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  static __device__ void store64_relaxed(uint64_t* p, uint64_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
   static __device__ uint64_t load64(uint64_t* p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }

@@ -76,6 +76,15 @@ typedef enum { NVFP4_RNE = 0, NVFP4_SR = 1 } nvfp4_rounding;
 typedef enum { NVFP4_ROW_1D = 0, NVFP4_COL_1D = 1, NVFP4_TILE_2D = 2 } nvfp4_layout;
 
 /*
+ * Arguments that take one of these enums (dt, layout, rnd, out_dt, and the
+ * status of nvfp4_status_str) are declared `int`: the width is fixed on every
+ * C and C++ compiler and foreign-function binding, and a value outside the
+ * enum reaches the library, which answers NVFP4_EINVAL (nvfp4_status_str:
+ * "unknown nvfp4 status") instead of depending on how the caller's language
+ * converts it.
+ */
+
+/*
  * nvfp4_quantize -- amax, two-level scales and E2M1 cast of one tensor.
  * ("Formato NVFP4" and techniques 3-4 of "Metodologia Proposta".)
  *
@@ -148,7 +157,12 @@ nvfp4_status nvfp4_rht_quantize(const void *x, int dt, int64_t tokens, int64_t c
  *                      rht_codes, rht_scales, rht_tensor_scale, rht_amax)
  * (same layouts, SR indices and errors), but both tensor amaxes (of x and of
  * its RHT) come from ONE read of x, saving a full pass over the tensor.
- * The two output sets must not overlap.
+ * With RNE on both copies, a bf16 tensor whose 256 x 128 tiles fit in the
+ * registers of one resident grid (two per workgroup: up to 8192 x 6144 on
+ * a 256-CU MI355X) is read only once in all: one launch takes both maxima,
+ * exchanges them between its workgroups and encodes from registers (the
+ * single-pass path below; same outputs).  The two output sets must not
+ * overlap.
  */
 nvfp4_status nvfp4_quantize_row_rht(const void *x, int dt, int64_t tokens, int64_t cols,
                                     int64_t ld_x, int row_rnd, uint64_t row_seed,
@@ -190,6 +204,11 @@ nvfp4_status nvfp4_quantize_row_rht(const void *x, int dt, int64_t tokens, int64
  *   inputs).  NULL, or fewer bytes than needed, runs without the split (same
  *   result up to FP32 summation order).  The workspace is in use until the
  *   call's work on `stream` completes.
+ *   The same call without the workspace pair, (M, N, K, a_codes, a_scales,
+ *   a_tensor_scale, b_codes, b_scales, b_scale_rowdiv, b_tensor_scale, c,
+ *   ldc, beta, stream), is nvfp4_gemm_noalloc below; it splits into the
+ *   library's own static scratch and gives, bit for bit, the result of this
+ *   call with a large enough workspace.
  */
 nvfp4_status nvfp4_gemm(int64_t M, int64_t N, int64_t K, const uint8_t *a_codes,
                         const uint8_t *a_scales, const float *a_tensor_scale,
@@ -270,8 +289,9 @@ nvfp4_status nvfp4_dequantize(const uint8_t *codes, const uint8_t *scales, int32
 nvfp4_status nvfp4_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int64_t *bytes);
 
 /*
- * Controls and counters of the single-pass quantize path (nvfp4_quantize,
- * ROW_1D).  Process-wide settings, safe to call from any thread.
+ * Controls and counters of the single-pass quantize paths (nvfp4_quantize
+ * ROW_1D, nvfp4_quantize_row_rht on bf16).  Process-wide settings, safe to
+ * call from any thread.
  *   nvfp4_set_quantize_passes(passes): 0 (default) picks the single pass where
  *     it applies; 2 always takes the two-pass path.  Other values: EINVAL.
  *   nvfp4_set_sync_spin_limit(polls): how many times a workgroup polls the

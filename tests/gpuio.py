@@ -119,18 +119,26 @@ def gpu_rht_quantize(x: np.ndarray, sign_mask: int, rnd: int = 0, seed: int = 0)
 
 
 def gpu_quantize_row_rht(x: np.ndarray, sign_mask: int, row_rnd: int, row_seed: int, rht_rnd: int,
-                         rht_seed: int) -> tuple[dict, dict]:
+                         rht_seed: int, ld: int | None = None, pad=0) -> tuple[dict, dict]:
     """nvfp4_quantize_row_rht: (row-1D outputs, RHT column outputs), both as
-    returned by gpu_quantize / gpu_rht_quantize."""
+    returned by gpu_quantize / gpu_rht_quantize.  With ld > cols the input
+    rows are ld elements apart and the gap holds `pad` (which no output may
+    depend on)."""
     torch = torch_cuda()
     tokens, cols = x.shape
-    xd = to_dev(x)
+    if ld is not None and ld != cols:
+        padded = np.full((tokens, ld), pad, dtype=x.dtype)
+        padded[:, :cols] = x
+        xd = to_dev(padded)
+    else:
+        ld = cols
+        xd = to_dev(x)
     g = Guarded()
     u8 = torch.uint8
     rc, rs = g.alloc((tokens, cols // 2), u8), g.alloc((tokens, cols // 16), u8)
     hc, hs = g.alloc((cols, tokens // 2), u8), g.alloc((cols, tokens // 16), u8)
     rts, ram, hts, ham = (g.alloc((1,), torch.float32) for _ in range(4))
-    nv.nvfp4_quantize_row_rht(xd, dtype_code(x), tokens, cols, cols, row_rnd, row_seed, rc, rs, rts, ram,
+    nv.nvfp4_quantize_row_rht(xd, dtype_code(x), tokens, cols, ld, row_rnd, row_seed, rc, rs, rts, ram,
                               sign_mask, rht_rnd, rht_seed, hc, hs, hts, ham)
     torch.cuda.synchronize()
     g.check()

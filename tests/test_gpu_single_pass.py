@@ -12,7 +12,15 @@ against the two-pass path: codes, scales, tensor scale and amax bit for bit.
   workgroups that arrive before the tensor amax is published give up and are
   counted, every kernel ends, the last workgroup to leave encodes their
   blocks from memory, so the output is still exact, and the next call on the
-  same slot is exact too."""
+  same slot is exact too.
+
+The single-pass fused call (nvfp4_quantize_row_rht on bf16 that fits on
+chip, RNE on both copies: the row-1D copy and the RHT column copy, two maxima
+exchanged) gets the same checks: the 8192 x 5120 X of the FFN up-projection
+whole, ragged shapes and strided rows (with huge values in the row gaps,
+which must not reach either amax), the two-pass path bit for bit, the cases
+that must take two passes (stochastic rounding on either copy, FP32 input,
+tensors beyond the capacity), and forced give-ups."""
 import numpy as np
 import pytest
 
@@ -152,3 +160,120 @@ def test_forced_give_up_ends_and_recovers(ora):
         n2, g2 = _launches()
         assert n2 == n1 + 1 and g2 == g1
         _same(g, ref)
+
+
+# --- single-pass fused row-1D + RHT column call ---------------------------------
+
+ROW_RHT_RNDS = [(nv.NVFP4_RNE, nv.NVFP4_RNE), (nv.NVFP4_SR, nv.NVFP4_SR), (nv.NVFP4_RNE, nv.NVFP4_SR),
+                (nv.NVFP4_SR, nv.NVFP4_RNE)]
+
+
+def _row_rht_vs_oracle(ora, x, mask, rr, rs, hr, hs, got):
+    g_row, g_rht = got
+    _same(g_row, ora.quantize(x, ora.ROW_1D, rr, rs))
+    _same(g_rht, ora.rht_quantize(x, mask, hr, hs))
+
+
+def _takes_single_pass(rr, hr):
+    """The fused call's single pass is for RNE on both copies."""
+    return rr == nv.NVFP4_RNE and hr == nv.NVFP4_RNE
+
+
+@pytest.mark.parametrize("case", ["ffn_up_x", "stress_dy"])
+def test_single_pass_row_rht_whole_tensor(ora, case):
+    """The fused calls of the two workloads whose operand is 8192 x 5120 bf16
+    (X of the FFN up-projection, RNE: one pass; dY of the large-token stress
+    layer, SR: two passes): every code and scale against the oracle and
+    against the forced two-pass path."""
+    if case == "ffn_up_x":
+        d = synth.ffn_up()
+        x, mask, rr, rs, hr, hs = d["x"], d["sign_mask"], nv.NVFP4_RNE, 0, nv.NVFP4_RNE, 0
+    else:
+        x = synth.lognormal_signed(17, (8192, 5120))
+        mask, rr, rs, hr, hs = synth.sign_mask16(18), nv.NVFP4_SR, 19, nv.NVFP4_SR, 20
+    x = synth.f32_to_bf16_bits(x)
+    n0, g0 = _launches()
+    got = gpuio.gpu_quantize_row_rht(x, mask, rr, rs, hr, hs)
+    n1, g1 = _launches()
+    assert n1 == n0 + int(_takes_single_pass(rr, hr)) and g1 == g0
+    _row_rht_vs_oracle(ora, x, mask, rr, rs, hr, hs, got)
+    nv.nvfp4_set_quantize_passes(2)
+    two = gpuio.gpu_quantize_row_rht(x, mask, rr, rs, hr, hs)
+    assert _launches()[0] == n1
+    _same(got[0], two[0])
+    _same(got[1], two[1])
+
+
+ROW_RHT_SHAPES = [(16, 16), (48, 80), (272, 528), (1040, 4112), (4096, 2064)]
+
+
+@pytest.mark.parametrize("shape", ROW_RHT_SHAPES)
+@pytest.mark.parametrize("rnds", ROW_RHT_RNDS)
+def test_single_pass_row_rht_ragged(ora, shape, rnds):
+    """Tiles cut by the tensor's edges in both directions, and workgroups
+    holding one or two tiles; the path follows the rounding modes."""
+    x = synth.f32_to_bf16_bits(synth.normal_with_outliers(400 + shape[1], shape))
+    mask = synth.sign_mask16(shape[0] + 3)
+    rr, hr = rnds
+    n0, g0 = _launches()
+    got = gpuio.gpu_quantize_row_rht(x, mask, rr, 51, hr, 52)
+    n1, g1 = _launches()
+    assert n1 == n0 + int(_takes_single_pass(rr, hr)) and g1 == g0
+    _row_rht_vs_oracle(ora, x, mask, rr, 51, hr, 52, got)
+
+
+def test_single_pass_row_rht_strided_rows(ora):
+    """Rows 448 elements apart beyond their 400; the gaps hold the largest
+    finite bf16 values, which neither maximum may see."""
+    x = synth.f32_to_bf16_bits(synth.student_t(71, (528, 400)))
+    n0, _ = _launches()
+    for rr, hr in ((nv.NVFP4_RNE, nv.NVFP4_RNE), (nv.NVFP4_SR, nv.NVFP4_SR)):
+        got = gpuio.gpu_quantize_row_rht(x, 0x1234, rr, 61, hr, 62, ld=448, pad=np.uint16(0x7F7F))
+        _row_rht_vs_oracle(ora, x, 0x1234, rr, 61, hr, 62, got)
+    assert _launches()[0] == n0 + 1
+
+
+def test_row_rht_two_pass_where_single_pass_does_not_apply(ora):
+    # FP32 input
+    x = synth.normal(81, (256, 512))
+    n0, _ = _launches()
+    got = gpuio.gpu_quantize_row_rht(x, 0x0F0F, nv.NVFP4_RNE, 3, nv.NVFP4_RNE, 4)
+    assert _launches()[0] == n0
+    _row_rht_vs_oracle(ora, x, 0x0F0F, nv.NVFP4_RNE, 3, nv.NVFP4_RNE, 4, got)
+    # 8192 x 20480 bf16 (5120 tiles) is beyond the on-chip capacity
+    torch = gpuio.torch_cuda()
+    T, C = 8192, 20480
+    xb = torch.zeros((T, C), dtype=torch.int16, device="cuda")
+    u8 = dict(dtype=torch.uint8, device="cuda")
+    f32 = dict(dtype=torch.float32, device="cuda")
+    rc, rs = torch.empty((T, C // 2), **u8), torch.empty((T, C // 16), **u8)
+    hc, hs = torch.empty((C, T // 2), **u8), torch.empty((C, T // 16), **u8)
+    f = [torch.empty(1, **f32) for _ in range(4)]
+    nv.nvfp4_quantize_row_rht(xb, nv.NVFP4_BF16, T, C, C, nv.NVFP4_RNE, 0, rc, rs, f[0], f[1], 0x00FF,
+                              nv.NVFP4_RNE, 0, hc, hs, f[2], f[3])
+    torch.cuda.synchronize()
+    assert _launches()[0] == n0
+    assert [float(t.item()) for t in f] == [1.0, 0.0, 1.0, 0.0]
+    # zero magnitudes everywhere (the transform's sign flips make -0, code 8)
+    assert not rc.any().item() and not (hc & 0x77).any().item()
+
+
+def test_forced_give_up_row_rht(ora):
+    """Spin limit zero on the fused call: early workgroups give up and are
+    counted, the publisher encodes their tiles from memory, the outputs are
+    exact, and the next call on the slot gives up nothing."""
+    d = synth.ffn_up()
+    x = synth.f32_to_bf16_bits(d["x"])
+    mask = d["sign_mask"]
+    n0, g0 = _launches()
+    nv.nvfp4_set_sync_spin_limit(0)
+    got = gpuio.gpu_quantize_row_rht(x, mask, nv.NVFP4_RNE, 0, nv.NVFP4_RNE, 0)
+    n1, g1 = _launches()
+    assert n1 == n0 + 1
+    assert g1 > g0, "with no polling the early workgroups must give up"
+    _row_rht_vs_oracle(ora, x, mask, nv.NVFP4_RNE, 0, nv.NVFP4_RNE, 0, got)
+    nv.nvfp4_set_sync_spin_limit(1 << 14)
+    again = gpuio.gpu_quantize_row_rht(x, mask, nv.NVFP4_RNE, 0, nv.NVFP4_RNE, 0)
+    assert _launches() == (n1 + 1, g1)
+    _same(got[0], again[0])
+    _same(got[1], again[1])

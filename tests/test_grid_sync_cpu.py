@@ -8,7 +8,10 @@ the publisher (each block written exactly once), that nothing hangs, and
 that the slot is back at its idle state for the next launch on it.
 
 * full residency: launches of G = 1 .. 200 workgroups (random start delays)
-  on one slot, nobody gives up;
+  on one slot, nobody gives up; every other launch also exchanges a second
+  maximum (the fused row + RHT cast's), which every workgroup that stays
+  must learn exactly, and which the slot's result word then holds with the
+  launch's epoch;
 * limited residency (at most R < G workgroups run at once, the rest start
   only when one ends, as on a GPU whose grid is partly displaced): workgroups
   that wait past the spin limit give up and are counted, the publisher
@@ -58,6 +61,8 @@ struct CpuOps {
     return at64(p).compare_exchange_strong(expected, desired, std::memory_order_acq_rel);
   }
   static uint64_t exchange64(uint64_t* p, uint64_t v) { return at64(p).exchange(v, std::memory_order_acq_rel); }
+  static uint64_t exchange64_release(uint64_t* p, uint64_t v) { return at64(p).exchange(v, std::memory_order_acq_rel); }
+  static void store64_relaxed(uint64_t* p, uint64_t v) { at64(p).store(v, std::memory_order_relaxed); }
   static uint64_t load64(uint64_t* p) { return at64(p).load(std::memory_order_acquire); }
   static uint32_t load_relaxed(uint32_t* p) { return at(p).load(std::memory_order_relaxed); }
   static void store_relaxed(uint32_t* p, uint32_t v) { at(p).store(v, std::memory_order_relaxed); }
@@ -87,30 +92,35 @@ static bool idle(const GridSyncSlot* s) {
   return !s->top.arrive && !s->top.amax && !s->top.amax2;
 }
 
-// one launch of G workgroups; returns how many gave up
+// one launch of G workgroups (with `two`, exchanging a second maximum too);
+// returns how many gave up
 static int launch(GridSyncSlot* s, uint32_t epoch, int G, int resident, uint64_t spin,
-                  std::mt19937& rng) {
-  std::vector<uint32_t> vals(G), got(G, 0xFFFFFFFFu);
+                  std::mt19937& rng, bool two = false) {
+  std::vector<uint32_t> vals(G), got(G, 0xFFFFFFFFu), vals2(G), got2(G, 0xFFFFFFFFu);
   std::vector<int> writes(G, 0);  // how many times workgroup i's blocks were written
   std::vector<int> ok(G, 0);
   uint32_t want = 0;
+  uint32_t want2 = 0;
   for (int i = 0; i < G; i++) { vals[i] = rng() >> 1; want = vals[i] > want ? vals[i] : want; }
+  for (int i = 0; i < G; i++) { vals2[i] = rng() >> 1; want2 = vals2[i] > want2 ? vals2[i] : want2; }
   std::vector<int> delay(G);
   for (int i = 0; i < G; i++) delay[i] = (int)(rng() % 200);
   std::mutex wmu;
   int lasts = 0;
-  uint32_t last_amax = 0xFFFFFFFFu;
+  uint32_t last_amax = 0xFFFFFFFFu, last_amax2 = 0xFFFFFFFFu;
   Residency res(resident);
   std::vector<std::thread> th;
   for (int i = 0; i < G; i++)
     th.emplace_back([&, i] {
       res.enter();
       std::this_thread::sleep_for(std::chrono::microseconds(delay[i]));
-      uint32_t bits = 0, n = 0;
+      uint32_t bits = 0, n = 0, bits2 = 0;
       const nvfp4::GridRole role =
-          nvfp4::grid_arrive_wait<CpuOps>(s, (uint32_t)G, (uint32_t)i, vals[i], epoch, spin, &bits, &n);
+          nvfp4::grid_arrive_wait<CpuOps>(s, (uint32_t)G, (uint32_t)i, vals[i], epoch, spin, &bits, &n,
+                                          vals2[i], two ? &bits2 : nullptr);
       ok[i] = role != nvfp4::kGridGaveUp;
       got[i] = bits;
+      got2[i] = bits2;
       if (ok[i]) { std::lock_guard<std::mutex> l(wmu); writes[i]++; }
       if (role == nvfp4::kGridPublisher) {
         std::vector<uint32_t> ws;
@@ -118,6 +128,7 @@ static int launch(GridSyncSlot* s, uint32_t epoch, int G, int resident, uint64_t
         std::lock_guard<std::mutex> l(wmu);
         lasts++;
         last_amax = bits;
+        last_amax2 = bits2;
         for (uint32_t w : ws) {
           CHECK(w < (uint32_t)G);
           if (w < (uint32_t)G) writes[w]++;
@@ -128,12 +139,20 @@ static int launch(GridSyncSlot* s, uint32_t epoch, int G, int resident, uint64_t
   for (auto& t : th) t.join();
   int gave_up = 0;
   for (int i = 0; i < G; i++) {
-    if (ok[i]) CHECK(got[i] == want);
-    else gave_up++;
+    if (ok[i]) {
+      CHECK(got[i] == want);
+      if (two) CHECK(got2[i] == want2);
+    } else {
+      gave_up++;
+    }
     CHECK(writes[i] == 1);
   }
   CHECK(lasts == 1);
   CHECK(last_amax == want);
+  if (two) {
+    CHECK(last_amax2 == want2);
+    CHECK(s->result2 == (((uint64_t)want2 << 32) | epoch));
+  }
   // the gate is closed for this epoch and carries the tensor amax
   CHECK((s->gate & nvfp4::kGateTagMask) == nvfp4::gate_tag(epoch));
   CHECK((s->gate & nvfp4::kGateClosed) != 0);
@@ -187,7 +206,7 @@ int main() {
   const int Gs[] = {1, 2, 3, 15, 16, 17, 33, 64, 200};
   for (int rep = 0; rep < 20 && !fails; rep++)
     for (int G : Gs) {
-      CHECK(launch(&slot, ++epoch, G, G, uint64_t(1) << 22, rng) == 0);
+      CHECK(launch(&slot, ++epoch, G, G, uint64_t(1) << 22, rng, rep % 2 == 1) == 0);
       if (fails) break;
     }
   CHECK(slot.gave_ups == 0);
@@ -195,20 +214,20 @@ int main() {
   // limited residency: must end, some give up, all blocks covered, the slot recovers
   for (int rep = 0; rep < 10; rep++) {
     const uint32_t before = slot.gave_ups;
-    const int g = launch(&slot, ++epoch, 40, 6, 2000, rng);
+    const int g = launch(&slot, ++epoch, 40, 6, 2000, rng, rep % 2 == 0);
     CHECK(g >= 1 && g <= 39);
     CHECK(slot.gave_ups == before + (uint32_t)g);
     CHECK(launch(&slot, ++epoch, 40, 40, uint64_t(1) << 22, rng) == 0);
     if (fails) break;
   }
   // spin limit zero, full residency
-  for (int rep = 0; rep < 20 && !fails; rep++) launch(&slot, ++epoch, 24, 24, 0, rng);
+  for (int rep = 0; rep < 20 && !fails; rep++) launch(&slot, ++epoch, 24, 24, 0, rng, rep % 2 == 0);
   // no-wait grid maxima, alternating with single-pass launches on the slot
   const int Ms[] = {1, 2, 15, 16, 17, 31, 100, 300};
   for (int rep = 0; rep < 8 && !fails; rep++)
     for (int G : Ms) {
       max_launch(&slot, G, rep % 2 ? 4 : G, rng);
-      CHECK(launch(&slot, ++epoch, 20, 20, uint64_t(1) << 22, rng) == 0);
+      CHECK(launch(&slot, ++epoch, 20, 20, uint64_t(1) << 22, rng, rep % 2 == 0) == 0);
       if (fails) break;
     }
   std::printf("%s\n", fails ? "FAILED" : "OK");
