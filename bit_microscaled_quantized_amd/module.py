@@ -19,7 +19,10 @@ saved activations are 4.5 bits per element.  Outputs and gradients come back in
 the dtype of the corresponding input (BF16 through nvfp4_gemm_bf16, FP32
 through nvfp4_gemm).  Every quantize, GEMM and rounding step runs in libnvfp4
 on torch's current stream; this module only allocates the buffers and orders
-the calls.
+the calls.  The buffers come from PyTorch's caching allocator, so from the
+second step on they are blocks it already holds and a step makes no device
+allocation call.  W is quantized once per forward (the weights change with
+every optimizer step); backward reuses that call's transposed copy.
 
 Shapes: x [..., in_features] with the flattened token count a multiple of 64,
 in_features and out_features multiples of 64 (each is the K of one GEMM).

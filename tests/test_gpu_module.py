@@ -206,6 +206,31 @@ def test_nvfp4_linear_is_reproducible_and_bf16_bypass():
     assert torch.equal(plain(x), torch.nn.functional.linear(x, plain.weight))
 
 
+def test_nvfp4_linear_steady_state_adds_no_device_segment():
+    """Once the first steps have filled PyTorch's cache, forward + backward
+    take every buffer (quantized copies, GEMM outputs, split workspaces) from
+    blocks it already holds: no new device segment, so no allocation call."""
+    torch = gpuio.torch_cuda()
+    from bit_microscaled_quantized_amd.module import NVFP4Linear
+    x = torch.from_numpy(synth.normal(83, (512, 256))).cuda().to(torch.bfloat16)
+    dy = torch.from_numpy(synth.normal(84, (512, 384)) * 1e-3).cuda().to(torch.bfloat16)
+    layer = NVFP4Linear(256, 384, seed=7)
+
+    def step():
+        xi = x.clone().requires_grad_(True)
+        layer(xi).backward(dy)
+        layer.weight.grad = None
+
+    for _ in range(2):
+        step()
+    torch.cuda.synchronize()
+    before = torch.cuda.memory_stats()["segment.all.allocated"]
+    for _ in range(3):
+        step()
+    torch.cuda.synchronize()
+    assert torch.cuda.memory_stats()["segment.all.allocated"] == before
+
+
 def test_nvfp4_linear_rejects_unsupported_shapes():
     torch = gpuio.torch_cuda()
     from bit_microscaled_quantized_amd.module import NVFP4Linear
