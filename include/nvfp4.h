@@ -40,7 +40,7 @@
  *     may overlap (but not while sharing a GEMM workspace).  Its state is a
  *     per-device cache of the compute-unit count and occupancy, and two static
  *     device arrays per device: the exchange slots of the quantize calls' amax
- *     reductions (64 slots of 18.4 KiB, one per stream in use, with a host
+ *     reductions (64 slots of 18.25 KiB, one per stream in use, with a host
  *     epoch counter each) and the split workspace of nvfp4_gemm_noalloc
  *     (64 MiB).
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All

@@ -277,3 +277,44 @@ def test_forced_give_up_row_rht(ora):
     assert _launches() == (n1 + 1, g1)
     _same(got[0], again[0])
     _same(got[1], again[1])
+
+
+def test_single_pass_row_rht_on_two_streams(ora):
+    """Two streams run the fused single pass on different tensors without
+    synchronizing in between, each on its own exchange slot, interleaved with
+    row-1D single passes on the same streams.  Grids of the two streams may
+    displace each other; workgroups that then give up are covered, so only
+    the outputs and the launch count are asserted."""
+    torch = gpuio.torch_cuda()
+    T, C = 2048, 5120
+    xs = [synth.f32_to_bf16_bits(synth.student_t(90 + i, (T, C))) for i in range(2)]
+    devs = [gpuio.to_dev(x) for x in xs]
+    masks = [0x3C3C, 0x0FF0]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    u8 = dict(dtype=torch.uint8, device="cuda")
+    f32 = dict(dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    n0, _ = _launches()
+    for rep in range(3):
+        outs = []
+        for i, st in enumerate(streams):
+            with torch.cuda.stream(st):
+                o = dict(rc=torch.empty((T, C // 2), **u8), rs=torch.empty((T, C // 16), **u8),
+                         hc=torch.empty((C, T // 2), **u8), hs=torch.empty((C, T // 16), **u8),
+                         qc=torch.empty((T, C // 2), **u8), qs=torch.empty((T, C // 16), **u8),
+                         f=[torch.empty(1, **f32) for _ in range(6)])
+                nv.nvfp4_quantize_row_rht(devs[i], nv.NVFP4_BF16, T, C, C, nv.NVFP4_RNE, 0, o["rc"], o["rs"],
+                                          o["f"][0], o["f"][1], masks[i], nv.NVFP4_RNE, 0, o["hc"], o["hs"],
+                                          o["f"][2], o["f"][3])
+                nv.nvfp4_quantize(devs[i], nv.NVFP4_BF16, T, C, C, nv.NVFP4_ROW_1D, nv.NVFP4_SR, 5 + i,
+                                  o["qc"], o["qs"], None, None, o["f"][4], o["f"][5])
+                outs.append(o)
+        torch.cuda.synchronize()
+        for i, o in enumerate(outs):
+            f = [float(t.item()) for t in o["f"]]
+            row = dict(codes=gpuio.host(o["rc"]), scales=gpuio.host(o["rs"]), tensor_scale=f[0], amax=f[1])
+            rht = dict(codes=gpuio.host(o["hc"]), scales=gpuio.host(o["hs"]), tensor_scale=f[2], amax=f[3])
+            sr = dict(codes=gpuio.host(o["qc"]), scales=gpuio.host(o["qs"]), tensor_scale=f[4], amax=f[5])
+            _row_rht_vs_oracle(ora, xs[i], masks[i], nv.NVFP4_RNE, 0, nv.NVFP4_RNE, 0, (row, rht))
+            _same(sr, ora.quantize(xs[i], ora.ROW_1D, ora.SR, 5 + i))
+    assert _launches()[0] == n0 + 12
