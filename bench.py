@@ -552,13 +552,14 @@ def summarize_trace(path, steps, warmup):
     rows = [rows[i] for i in order]
     grids = [grids[i] for i in order]
     stats = {}
-    for (s, e, k), g in zip(rows, grids):
-        stats.setdefault((k, g), []).append((e - s) / 1e3)
+    for i, ((s, e, k), g) in enumerate(zip(rows, grids)):
+        nxt = f"{rows[i + 1][2]} {grids[i + 1][0]}x{grids[i + 1][1]}" if i + 1 < len(rows) else None
+        stats.setdefault((_with_next(k, nxt), g), []).append((e - s) / 1e3)
     total = sum(sum(v) for v in stats.values())
     print("| kernel | grid (workgroups x by y) | calls | mean µs | median µs | total ms | % of kernel time |")
     print("|---|---|---:|---:|---:|---:|---:|")
     for (k, g), v in sorted(stats.items(), key=lambda kv: -sum(kv[1])):
-        name = k if len(k) <= 60 else k[:57] + "..."
+        name = k if len(k) <= 90 else k[:87] + "..."
         print(f"| `{name}` | {g[0]}x{g[1]} | {len(v)} | {np.mean(v):.1f} | {np.median(v):.1f} | "
               f"{sum(v) / 1e3:.3f} | {100 * sum(v) / total:.1f} |")
     per_step = 3 * S_CHUNKS
@@ -590,32 +591,40 @@ def summarize_trace(path, steps, warmup):
         print(f"- {name}: {len(d)} launches, mean {np.mean(d):.1f} µs, median {np.median(d):.1f} µs")
 
 
+def _with_next(k, nxt):
+    """An amax pass is told apart by the cast that follows it, named with its
+    grid (passes over tensors of different sizes can share one grid: a
+    resident grid)."""
+    if nxt is not None and (k.startswith("k_rht_amax") or k.startswith("k_amax")):
+        return f"{k} -> {nxt}"
+    return k
+
+
 # ----------------------------------------------------------------- counter summary
 def _headline_labels():
     """(short kernel name, workgroups) -> (label, algorithmic bytes read, written)
     for the launches of one headline step on a 256-CU device; the Wgrad
-    figures average its beta = 0 launch and its three beta = 1 launches."""
+    figures average its beta = 0 launch and its three beta = 1 launches.  An
+    amax pass is keyed by "<kernel> -> <the kernel after it>" and any grid
+    (None)."""
     T, I, O = S_CHUNK, S_IN, S_OUT
 
     def q_out(rows, cols):  # codes + scales of one NVFP4 copy
         return rows * cols // 2 + rows * cols // 16
 
-    def rht_amax_grid(tokens, cols):
-        units = (tokens // 16) * (cols // 4)
-        wgs = -(-units // 256)
-        rounds = -(-wgs // 2048)
-        return min(-(-wgs // rounds), 2048)
-
     w_in, x_in, d_in = O * I * 2, T * I * 2, T * O * 2
     wg_acc = 0.75 * O * I * 4
     return {
-        ("k_amax<unsigned short, 8>", 1024): ("W amax (5120x20480)", w_in, 0),
+        (f"k_amax<unsigned short, 8> -> k_cast_tile2d<unsigned short, 0> {(O // 256) * (I // 64)}", None):
+            ("W amax (5120x20480)", w_in, 0),
         ("k_cast_tile2d<unsigned short, 0>", (O // 256) * (I // 64)):
             ("W 2D cast + transposed copy", w_in, 2 * q_out(O, I) - 2 * (O * I // 16) + 2 * (O * I // 256)),
-        ("k_rht_amax<unsigned short>", rht_amax_grid(T, I)): ("X RHT + plain amax (8192x20480)", x_in, 0),
+        (f"k_rht_amax<unsigned short> -> k_cast_row_rht<unsigned short, 0, 0> {(I // 128) * (T // 256)}", None):
+            ("X RHT + plain amax (8192x20480)", x_in, 0),
         ("k_cast_row_rht<unsigned short, 0, 0>", (I // 128) * (T // 256)):
             ("X row + RHT column cast, RNE", x_in, 2 * q_out(T, I)),
-        ("k_rht_amax<unsigned short>", rht_amax_grid(T, O)): ("dY RHT + plain amax (8192x5120)", d_in, 0),
+        (f"k_rht_amax<unsigned short> -> k_cast_row_rht<unsigned short, 1, 1> {(O // 128) * (T // 256)}", None):
+            ("dY RHT + plain amax (8192x5120)", d_in, 0),
         ("k_cast_row_rht<unsigned short, 1, 1>", (O // 128) * (T // 256)):
             ("dY row + RHT column cast, SR", d_in, 2 * q_out(T, O)),
         ("k_gemm_nvfp4<float>", 768): ("Fprop 8192x5120x20480", q_out(T, I) + O * I // 2 + O * I // 256,
@@ -637,11 +646,15 @@ def summarize_pmc(paths):
     groups = {}
     for path in paths:
         with open(path) as f:
-            for r in csv.DictReader(f):
-                wgs = int(r["Grid_Size"]) // max(int(r["Workgroup_Size"]), 1)
-                key = (_kernel_short(r["Kernel_Name"]), wgs)
-                g = groups.setdefault(key, {})
-                g.setdefault(r["Counter_Name"], {})[r["Dispatch_Id"]] = float(r["Counter_Value"])
+            recs = list(csv.DictReader(f))
+        names = {int(r["Dispatch_Id"]): f'{_kernel_short(r["Kernel_Name"])} '
+                 f'{int(r["Grid_Size"]) // max(int(r["Workgroup_Size"]), 1)}' for r in recs}
+        for r in recs:
+            wgs = int(r["Grid_Size"]) // max(int(r["Workgroup_Size"]), 1)
+            d = int(r["Dispatch_Id"])
+            key = (_with_next(_kernel_short(r["Kernel_Name"]), names.get(d + 1)), wgs)
+            g = groups.setdefault(key, {})
+            g.setdefault(r["Counter_Name"], {})[r["Dispatch_Id"]] = float(r["Counter_Value"])
     probe = [g for (k, _), g in groups.items() if "neg_kernel" in k]
     gib_kib = float(1 << 20)
     fetch_f = write_f = None
@@ -667,7 +680,7 @@ def summarize_pmc(paths):
         wk = np.mean(list(g["WRITE_SIZE"].values())) if "WRITE_SIZE" in g else None
         rd = fk * 1024 * fetch_f if fk is not None and fetch_f else None
         wr = wk * 1024 * write_f if wk is not None and write_f else None
-        lab, ar, aw = labels.get((k, wgs), ("", None, None))
+        lab, ar, aw = labels.get((k, wgs), labels.get((k, None), ("", None, None)))
         ratio = ""
         if rd is not None and wr is not None and ar is not None:
             ratio = f"{(rd + wr) / (ar + aw):.2f}"
