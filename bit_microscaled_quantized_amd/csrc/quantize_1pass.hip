@@ -326,6 +326,11 @@ hipError_t try_quantize_row_1pass(const void* x, int dt, int64_t rows, int64_t c
                                   float* tensor_scale, float* amax, hipStream_t s, bool* done) {
   *done = false;
   if (ld != cols) return hipSuccess;
+  // before device_setup: its first call on a device clears the slots with a
+  // synchronous memset, which a stream under capture must not see
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &cap) != hipSuccess || cap != hipStreamCaptureStatusNone)
+    return hipSuccess;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return hipSuccess;
   int per_cu = 0, cus = 0;
