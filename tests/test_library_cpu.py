@@ -37,6 +37,48 @@ def test_library_exports_every_declared_symbol():
     assert exported_c == declared_symbols()
 
 
+def _declarations():
+    """name -> (return type, [parameter types]) of every entry point in include/*.h."""
+    text = "".join(open(os.path.join(os.path.dirname(HEADER), f)).read()
+                   for f in sorted(os.listdir(os.path.dirname(HEADER))) if f.endswith(".h"))
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    out = {}
+    for ret, name, params in re.findall(r"^\s*(nvfp4_status|const char \*)\s*((?:nvfp4|mxfp4)_\w+)\s*\(([^)]*)\)\s*;",
+                                        text, re.M):
+        types = []
+        for p in params.split(","):
+            p = " ".join(p.split())
+            m = re.match(r"^(.*?)(\w+)$", p)
+            assert m, (name, p)
+            types.append(m.group(1).replace(" ", ""))
+        out[name] = (ret.replace(" ", ""), types)
+    return out
+
+
+def test_binding_argument_types_match_the_header():
+    """Each entry point's ctypes argument and return types are the C types
+    the header declares, in order (so no argument is marshalled at another
+    width or position)."""
+    import ctypes
+    lib = nv.load_library()
+    scalar = {"int64_t": ctypes.c_int64, "uint64_t": ctypes.c_uint64, "uint32_t": ctypes.c_uint32,
+              "int32_t": ctypes.c_int32, "int": ctypes.c_int32, "float": ctypes.c_float}
+    decls = _declarations()
+    assert sorted(decls) == sorted(b.EXPORTED)
+    for name, (ret, types) in decls.items():
+        fn = getattr(lib, name)
+        want = []
+        for t in types:
+            if t == "int64_t*":
+                want.append(ctypes.POINTER(ctypes.c_int64))
+            elif t.endswith("*"):
+                want.append(ctypes.c_void_p)
+            else:
+                want.append(scalar[t.replace("const", "")])
+        assert list(fn.argtypes) == want, (name, types, fn.argtypes)
+        assert fn.restype == (ctypes.c_char_p if ret == "constchar*" else ctypes.c_int32), name
+
+
 def test_mxfp4_argument_errors():
     def q(**kw):
         args = dict(x=FAKE, dt=0, rows=32, cols=64, ld_x=64, layout=0, rnd=0, seed=0, codes=FAKE,
